@@ -1,0 +1,411 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Every check here is fixed by the pages or by mathematics, not by re-running
+the oracle's own formula:
+  * exact rational brute force (tests/exact_ref.py) on tiny integer inputs;
+  * closed forms (K, valid counts, proxy rounding);
+  * special cases that reduce to a library routine (torch.topk in float64);
+  * invariants (causality, uniqueness, padding, order, nesting);
+  * a re-expression of the pages' Reuse loop in torch float64;
+  * the only value the pages print: the quick test's index shape.
+Citations name "PIVOT Explained -- From Paper to Working Code in 10 Minutes"
+(sunghee.kr, republished by wpnews.pro) and the arXiv abstract (fugumt.com).
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+from tests import exact_ref
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- helpers
+
+def valid_counts(row_idx: np.ndarray) -> np.ndarray:
+    return (row_idx >= 0).sum(-1)
+
+
+def check_row_structure(idx, sc, limit_fn):
+    """Valid entries first, then -1; distinct; causal (< limit); scores
+    non-increasing with ties broken by ascending index; -inf padding."""
+    S, H, k = idx.shape
+    for i in range(S):
+        lim = limit_fn(i)
+        for h in range(H):
+            r = idx[i, h]
+            nv = int((r >= 0).sum())
+            assert (r[:nv] >= 0).all() and (r[nv:] == -1).all()
+            assert len(set(r[:nv].tolist())) == nv
+            assert (r[:nv] < lim).all()
+            s = sc[i, h]
+            assert np.isneginf(s[nv:]).all()
+            for t in range(nv - 1):
+                assert s[t] > s[t + 1] or (s[t] == s[t + 1] and r[t] < r[t + 1])
+
+
+# ------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("top_k,ratio,K", [
+    (64, 2.0, 128),     # the code's defaults: K = 2 x top_k ("How It Works")
+    (2048, 2.0, 4096),
+    (3, 1.5, 4),        # int() truncates 4.5
+    (3, 1.1, 3),        # 3.3000000000000003 -> 3
+    (10, 2.55, 25),     # 25.499999999999996 -> 25
+    (5, 1.0, 5),
+    (5, 0.9, -1),       # K < top_k rejected
+    (0, 2.0, -1),
+])
+def test_candidate_count_closed_form(top_k, ratio, K):
+    assert oracle.candidate_count(top_k, ratio) == K
+
+
+def test_quick_test_shape_golden():
+    """The quick test of "Show Me The Code" prints the index shape
+    (1024, 8, 64); the oracle's output has that shape at those sizes."""
+    meta = {}
+    with open(os.path.join(GOLDEN, "quick_test_shape.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            for tok in line.split():
+                key, val = tok.split("=")
+                meta[key] = val
+    S, H, D = int(meta["S"]), int(meta["H"]), int(meta["D"])
+    shape = tuple(int(x) for x in meta["shape"].split(","))
+    cfg = syn.tiny_prefill(integer=False)
+    assert cfg["q"].shape == (S, H, D)
+    # one head is enough for the shape; the others stay padding
+    idx, sc = oracle.prefill(cfg["q"], cfg["k"], int(meta["top_k"]), int(meta["g"]),
+                             float(meta["candidate_ratio"]), "refine", heads=(0, 1))
+    assert idx.shape == shape
+    assert idx.dtype == np.int32
+
+
+# ---------------------------------------------------- exact brute force
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+@pytest.mark.parametrize("S,H,D,top_k,g,ratio", [
+    (24, 2, 4, 3, 4, 2.0),
+    (19, 1, 8, 4, 4, 1.5),   # ragged last group (m = 3), K = 6
+    (16, 2, 4, 2, 1, 2.0),   # g = 1
+    (12, 1, 4, 8, 8, 3.0),   # top_k larger than early prefixes
+])
+def test_oracle_matches_exact_bruteforce(dtype, mode, S, H, D, top_k, g, ratio):
+    q = syn.integers((S, H, D), 11 + S, 3, dtype)
+    k = syn.integers((S, H, D), 29 + S, 3, dtype)
+    K = oracle.candidate_count(top_k, ratio)
+    want_idx, want_sc = exact_ref.pivot_exact(q, k, top_k, g, K, mode)
+    got_idx, got_sc = oracle.prefill(q, k, top_k, g, ratio, mode)
+    np.testing.assert_array_equal(got_idx, want_idx)
+    np.testing.assert_array_equal(got_sc.astype(np.float64), want_sc)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dense_matches_exact_bruteforce(dtype):
+    q = syn.integers((20, 2, 4), 5, 4, dtype)
+    k = syn.integers((20, 2, 4), 6, 4, dtype)
+    want_idx, want_sc = exact_ref.dense_exact(q, k, 5)
+    got_idx, got_sc = oracle.dense(q, k, 5)
+    np.testing.assert_array_equal(got_idx, want_idx)
+    np.testing.assert_array_equal(got_sc.astype(np.float64), want_sc)
+
+
+@pytest.mark.parametrize("m", [3, 5, 6, 7])
+def test_proxy_rounding_non_power_of_two_group(m):
+    """The proxy of a group of m members is the float32 quotient of the exact
+    sum (integer inputs) by m, then RNE to bf16 for bf16 inputs: checked
+    bit for bit against a rational-arithmetic rounding."""
+    S, H, D = m, 1, 32
+    for dtype in ("f32", "bf16"):
+        q = syn.integers((S, H, D), 100 + m, 8, dtype)
+        got = oracle.proxy(q, m, 0, 0)
+        want = exact_ref.proxy_exact(exact_ref.values(q), 0, m, 0, dtype == "bf16")
+        np.testing.assert_array_equal(got, np.array([float(w) for w in want], np.float32))
+
+
+def test_scores_are_rounded_once_from_the_exact_dot():
+    """Reported scores equal the exact dot product rounded to float32 (bf16
+    inputs: every product is exact in double, so the double sum of 64
+    products can differ from the exact value only by double rounding; allow
+    one float32 ulp)."""
+    S, H, D = 40, 1, 64
+    q = syn.gaussian((S, H, D), 3, "bf16")
+    k = syn.gaussian((S, H, D), 4, "bf16")
+    idx, sc = oracle.dense(q, k, 6)
+    qv, kv = exact_ref.values(q), exact_ref.values(k)
+    from fractions import Fraction
+    for i in range(1, S, 7):
+        qi = [Fraction(float(x)) for x in qv[i, 0]]
+        for t in range(6):
+            c = idx[i, 0, t]
+            if c < 0:
+                continue
+            want = np.float32(exact_ref.dot_f32(qi, kv, c, 0))
+            assert abs(int(np.float32(sc[i, 0, t]).view(np.int32)) - int(want.view(np.int32))) <= 1
+
+
+# ------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+def test_structure_invariants_gaussian(mode):
+    S, H, D, top_k, g = 200, 2, 16, 12, 8
+    q = syn.gaussian((S, H, D), 21, "bf16")
+    k = syn.gaussian((S, H, D), 22, "bf16")
+    idx, sc = oracle.prefill(q, k, top_k, g, 2.0, mode)
+    check_row_structure(idx, sc, lambda i: max((i // g) * g, 1))
+    # valid count = min(top_k, min(K, n_j)) for both modes
+    K = 2 * top_k
+    for i in range(S):
+        n = max((i // g) * g, 1)
+        assert (valid_counts(idx[i]) == min(top_k, min(K, n))).all()
+    if mode == "reuse":
+        for i in range(S):
+            j0 = (i // g) * g
+            np.testing.assert_array_equal(idx[i], idx[j0])
+
+
+def test_dense_invariants():
+    S, H, D, top_k = 150, 2, 16, 9
+    q = syn.gaussian((S, H, D), 31, "f32")
+    k = syn.gaussian((S, H, D), 32, "f32")
+    idx, sc = oracle.dense(q, k, top_k)
+    check_row_structure(idx, sc, lambda i: max(i, 1))
+    for i in range(S):
+        assert (valid_counts(idx[i]) == min(top_k, max(i, 1))).all()
+
+
+def test_refine_rows_are_subsets_of_candidates():
+    S, H, D, top_k, g = 160, 1, 16, 10, 8
+    q = syn.gaussian((S, H, D), 41, "bf16")
+    k = syn.gaussian((S, H, D), 42, "bf16")
+    idx, _ = oracle.prefill(q, k, top_k, g, 2.0, "refine")
+    for j in range(S // g):
+        cand, _ = oracle.prefill_candidates(q, k, 0, j, top_k, g, 2.0)
+        cs = set(cand.tolist())
+        for i in range(j * g, j * g + g):
+            r = idx[i, 0]
+            assert set(r[r >= 0].tolist()) <= cs
+
+
+# -------------------------------------------------------- special cases
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_g1_reuse_equals_dense(dtype):
+    """With one query per group the proxy is the query itself and the prefix
+    is [0, max(i, 1)): Reuse is the dense indexer."""
+    S, H, D, top_k = 130, 2, 16, 7
+    q = syn.gaussian((S, H, D), 51, dtype)
+    k = syn.gaussian((S, H, D), 52, dtype)
+    a, sa = oracle.prefill(q, k, top_k, 1, 2.0, "reuse")
+    b, sb = oracle.dense(q, k, top_k)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(sa, sb)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_g1_refine_equals_dense(dtype):
+    S, H, D, top_k = 90, 1, 16, 5
+    q = syn.gaussian((S, H, D), 53, dtype)
+    k = syn.gaussian((S, H, D), 54, dtype)
+    a, _ = oracle.prefill(q, k, top_k, 1, 2.0, "refine")
+    b, _ = oracle.dense(q, k, top_k)
+    np.testing.assert_array_equal(a, b)
+
+
+def group_prefix_dense_torch(q, k, top_k, g):
+    """Each query ranks the keys [0, max(group_start, 1)) by its own score,
+    with torch.topk on float64 values (tie-free inputs)."""
+    import torch
+    qv = torch.from_numpy(exact_ref.values(q))
+    kv = torch.from_numpy(exact_ref.values(k))
+    S, H, D = q.shape
+    out = np.full((S, H, top_k), -1, np.int64)
+    for h in range(H):
+        for i in range(S):
+            n = max((i // g) * g, 1)
+            s = kv[:n, h, :] @ qv[i, h, :]
+            kk = min(top_k, n)
+            out[i, h, :kk] = torch.topk(s, kk).indices.numpy()
+    return out
+
+
+def test_refine_equals_group_prefix_dense_when_K_covers_prefix():
+    """When K >= every prefix length, C is the whole prefix and Refine is each
+    query's own top-k over [0, n_j): checked against torch.topk in float64."""
+    S, H, D, top_k, g = 96, 2, 16, 6, 8
+    q = syn.gaussian((S, H, D), 61, "f32")
+    k = syn.gaussian((S, H, D), 62, "f32")
+    ratio = float(S)  # K = top_k * S >= S
+    idx, _ = oracle.prefill(q, k, top_k, g, ratio, "refine")
+    want = group_prefix_dense_torch(q, k, top_k, g)
+    np.testing.assert_array_equal(idx, want)
+
+
+def test_dense_equals_torch_topk_float64():
+    import torch
+    S, H, D, top_k = 70, 2, 32, 8
+    q = syn.gaussian((S, H, D), 71, "f32")
+    k = syn.gaussian((S, H, D), 72, "f32")
+    idx, _ = oracle.dense(q, k, top_k)
+    qv, kv = torch.from_numpy(q.astype(np.float64)), torch.from_numpy(k.astype(np.float64))
+    for h in range(H):
+        for i in range(S):
+            n = max(i, 1)
+            kk = min(top_k, n)
+            want = torch.topk(kv[:n, h] @ qv[i, h], kk).indices.numpy()
+            np.testing.assert_array_equal(idx[i, h, :kk], want)
+
+
+def test_refine_with_K_equal_top_k_permutes_reuse():
+    S, H, D, top_k, g = 120, 1, 16, 9, 6
+    q = syn.gaussian((S, H, D), 81, "bf16")
+    k = syn.gaussian((S, H, D), 82, "bf16")
+    a, _ = oracle.prefill(q, k, top_k, g, 1.0, "refine")
+    b, _ = oracle.prefill(q, k, top_k, g, 1.0, "reuse")
+    for i in range(S):
+        assert sorted(a[i, 0].tolist()) == sorted(b[i, 0].tolist())
+
+
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+def test_zero_queries_tie_break_by_index(mode):
+    """Zero queries make every score +-0: the order is by ascending index,
+    and -0.0 products (negative keys) must tie with +0.0."""
+    S, H, D, top_k, g = 64, 1, 8, 5, 4
+    q = np.zeros((S, H, D), np.float32)
+    k = syn.integers((S, H, D), 91, 3, "f32")
+    idx, sc = oracle.prefill(q, k, top_k, g, 2.0, mode)
+    for i in range(S):
+        n = max((i // g) * g, 1)
+        kk = min(top_k, n)
+        np.testing.assert_array_equal(idx[i, 0, :kk], np.arange(kk))
+        assert (sc[i, 0, :kk] == 0).all() and not np.signbit(sc[i, 0, :kk]).any()
+    didx, _ = oracle.dense(q, k, top_k)
+    for i in range(S):
+        kk = min(top_k, max(i, 1))
+        np.testing.assert_array_equal(didx[i, 0, :kk], np.arange(kk))
+
+
+def test_first_group_sees_key_zero():
+    """Group 0 scans the prefix [0, max(0, 1)) = {0}: its rows are [0, -1, ...]
+    (the Reuse code's max(g_start, 1))."""
+    q = syn.gaussian((16, 1, 8), 95, "f32")
+    k = syn.gaussian((16, 1, 8), 96, "f32")
+    for mode in ("refine", "reuse"):
+        idx, _ = oracle.prefill(q, k, 4, 4, 2.0, mode)
+        for i in range(4):
+            np.testing.assert_array_equal(idx[i, 0], [0, -1, -1, -1])
+
+
+def test_recall_nested_in_K_and_refine_beats_reuse():
+    """Top-K sets are nested in K under a total order, so Refine's recall
+    against group-prefix dense cannot drop as K grows, and Refine (which
+    re-ranks a superset of Reuse's rows) is never below Reuse."""
+    S, H, D, top_k, g = 256, 1, 16, 8, 8
+    q = syn.ar1_queries(S, H, D, 101, dtype="f32")
+    k = syn.pareto_keys(S, H, D, 102, dtype="f32")
+    ref = group_prefix_dense_torch(q, k, top_k, g)
+
+    def recall(idx):
+        tot = 0.0
+        for i in range(g, S):
+            a = set(idx[i, 0][idx[i, 0] >= 0].tolist())
+            b = set(ref[i, 0][ref[i, 0] >= 0].tolist())
+            tot += len(a & b) / len(b)
+        return tot / (S - g)
+
+    prev = -1.0
+    for ratio in (1.0, 1.5, 2.0, 4.0, 8.0):
+        r = recall(oracle.prefill(q, k, top_k, g, ratio, "refine")[0])
+        assert r >= prev - 1e-12
+        prev = r
+    reuse = recall(oracle.prefill(q, k, top_k, g, 2.0, "reuse")[0])
+    refine = recall(oracle.prefill(q, k, top_k, g, 2.0, "refine")[0])
+    assert refine >= reuse
+
+
+# ------------------------------------------------- the pages' Reuse loop
+
+def pages_reuse_torch(q, k, top_k, group_size, candidate_ratio):
+    """The Reuse loop of "Show Me The Code", re-expressed in torch float64:
+    per head, per group: proxy = mean of the group, one scan over
+    k[:max(g_start, 1)], top-K, and every member takes the first top_k.
+    Zero-initialised output as on the pages."""
+    import torch
+    qv = torch.from_numpy(exact_ref.values(q))
+    kv = torch.from_numpy(exact_ref.values(k))
+    S, H, D = q.shape
+    K = int(top_k * candidate_ratio)
+    out = torch.zeros(S, H, top_k, dtype=torch.long)
+    for h in range(H):
+        for g_start in range(0, S, group_size):
+            g_end = min(g_start + group_size, S)
+            ref_pos = max(g_start, 1)
+            proxy = qv[g_start:g_end, h].mean(dim=0)
+            scores = kv[:ref_pos, h] @ proxy
+            n_take = min(K, ref_pos)
+            cand = torch.topk(scores, n_take).indices
+            kk = min(top_k, n_take)
+            out[g_start:g_end, h, :kk] = cand[:kk]
+    return out.numpy()
+
+
+def test_reuse_matches_pages_loop_float64():
+    """On tie-free fp32 inputs with power-of-two groups the proxy is exact
+    in float32 up to the one division, and the pages' float64 loop and the
+    oracle agree on every row once -1 padding is mapped to the pages' 0."""
+    S, H, D, top_k, g = 128, 2, 16, 6, 8
+    q = syn.integers((S, H, D), 111, 8, "f32")  # exact float32 means (g = 8)
+    k = syn.gaussian((S, H, D), 112, "f32")
+    idx, _ = oracle.prefill(q, k, top_k, g, 2.0, "reuse")
+    want = pages_reuse_torch(q, k, top_k, g, 2.0)
+    np.testing.assert_array_equal(np.where(idx < 0, 0, idx), want)
+
+
+# ----------------------------------------------------------- decode path
+
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+def test_decode_equals_last_prefill_group(mode):
+    """A decode step of g queries after a context of length L (L % g == 0) is
+    the group j = L / g of a prefill of length L + g whose last g queries are
+    the MTP queries (the abstract: one algorithm, groups formed differently)."""
+    g, H, D, top_k = 4, 2, 16, 6
+    ctx = np.array([40, 8, 64], np.int64)
+    B = len(ctx)
+    kc = syn.gaussian((int(ctx.sum()), H, D), 121, "bf16")
+    qd = syn.gaussian((B * g, H, D), 122, "bf16")
+    idx, sc = oracle.decode(qd, kc, ctx, g, top_k, 2.0, mode)
+    off = 0
+    for b in range(B):
+        L = int(ctx[b])
+        keys = np.concatenate([kc[off:off + L], syn.gaussian((g, H, D), 123 + b, "bf16")])
+        qs = np.concatenate([syn.gaussian((L, H, D), 124 + b, "bf16"), qd[b * g:(b + 1) * g]])
+        pidx, psc = oracle.prefill(qs, keys, top_k, g, 2.0, mode)
+        np.testing.assert_array_equal(idx[b * g:(b + 1) * g], pidx[L:L + g])
+        np.testing.assert_array_equal(sc[b * g:(b + 1) * g], psc[L:L + g])
+        off += L
+
+
+def test_rows_api_matches_full():
+    S, H, D, top_k, g = 100, 3, 16, 7, 8
+    q = syn.gaussian((S, H, D), 131, "bf16")
+    k = syn.gaussian((S, H, D), 132, "bf16")
+    rng = np.random.default_rng(0)
+    ri = rng.integers(0, S, 40)
+    rh = rng.integers(0, H, 40)
+    for mode in ("refine", "reuse"):
+        full, fs = oracle.prefill(q, k, top_k, g, 2.0, mode)
+        rows, rs = oracle.prefill_rows(q, k, ri, rh, top_k, g, 2.0, mode)
+        np.testing.assert_array_equal(rows, full[ri, rh])
+        np.testing.assert_array_equal(rs, fs[ri, rh])
+    fd, _ = oracle.dense(q, k, top_k)
+    rd, _ = oracle.dense_rows(q, k, ri, rh, top_k)
+    np.testing.assert_array_equal(rd, fd[ri, rh])
