@@ -1,0 +1,210 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer-valued inputs (every float32 score exact) are compared bit for bit:
+indices, order, -1 padding and scores. Gaussian inputs are compared
+tie-tolerantly (tests/parity.py). Sizes span several scan tiles (256 groups)
+and ragged tails; the degenerate cases (all-equal scores, one-key prefixes,
+top_k beyond the prefix) are included.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+from tests import parity
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def dev_tensor(a: np.ndarray):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(a).to(DEV)
+
+
+@pytest.fixture(scope="module")
+def pv():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import top_token_selection_amd as pv
+    return pv
+
+
+def run_prefill(pv, q, k, top_k, g, ratio, mode):
+    idx, sc = pv.index_prefill(dev_tensor(q), dev_tensor(k), top_k=top_k, g=g, candidate_ratio=ratio,
+                               mode=mode, return_scores=True)
+    torch.cuda.synchronize()
+    return parity.to_host(idx), parity.to_host(sc)
+
+
+def prefill_limits(S, g):
+    i = np.arange(S)
+    return np.maximum((i // g) * g, 1)[:, None]
+
+
+# ----------------------------------------------------------- bit-exact
+
+EXACT_CASES = [
+    # S, H, D, top_k, g, ratio, dtype
+    (1024, 8, 64, 64, 8, 2.0, "f32"),     # the tiny workload's integer twin
+    (700, 3, 128, 16, 8, 2.0, "bf16"),    # ragged tail, several tiles of rows
+    (600, 2, 64, 24, 3, 1.5, "bf16"),     # non-power-of-two groups
+    (513, 2, 128, 8, 1, 2.0, "bf16"),     # g = 1
+    (300, 2, 64, 40, 16, 2.0, "f32"),     # top_k beyond early prefixes
+    (2100, 1, 128, 100, 8, 2.0, "bf16"),  # > 8 scan tiles, rows that need sampling
+]
+
+
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+@pytest.mark.parametrize("S,H,D,top_k,g,ratio,dtype", EXACT_CASES)
+def test_prefill_bit_exact_integer_inputs(pv, mode, S, H, D, top_k, g, ratio, dtype):
+    print(f"\n[prefill exact] S={S} H={H} D={D} k={top_k} g={g} r={ratio} {dtype} {mode}", flush=True)
+    a = 8 if dtype == "f32" else 4
+    q = syn.integers((S, H, D), 7000 + S + g, a, dtype)
+    k = syn.integers((S, H, D), 8000 + S + g, a, dtype)
+    gi, gs = run_prefill(pv, q, k, top_k, g, ratio, mode)
+    oi, os_ = oracle.prefill(q, k, top_k, g, ratio, mode)
+    np.testing.assert_array_equal(gi, oi)
+    if dtype == "bf16" or S % g == 0 and (g & (g - 1)) == 0:
+        # every proxy is exact (power-of-two group of small integers, or a
+        # bf16 proxy whose products and sums stay within float32's 24 bits)
+        np.testing.assert_array_equal(gs, os_)
+    else:
+        # fp32 proxy of a ragged group (sum / m, m not a power of two) is
+        # rounded once; float32 accumulation order then moves scores by ulps
+        np.testing.assert_allclose(gs, os_, rtol=4 * 2.0 ** -23, atol=0)
+
+
+@pytest.mark.parametrize("S,H,D,top_k,dtype", [(1024, 8, 64, 64, "f32"), (700, 3, 128, 32, "bf16")])
+def test_dense_bit_exact_integer_inputs(pv, S, H, D, top_k, dtype):
+    print(f"\n[dense exact] S={S} H={H} D={D} k={top_k} {dtype}", flush=True)
+    a = 8 if dtype == "f32" else 4
+    q = syn.integers((S, H, D), 7100 + S, a, dtype)
+    k = syn.integers((S, H, D), 8100 + S, a, dtype)
+    idx, sc = pv.dense_index(dev_tensor(q), dev_tensor(k), top_k=top_k, return_scores=True)
+    torch.cuda.synchronize()
+    oi, os_ = oracle.dense(q, k, top_k)
+    np.testing.assert_array_equal(parity.to_host(idx), oi)
+    np.testing.assert_array_equal(parity.to_host(sc), os_)
+
+
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+@pytest.mark.parametrize("g", [2, 4])
+def test_decode_bit_exact_integer_inputs(pv, mode, g):
+    print(f"\n[decode exact] g={g} {mode}", flush=True)
+    H, D, top_k = 4, 128, 32
+    ctx = np.array([1, 5, 64, 300, 1000, 77], np.int64)
+    kc = syn.integers((int(ctx.sum()), H, D), 9001, 4, "bf16")
+    q = syn.integers((len(ctx) * g, H, D), 9002 + g, 4, "bf16")
+    idx, sc = pv.index_decode(dev_tensor(q), dev_tensor(kc), ctx, g, top_k=top_k, mode=mode, return_scores=True)
+    torch.cuda.synchronize()
+    oi, os_ = oracle.decode(q, kc, ctx, g, top_k, 2.0, mode)
+    np.testing.assert_array_equal(parity.to_host(idx), oi)
+    np.testing.assert_array_equal(parity.to_host(sc), os_)
+
+
+# ------------------------------------------------------- degenerate cases
+
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+def test_all_scores_equal_ties_by_index(pv, mode):
+    """Zero queries: every score is 0, so every row is the smallest indices
+    (exercises the tie resolution and the exact fallback)."""
+    print(f"\n[ties] {mode}", flush=True)
+    S, H, D, top_k, g = 900, 2, 64, 20, 4
+    q = np.zeros((S, H, D), np.float32)
+    k = syn.integers((S, H, D), 31, 3, "f32")
+    gi, gs = run_prefill(pv, q, k, top_k, g, 2.0, mode)
+    oi, os_ = oracle.prefill(q, k, top_k, g, 2.0, mode)
+    np.testing.assert_array_equal(gi, oi)
+    np.testing.assert_array_equal(gs, os_)
+
+
+def test_tiny_and_degenerate_shapes(pv):
+    for (S, H, D, top_k, g) in [(1, 1, 64, 4, 8), (5, 2, 64, 3, 8), (9, 1, 128, 16, 4), (64, 1, 64, 64, 64)]:
+        for mode in ("refine", "reuse"):
+            print(f"\n[shape] S={S} H={H} D={D} k={top_k} g={g} {mode}", flush=True)
+            q = syn.integers((S, H, D), 41 + S, 4, "bf16")
+            k = syn.integers((S, H, D), 42 + S, 4, "bf16")
+            gi, gs = run_prefill(pv, q, k, top_k, g, 2.0, mode)
+            oi, os_ = oracle.prefill(q, k, top_k, g, 2.0, mode)
+            np.testing.assert_array_equal(gi, oi)
+            np.testing.assert_array_equal(gs, os_)
+
+
+def test_refine_with_K_covering_prefix_equals_group_prefix_dense(pv):
+    S, H, D, top_k, g = 256, 2, 64, 8, 8
+    q = syn.integers((S, H, D), 51, 4, "bf16")
+    k = syn.integers((S, H, D), 52, 4, "bf16")
+    ratio = 512 / top_k  # K = 512 >= S
+    gi, _ = run_prefill(pv, q, k, top_k, g, ratio, "refine")
+    oi, _ = oracle.prefill(q, k, top_k, g, ratio, "refine")
+    np.testing.assert_array_equal(gi, oi)
+
+
+def test_g1_reuse_equals_dense_on_gpu(pv):
+    S, H, D, top_k = 400, 2, 128, 16
+    q = syn.gaussian((S, H, D), 61, "bf16")
+    k = syn.gaussian((S, H, D), 62, "bf16")
+    a = pv.index_prefill(dev_tensor(q), dev_tensor(k), top_k=top_k, g=1, mode="reuse")
+    b = pv.dense_index(dev_tensor(q), dev_tensor(k), top_k=top_k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(parity.to_host(a), parity.to_host(b))
+
+
+def test_head_chunking_matches_single_pass(pv):
+    """A workspace for one head per pass gives the same result."""
+    S, H, D, top_k, g = 600, 4, 64, 16, 8
+    q = syn.gaussian((S, H, D), 71, "bf16")
+    k = syn.gaussian((S, H, D), 72, "bf16")
+    full = pv.index_prefill(dev_tensor(q), dev_tensor(k), top_k=top_k, g=g)
+    one = pv.prefill_workspace_bytes(S, 1, D, top_k, g, 2.0, "refine", torch.bfloat16)
+    chunked = pv.index_prefill(dev_tensor(q), dev_tensor(k), top_k=top_k, g=g, max_workspace_bytes=one)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(parity.to_host(full), parity.to_host(chunked))
+
+
+def test_deterministic_repeat(pv):
+    S, H, D, top_k, g = 1500, 2, 128, 64, 8
+    q = dev_tensor(syn.gaussian((S, H, D), 81, "bf16"))
+    k = dev_tensor(syn.gaussian((S, H, D), 82, "bf16"))
+    for mode in ("refine", "reuse"):
+        a = pv.index_prefill(q, k, top_k=top_k, g=g, mode=mode, return_scores=True)
+        b = pv.index_prefill(q, k, top_k=top_k, g=g, mode=mode, return_scores=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------ tolerant (Gaussian)
+
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+def test_tiny_workload_gaussian_tolerant(pv, mode):
+    """The tiny workload (S=1024, H=8, D=64, fp32 N(0,1), top_k=64, g=8)."""
+    print(f"\n[tiny gaussian] {mode}", flush=True)
+    cfg = syn.tiny_prefill(integer=False)
+    q, k = cfg["q"], cfg["k"]
+    S, H, D = q.shape
+    top_k, g = cfg["top_k"], cfg["g"]
+    gi, gs = run_prefill(pv, q, k, top_k, g, 2.0, mode)
+    oi, os_ = oracle.prefill(q, k, top_k, g, 2.0, mode)
+    K = oracle.candidate_count(top_k, 2.0)
+    valid = np.minimum(top_k, np.minimum(K, prefill_limits(S, g)))
+    parity.structure_ok(gi, gs, prefill_limits(S, g), valid)
+    errs = []
+    qv = q.astype(np.float64)
+    for h in range(H):
+        for j in range(S // g):
+            proxy = oracle.proxy(q, g, h, j).astype(np.float64)
+            cand = csc = None
+            if mode == "refine":
+                cand, csc = oracle.prefill_candidates(q, k, h, j, top_k, g, 2.0)
+            for i in range(j * g, j * g + g):
+                avec = qv[i, h] if mode == "refine" else proxy
+                e = parity.tolerant_row_match(gi[i, h], gs[i, h], oi[i, h], os_[i, h], avec, k, h, D,
+                                              cand_idx=cand, cand_sc=csc, proxy=proxy)
+                if e:
+                    errs.append((i, h, e))
+    assert not errs, errs[:5]

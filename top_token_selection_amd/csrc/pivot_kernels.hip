@@ -1,0 +1,1353 @@
+// pivot_kernels.hip -- HIP kernels of the PIVOT query-group indexer for
+// CDNA4 (gfx950), and the C ABI that launches them (include/pivot.h).
+//
+// Method (arXiv abstract of "PIVOT: Efficient Query-Group Indexing for
+// Token-Level Sparse Attention"; "PIVOT Explained", sections "How It Works"
+// and "Show Me The Code"): a group of queries is averaged into a proxy; ONE
+// causal prefix scan of the proxy against the keys gives a candidate set C
+// of the K best keys; PIVOT-Refine re-scores C with each member query and
+// keeps its own top_k, PIVOT-Reuse hands the proxy's top_k to the members.
+//
+// Pipeline of one prefill call (per chunk of heads):
+//   k_proxy    q -> P (head-major (h, group, d)), float32 sum + IEEE divide
+//   k_scan     (sample pass) proxy . every s-th key of the prefix, on bf16 /
+//              fp32 MFMA; all sample scores kept
+//   k_tau      per row: threshold tau = r-th best sample score, chosen so
+//              that at least K keys of the full prefix score >= tau with
+//              overwhelming probability
+//   k_scan     (main pass) proxy . every key of the prefix on MFMA; only
+//              scores >= tau leave the chip, as (key, index) survivors
+//   k_select   per row: exact top-K of the survivors (Refine: candidate
+//              list) or exact sorted top_k (Reuse / dense: output rows);
+//              rows whose survivors cannot prove exactness are queued
+//   k_fallback queued rows: recompute the whole prefix, exact selection
+//   k_refine   per group: gather K[C], members' scores on MFMA, per-member
+//              exact sorted top_k
+// Decode replaces the scans by k_decode_scan (an HBM-streaming GEMV that
+// writes every score of each (sequence, head) row) and selects with the
+// streaming selector of k_fallback.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <type_traits>
+
+#include "../../include/pivot.h"
+#include "pivot_device.hpp"
+
+using namespace pivot;
+
+namespace {
+
+constexpr int SCAN_THREADS = 256;  // 4 wavefronts
+constexpr int SCAN_ROWS = 256;     // groups per scan block (64 per wave)
+constexpr int SCAN_KEYS = 64;      // keys per k-tile
+constexpr int SEL_THREADS = 256;
+constexpr int SEL_LOG2NB = 11;
+constexpr int SEL_E = 48;          // survivors per thread held in registers
+constexpr int TAU_E = 16;          // samples per thread held in registers
+constexpr int REF_LOG2NB = 10;
+constexpr int REF_E = 64;          // candidates per lane (K <= 4096)
+constexpr int MAX_K = 4096;
+constexpr int MAX_TOPK = 4096;
+constexpr int FB_BLOCKS = 256;
+constexpr int DEC_THREADS = 256;
+constexpr int DEC_TOKENS = 512;    // tokens per decode-scan block
+
+// Hardware places block b on XCD b % 8; hand each XCD a contiguous range of
+// logical work so neighbouring work shares that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb) {
+    const uint32_t per = nb / 8u, rem = nb % 8u;
+    const uint32_t x = b % 8u, i = b / 8u;
+    return x * per + min(x, rem) + i;
+}
+
+__device__ __forceinline__ int64_t prefix_len(int64_t j, int g) {
+    const int64_t s = j * (int64_t)g;
+    return s > 1 ? s : 1;
+}
+
+// virtual keys v = 0, 1, ... stand for keys koff + kstride * v; count of
+// those below n
+__device__ __forceinline__ int64_t virt_count(int64_t n, int kstride, int koff) {
+    return n > koff ? (n - koff - 1) / kstride + 1 : 0;
+}
+
+// ------------------------------------------------------------------ proxy
+
+template <typename T>
+__global__ void k_proxy(const T *__restrict__ q, int64_t S, int H, int D, int g,
+                        int h0, int Hc, int64_t G, T *__restrict__ P) {
+    const int64_t total = (int64_t)Hc * G * D;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int d = (int)(t % D);
+        const int64_t j = (t / D) % G;
+        const int hl = (int)(t / ((int64_t)D * G));
+        const int64_t i0 = j * g;
+        const int64_t m = min((int64_t)g, S - i0);
+        const T *src = q + (i0 * H + (h0 + hl)) * (int64_t)D + d;
+        float sum = 0.f;  // sequential float32 sum in position order
+        for (int64_t i = 0; i < m; ++i) sum += load_f32(src + i * (int64_t)H * D);
+        store_from_f32(P + t, __fdiv_rn(sum, (float)m));
+    }
+}
+
+__global__ void k_zero_u32(uint32_t *p, int64_t n) {
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n;
+         t += (int64_t)gridDim.x * blockDim.x)
+        p[t] = 0u;
+}
+
+struct Offsets64 {
+    int64_t v[64];
+    int count;
+    int start;
+};
+__global__ void k_put_offsets(int64_t *dst, Offsets64 a) {
+    const int t = threadIdx.x;
+    if (t < a.count) dst[a.start + t] = a.v[t];
+}
+
+// ------------------------------------------------------------------- scan
+
+struct ScanParams {
+    const void *P;
+    int64_t p_row, p_head;  // element strides of a proxy row / local head
+    const void *K;
+    int64_t k_row;          // element stride between consecutive keys
+    int64_t k_head0;        // element offset of the chunk's first head
+    int64_t k_head;         // element stride between heads
+    int64_t G;              // rows (groups) per head
+    int g;                  // group size (prefix of row j = max(j*g, 1))
+    int kstride, koff;      // key sampling
+    const float *tau;       // per-row threshold, nullptr = keep all
+    uint2 *out;             // survivors (key, index) [(row*2+half)*cap + slot]
+    int cap_half;
+    int *cnt;               // survivors per (row, half), may exceed cap
+    int64_t min_n;          // rows with prefix <= min_n are skipped
+    int n_tiles, Hc;
+};
+
+// One block: 256 consecutive groups of one head against every key of their
+// prefixes, 64 keys per step. MFMA 32x32 with keys as the A operand (rows)
+// and proxies as B (columns): lane l holds column l%32 of each 32x32 tile,
+// i.e. one group, for 16 keys -- its threshold and running survivor count
+// stay in registers. Keys stream through double-buffered LDS tiles.
+template <typename T, int D>
+__global__ void __launch_bounds__(SCAN_THREADS) k_scan(ScanParams p) {
+    constexpr int RB = D * (int)sizeof(T);     // bytes per key row
+    constexpr int KROW = RB + 16;              // LDS row stride (bank spread)
+    constexpr int NCH = RB / 64;               // 16-byte chunks per thread per tile
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int nb = p.Hc * p.n_tiles;
+    const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)nb);
+    const int hl = (int)(L / p.n_tiles);
+    const int tile = p.n_tiles - 1 - (int)(L % p.n_tiles);  // longest first
+    const int64_t j0 = (int64_t)tile * SCAN_ROWS;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int half = l >> 5;
+
+    const int64_t jlast = min(j0 + SCAN_ROWS - 1, p.G - 1);
+    const int64_t vmax = virt_count(prefix_len(jlast, p.g) > p.min_n ? prefix_len(jlast, p.g) : 0,
+                                    p.kstride, p.koff);
+
+    // this lane's two groups
+    int64_t row[2];
+    int64_t vcount[2];
+    float tau[2];
+    int cntl[2] = {0, 0};
+    for (int gb = 0; gb < 2; ++gb) {
+        const int64_t j = j0 + 64 * w + 32 * gb + (l & 31);
+        row[gb] = (int64_t)hl * p.G + j;
+        int64_t vc = 0;
+        tau[gb] = -INFINITY;
+        if (j < p.G) {
+            const int64_t n = prefix_len(j, p.g);
+            if (n > p.min_n) vc = virt_count(n, p.kstride, p.koff);
+            if (p.tau) tau[gb] = p.tau[row[gb]];
+        }
+        vcount[gb] = vc;
+    }
+
+    // proxies as resident B fragments
+    typedef typename std::conditional<std::is_same<T, float>::value, f32x4_t, bf16x8_t>::type frag_t;
+    constexpr int NKS = std::is_same<T, float>::value ? D / 8 : D / 16;
+    frag_t bq[2][NKS];
+    const T *Pb = (const T *)p.P + (int64_t)hl * p.p_head;
+    for (int gb = 0; gb < 2; ++gb) {
+        const int64_t j = j0 + 64 * w + 32 * gb + (l & 31);
+        for (int ks = 0; ks < NKS; ++ks) {
+            frag_t f;
+            if (j < p.G) {
+                const int dofs = std::is_same<T, float>::value ? 8 * ks + 4 * half : 16 * ks + 8 * half;
+                f = *(const frag_t *)(Pb + j * p.p_row + dofs);
+            } else {
+                f = frag_t{};
+            }
+            bq[gb][ks] = f;
+        }
+    }
+
+    const int64_t ntiles_k = (vmax + SCAN_KEYS - 1) / SCAN_KEYS;
+    const T *Kb = (const T *)p.K + p.k_head0 + (int64_t)hl * p.k_head;
+    unsigned char *buf0 = smem;
+    unsigned char *buf1 = smem + SCAN_KEYS * KROW;
+
+    uint4 pre[NCH];
+    auto gload = [&](int64_t kt) {
+        for (int i = 0; i < NCH; ++i) {
+            const int ch = tid + SCAN_THREADS * i;
+            const int r = ch / (RB / 16), c16 = ch % (RB / 16);
+            const int64_t v = kt * SCAN_KEYS + r;
+            if (v < vmax) {
+                const int64_t key = p.koff + (int64_t)p.kstride * v;
+                pre[i] = *(const uint4 *)((const unsigned char *)(Kb + key * p.k_row) + c16 * 16);
+            } else {
+                pre[i] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    };
+    auto lstore = [&](unsigned char *dst) {
+        for (int i = 0; i < NCH; ++i) {
+            const int ch = tid + SCAN_THREADS * i;
+            const int r = ch / (RB / 16), c16 = ch % (RB / 16);
+            *(uint4 *)(dst + r * KROW + c16 * 16) = pre[i];
+        }
+    };
+
+    if (ntiles_k > 0) {
+        gload(0);
+        lstore(buf0);
+    }
+    __syncthreads();
+
+    for (int64_t kt = 0; kt < ntiles_k; ++kt) {
+        unsigned char *cur = (kt & 1) ? buf1 : buf0;
+        unsigned char *nxt = (kt & 1) ? buf0 : buf1;
+        if (kt + 1 < ntiles_k) gload(kt + 1);
+
+        f32x16_t acc[2][2];
+        for (int a = 0; a < 2; ++a)
+            for (int b = 0; b < 2; ++b) acc[a][b] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const unsigned char *ap = cur + (kb * 32 + (l & 31)) * KROW;
+                if constexpr (std::is_same<T, float>::value) {
+                    const f32x4_t a = *(const f32x4_t *)(ap + (8 * ks + 4 * half) * 4);
+#pragma unroll
+                    for (int gb = 0; gb < 2; ++gb)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            acc[kb][gb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                a[v], bq[gb][ks][v], acc[kb][gb], 0, 0, 0);
+                } else {
+                    const bf16x8_t a = *(const bf16x8_t *)(ap + (16 * ks + 8 * half) * 2);
+#pragma unroll
+                    for (int gb = 0; gb < 2; ++gb)
+                        acc[kb][gb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            a, bq[gb][ks], acc[kb][gb], 0, 0, 0);
+                }
+            }
+        }
+
+        // keep the scores that reach the row's threshold
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int gb = 0; gb < 2; ++gb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t vk = kt * SCAN_KEYS + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+                    const float s = acc[kb][gb][v];
+                    const bool keep = (vk < vcount[gb]) && (s >= tau[gb]);
+                    if (keep) {
+                        if (cntl[gb] < p.cap_half) {
+                            const int64_t key = p.koff + (int64_t)p.kstride * vk;
+                            p.out[(row[gb] * 2 + half) * (int64_t)p.cap_half + cntl[gb]] =
+                                make_uint2(score_key(s), (uint32_t)key);
+                        }
+                        cntl[gb] += 1;
+                    }
+                }
+
+        if (kt + 1 < ntiles_k) lstore(nxt);
+        __syncthreads();
+    }
+
+    for (int gb = 0; gb < 2; ++gb) {
+        const int64_t j = j0 + 64 * w + 32 * gb + (l & 31);
+        if (j < p.G) p.cnt[row[gb] * 2 + half] = cntl[gb];
+    }
+}
+
+// -------------------------------------------------------------------- tau
+
+struct TauParams {
+    const uint2 *samp;
+    const int *scnt;
+    int samp_half;
+    float *tau;
+    int64_t G;
+    int g;
+    int64_t keep_all_n;  // rows with prefix <= this keep every key
+    int64_t rsel;        // rank of the threshold sample
+};
+
+// Per row: tau = the rsel-th best sample score (-inf when the row keeps
+// every key or has too few samples -- then k_select finds the overflow and
+// the row takes the exact fallback).
+__global__ void __launch_bounds__(SEL_THREADS) k_tau(TauParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *hist = (uint32_t *)smem;
+    uint32_t *vars = hist + (1 << SEL_LOG2NB);
+    uint32_t *red = vars + 8;
+    const int64_t r = blockIdx.x;
+    const int64_t j = r % p.G;
+    const int64_t n = prefix_len(j, p.g);
+    if (n <= p.keep_all_n) {
+        if (threadIdx.x == 0) p.tau[r] = -INFINITY;
+        return;
+    }
+    const int c0 = min(p.scnt[2 * r], p.samp_half), c1 = min(p.scnt[2 * r + 1], p.samp_half);
+    const uint32_t ns = min((uint32_t)(c0 + c1), (uint32_t)(TAU_E * SEL_THREADS));
+    if ((int64_t)ns <= p.rsel) {
+        if (threadIdx.x == 0) p.tau[r] = -INFINITY;
+        return;
+    }
+    Group<4> G{(int)threadIdx.x, red};
+    Selector<4, SEL_LOG2NB> sel{G, hist, vars};
+    uint32_t key[TAU_E], pl[TAU_E];
+    const uint2 *b0 = p.samp + (2 * r) * (int64_t)p.samp_half;
+    const uint2 *b1 = p.samp + (2 * r + 1) * (int64_t)p.samp_half;
+#pragma unroll
+    for (int e = 0; e < TAU_E; ++e) {
+        const uint32_t gi = e * SEL_THREADS + threadIdx.x;
+        uint2 x = make_uint2(0u, 0u);
+        if (gi < ns) x = gi < (uint32_t)c0 ? b0[gi] : b1[gi - c0];
+        key[e] = x.x;
+        pl[e] = x.y;
+    }
+    auto fe = [&](auto f) {
+#pragma unroll
+        for (int e = 0; e < TAU_E; ++e)
+            if (e * SEL_THREADS + threadIdx.x < ns) f(key[e], pl[e]);
+    };
+    const Rule rule = sel.select(fe, [](uint32_t x) { return x; }, ns, (uint32_t)p.rsel);
+    if (threadIdx.x == 0) p.tau[r] = key_score(rule.T);
+}
+
+// ----------------------------------------------------------------- select
+
+struct RowOut {
+    // candidate mode (Refine): list of K' indices per row
+    uint32_t *cand;
+    int64_t K;
+    // output mode (Reuse / dense): sorted rows written for every member
+    int32_t *out_idx;
+    float *out_score;
+    int top_k;
+    int H, h0;
+    int64_t S;
+    int g;
+};
+
+// Writes the selected, ordered entry `pos` of group (hl, j) to every member
+// row of the group (prefill layout).
+__device__ __forceinline__ void put_member_rows(const RowOut &o, int hl, int64_t j, uint32_t pos,
+                                                uint32_t key, uint32_t idx) {
+    const int64_t i0 = j * o.g;
+    const int64_t m = min((int64_t)o.g, o.S - i0);
+    for (int64_t t = 0; t < m; ++t) {
+        const int64_t off = ((i0 + t) * o.H + o.h0 + hl) * (int64_t)o.top_k + pos;
+        o.out_idx[off] = (int32_t)idx;
+        if (o.out_score) o.out_score[off] = key_score(key);
+    }
+}
+
+__device__ void pad_member_rows(const RowOut &o, int hl, int64_t j, uint32_t from, int tid, int nt) {
+    const int64_t i0 = j * o.g;
+    const int64_t m = min((int64_t)o.g, o.S - i0);
+    for (int64_t t = 0; t < m; ++t) {
+        const int64_t base = ((i0 + t) * o.H + o.h0 + hl) * (int64_t)o.top_k;
+        for (uint32_t pos = from + tid; pos < (uint32_t)o.top_k; pos += nt) {
+            o.out_idx[base + pos] = -1;
+            if (o.out_score) o.out_score[base + pos] = -INFINITY;
+        }
+    }
+}
+
+struct SelParams {
+    const uint2 *surv;
+    const int *cnt;
+    int cap_half;
+    int64_t G;
+    int g;
+    int64_t Ksel;     // how many to select (K for Refine, top_k otherwise)
+    int sorted_out;   // 0: candidate list, 1: sorted member rows
+    RowOut o;
+    uint32_t *fb_list;
+    uint32_t *fb_count;
+};
+
+// One block per row: the survivors of the main scan (a superset of the
+// row's best Ksel keys when the row is not queued) are held in registers and
+// the exact best min(Ksel, n) of them selected.
+__global__ void __launch_bounds__(SEL_THREADS) k_select(SelParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *hist = (uint32_t *)smem;
+    uint32_t *vars = hist + (1 << SEL_LOG2NB);
+    uint32_t *red = vars + 8;
+    uint32_t *ctr = red + 16;
+    uint32_t *bufk = ctr + 4;
+    uint32_t *bufp = bufk + MAX_TOPK;
+
+    const int64_t r = blockIdx.x;
+    const int64_t j = r % p.G;
+    const int hl = (int)(r / p.G);
+    const int64_t n = prefix_len(j, p.g);
+    const int c0 = p.cnt[2 * r], c1 = p.cnt[2 * r + 1];
+    const uint32_t msel = (uint32_t)min(p.Ksel, n);
+    if (c0 > p.cap_half || c1 > p.cap_half || (uint32_t)(c0 + c1) < msel) {
+        if (threadIdx.x == 0) {
+            const uint32_t slot = atomicAdd(p.fb_count, 1u);
+            p.fb_list[slot] = (uint32_t)r;
+        }
+        return;
+    }
+    const uint32_t ns = (uint32_t)(c0 + c1);
+    Group<4> G{(int)threadIdx.x, red};
+    Selector<4, SEL_LOG2NB> sel{G, hist, vars};
+    uint32_t key[SEL_E], pl[SEL_E];
+    const uint2 *b0 = p.surv + (2 * r) * (int64_t)p.cap_half;
+    const uint2 *b1 = p.surv + (2 * r + 1) * (int64_t)p.cap_half;
+#pragma unroll
+    for (int e = 0; e < SEL_E; ++e) {
+        const uint32_t gi = e * SEL_THREADS + threadIdx.x;
+        uint2 x = make_uint2(0u, 0u);
+        if (gi < ns) x = gi < (uint32_t)c0 ? b0[gi] : b1[gi - c0];
+        key[e] = x.x;
+        pl[e] = x.y;
+    }
+    auto fe = [&](auto f) {
+#pragma unroll
+        for (int e = 0; e < SEL_E; ++e)
+            if (e * SEL_THREADS + threadIdx.x < ns) f(key[e], pl[e]);
+    };
+    auto ident = [](uint32_t x) { return x; };
+    const Rule rule = sel.select(fe, ident, ns, msel);
+    auto fs = [&](auto f) {
+#pragma unroll
+        for (int e = 0; e < SEL_E; ++e)
+            if (e * SEL_THREADS + threadIdx.x < ns && rule.sel(key[e], pl[e])) f(key[e], pl[e]);
+    };
+    if (!p.sorted_out) {
+        if (threadIdx.x == 0) ctr[0] = 0;
+        __syncthreads();
+        uint32_t *dst = p.o.cand + r * p.o.K;
+        fs([&](uint32_t, uint32_t idx) {
+            const uint32_t slot = atomicAdd(&ctr[0], 1u);
+            if (slot < msel) dst[slot] = idx;
+        });
+    } else {
+        sel.sort_selected(fs, ident, msel, bufk, bufp,
+                          [&](uint32_t pos, uint32_t k, uint32_t idx) {
+                              put_member_rows(p.o, hl, j, pos, k, idx);
+                          });
+        pad_member_rows(p.o, hl, j, msel, threadIdx.x, SEL_THREADS);
+    }
+}
+
+// --------------------------------------------------------------- fallback
+
+struct FbParams {
+    // prefill: rows come from the queue and are rescored here
+    const uint32_t *fb_list;
+    const uint32_t *fb_count;
+    const void *P;
+    int64_t p_row, p_head;
+    const void *K;
+    int64_t k_row, k_head0, k_head;
+    int64_t G;
+    int g;
+    uint32_t *scratch;  // FB_BLOCKS rows of n_max keys
+    int64_t n_max;
+    // decode: every (sequence, head) row, scores already in `dense`
+    int decode;
+    const uint32_t *dense;
+    const int64_t *offs;  // B+1 prefix offsets of the sequences
+    int B, H;
+    int64_t Ksel;
+    int sorted_out;
+    RowOut o;
+    int D;
+};
+
+// Streaming exact selection over a whole score row in global memory (the
+// row is re-read once per narrowing pass).
+template <typename T>
+__global__ void __launch_bounds__(SEL_THREADS) k_fallback(FbParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *hist = (uint32_t *)smem;
+    uint32_t *vars = hist + (1 << SEL_LOG2NB);
+    uint32_t *red = vars + 8;
+    uint32_t *ctr = red + 16;
+    uint32_t *bufk = ctr + 4;
+    uint32_t *bufp = bufk + MAX_TOPK;
+    float *prow = (float *)(bufp + MAX_TOPK);  // D floats
+
+    Group<4> G{(int)threadIdx.x, red};
+    Selector<4, SEL_LOG2NB> sel{G, hist, vars};
+    const int tid = threadIdx.x;
+    const uint32_t nrows = p.decode ? (uint32_t)(p.B * p.H) : *p.fb_count;
+
+    for (uint32_t it = blockIdx.x; it < nrows; it += gridDim.x) {
+        const uint32_t *keys;
+        int64_t n;
+        int hl;
+        int64_t j;
+        if (!p.decode) {
+            const int64_t r = p.fb_list[it];
+            j = r % p.G;
+            hl = (int)(r / p.G);
+            n = prefix_len(j, p.g);
+            const T *pr = (const T *)p.P + hl * p.p_head + j * p.p_row;
+            for (int d = tid; d < p.D; d += SEL_THREADS) prow[d] = load_f32(pr + d);
+            __syncthreads();
+            uint32_t *dst = p.scratch + (int64_t)blockIdx.x * p.n_max;
+            const T *Kb = (const T *)p.K + p.k_head0 + (int64_t)hl * p.k_head;
+            for (int64_t c = tid; c < n; c += SEL_THREADS) {
+                const T *kr = Kb + c * p.k_row;
+                float acc = 0.f;
+                for (int d = 0; d < p.D; ++d) acc = fmaf(prow[d], load_f32(kr + d), acc);
+                dst[c] = score_key(acc);
+            }
+            __syncthreads();
+            keys = dst;
+        } else {
+            const int b = (int)(it / p.H);
+            hl = (int)(it % p.H);
+            j = b;
+            const int64_t off = p.offs[b];
+            n = p.offs[b + 1] - off;
+            keys = p.dense + off * p.H + (int64_t)hl * n;
+        }
+        const uint32_t msel = (uint32_t)min(p.Ksel, n);
+        auto fe = [&](auto f) {
+            for (int64_t c = tid; c < n; c += SEL_THREADS) f(keys[c], (uint32_t)c);
+        };
+        auto ident = [](uint32_t x) { return x; };
+        const Rule rule = sel.select(fe, ident, (uint32_t)n, msel);
+        auto fs = [&](auto f) {
+            for (int64_t c = tid; c < n; c += SEL_THREADS) {
+                const uint32_t k = keys[c];
+                if (rule.sel(k, (uint32_t)c)) f(k, (uint32_t)c);
+            }
+        };
+        const int64_t row = (int64_t)hl * (p.decode ? p.B : p.G) + j;
+        if (!p.sorted_out) {
+            if (tid == 0) ctr[0] = 0;
+            __syncthreads();
+            uint32_t *dst = p.o.cand + row * p.o.K;
+            fs([&](uint32_t, uint32_t idx) {
+                const uint32_t slot = atomicAdd(&ctr[0], 1u);
+                if (slot < msel) dst[slot] = idx;
+            });
+        } else if (!p.decode) {
+            sel.sort_selected(fs, ident, msel, bufk, bufp,
+                              [&](uint32_t pos, uint32_t k, uint32_t idx) {
+                                  put_member_rows(p.o, hl, j, pos, k, idx);
+                              });
+            pad_member_rows(p.o, hl, j, msel, tid, SEL_THREADS);
+        } else {
+            // decode member rows: b*g .. b*g+g-1
+            const RowOut &o = p.o;
+            sel.sort_selected(fs, ident, msel, bufk, bufp,
+                              [&](uint32_t pos, uint32_t k, uint32_t idx) {
+                                  for (int t = 0; t < o.g; ++t) {
+                                      const int64_t off =
+                                          (((int64_t)j * o.g + t) * o.H + hl) * (int64_t)o.top_k + pos;
+                                      o.out_idx[off] = (int32_t)idx;
+                                      if (o.out_score) o.out_score[off] = key_score(k);
+                                  }
+                              });
+            for (int t = 0; t < o.g; ++t) {
+                const int64_t base = (((int64_t)j * o.g + t) * o.H + hl) * (int64_t)o.top_k;
+                for (uint32_t pos = msel + tid; pos < (uint32_t)o.top_k; pos += SEL_THREADS) {
+                    o.out_idx[base + pos] = -1;
+                    if (o.out_score) o.out_score[base + pos] = -INFINITY;
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------ decode scan
+
+struct DecScanParams {
+    const void *P;   // (H, B, D) proxies
+    const void *kc;  // (sum ctx, H, D)
+    const int64_t *offs;
+    int B, H;
+    int64_t max_chunks;
+    uint32_t *dense;  // row (b, h) at offs[b]*H + h*ctx_b
+};
+
+// Streams the key cache once: thread task = (token, head) full dot product
+// of the head's proxy with that key row. Block = (sequence, 512-token chunk).
+template <typename T, int D>
+__global__ void __launch_bounds__(DEC_THREADS) k_decode_scan(DecScanParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    float *pr = (float *)smem;  // H x D proxies of this sequence
+    const int b = (int)(blockIdx.x / p.max_chunks);
+    const int64_t chunk = blockIdx.x % p.max_chunks;
+    const int64_t off = p.offs[b];
+    const int64_t ctx = p.offs[b + 1] - off;
+    const int64_t t0 = chunk * DEC_TOKENS;
+    if (t0 >= ctx) return;
+    const T *P = (const T *)p.P;
+    for (int e = threadIdx.x; e < p.H * D; e += DEC_THREADS) {
+        const int h = e / D, d = e % D;
+        pr[e] = load_f32(P + ((int64_t)h * p.B + b) * D + d);
+    }
+    __syncthreads();
+    const int64_t ntok = min((int64_t)DEC_TOKENS, ctx - t0);
+    const int64_t ntask = ntok * p.H;
+    const T *kc = (const T *)p.kc;
+    for (int64_t task = threadIdx.x; task < ntask; task += DEC_THREADS) {
+        const int64_t tok = t0 + task / p.H;
+        const int h = (int)(task % p.H);
+        const T *kr = kc + ((off + tok) * p.H + h) * (int64_t)D;
+        const float *ph = pr + h * D;
+        float acc = 0.f;
+        constexpr int PER = 16 / (int)sizeof(T);
+#pragma unroll 4
+        for (int d0 = 0; d0 < D; d0 += PER) {
+            const uint4 raw = *(const uint4 *)(kr + d0);
+            if constexpr (std::is_same<T, float>::value) {
+                acc = fmaf(ph[d0 + 0], __uint_as_float(raw.x), acc);
+                acc = fmaf(ph[d0 + 1], __uint_as_float(raw.y), acc);
+                acc = fmaf(ph[d0 + 2], __uint_as_float(raw.z), acc);
+                acc = fmaf(ph[d0 + 3], __uint_as_float(raw.w), acc);
+            } else {
+                const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2) {
+                    acc = fmaf(ph[d0 + 2 * q2], __uint_as_float(wds[q2] << 16), acc);
+                    acc = fmaf(ph[d0 + 2 * q2 + 1], __uint_as_float(wds[q2] & 0xFFFF0000u), acc);
+                }
+            }
+        }
+        p.dense[off * p.H + (int64_t)h * ctx + tok] = score_key(acc);
+    }
+}
+
+// ----------------------------------------------------------------- refine
+
+struct RefParams {
+    const void *q;
+    const void *K;
+    const uint32_t *cand;  // (groups, Kc) candidate lists
+    int64_t Kc;            // list stride (K)
+    int H, h0;             // heads of the tensors, first head of this pass
+    int Hc;                // heads in this pass
+    int64_t NG;            // groups per head (prefill: G; decode: B)
+    int g;
+    int64_t S;             // prefill sequence length
+    int decode;
+    const int64_t *offs;   // decode sequence offsets
+    int nqw;               // queries (wavefronts) per block
+    int nqb;               // blocks per group
+    int top_k;
+    int reg_bytes;         // per-wave LDS region
+    int32_t *out_idx;
+    float *out_score;
+};
+
+// One block per (group, block of <= 8 member queries): gathers the keys of
+// the group's candidate list, scores them against the member queries on MFMA
+// (16x16: 16 candidates x 16 query columns, members in the first columns)
+// into LDS, then every wavefront selects and orders its own query's top_k.
+template <typename T, int D>
+__global__ void __launch_bounds__(512) k_refine(RefParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int nblk = (int)(p.NG * p.Hc) * p.nqb;
+    const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)nblk);
+    const int64_t grp = L / p.nqb;
+    const int qb = (int)(L % p.nqb);
+    const int hl = (int)(grp / p.NG);
+    const int64_t j = grp % p.NG;
+    const int h = p.h0 + hl;
+    int64_t qrow0, m, kbase, n;
+    if (!p.decode) {
+        qrow0 = j * p.g;
+        m = min((int64_t)p.g, p.S - qrow0);
+        kbase = 0;
+        n = prefix_len(j, p.g);
+    } else {
+        qrow0 = j * p.g;
+        m = p.g;
+        kbase = p.offs[j];
+        n = p.offs[j + 1] - kbase;
+    }
+    const int nc = (int)min(p.Kc, n);
+    const int q0 = qb * p.nqw;
+    const int nq = (int)min((int64_t)p.nqw, m - q0);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int nthreads = p.nqw * 64;
+
+    uint32_t *cl = (uint32_t *)smem;                    // candidate list (Kc)
+    unsigned char *regs = smem + ((p.Kc * 4 + 15) & ~15);
+    const uint32_t *src = p.cand + grp * p.Kc;
+    for (int i = tid; i < nc; i += nthreads) cl[i] = src[i];
+
+    typedef typename std::conditional<std::is_same<T, float>::value, f32x4_t, bf16x8_t>::type frag_t;
+    constexpr bool F32 = std::is_same<T, float>::value;
+    constexpr int NKS = F32 ? D / 16 : D / 32;
+    const T *Q = (const T *)p.q;
+    const T *Kx = (const T *)p.K;
+    const int qcol = l & 15, lq = l >> 4;
+    frag_t bq[NKS];
+    for (int ks = 0; ks < NKS; ++ks) {
+        if (qcol < nq) {
+            const int dofs = F32 ? 16 * ks + 4 * lq : 32 * ks + 8 * lq;
+            bq[ks] = *(const frag_t *)(Q + ((qrow0 + q0 + qcol) * p.H + h) * (int64_t)D + dofs);
+        } else {
+            bq[ks] = frag_t{};
+        }
+    }
+    __syncthreads();
+
+    const int nblocks = (nc + 15) / 16;
+    for (int blk = w; blk < nblocks; blk += p.nqw) {
+        const int pidx = blk * 16 + qcol;
+        const bool pv = pidx < nc;
+        // a candidate list entry is always a key of the prefix; the clamp
+        // keeps the gather inside the tensor whatever the list holds
+        const uint32_t c = pv ? min(cl[pidx], (uint32_t)(n - 1)) : 0u;
+        const T *kr = Kx + ((kbase + c) * p.H + h) * (int64_t)D;
+        frag_t a[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int dofs = F32 ? 16 * ks + 4 * lq : 32 * ks + 8 * lq;
+            a[ks] = pv ? *(const frag_t *)(kr + dofs) : frag_t{};
+        }
+        f32x4_t acc = f32x4_t{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            if constexpr (F32) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ks][v], bq[ks][v], acc, 0, 0, 0);
+            } else {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bq[ks], acc, 0, 0, 0);
+            }
+        }
+        // lane holds query column qcol, candidates blk*16 + 4*lq + v
+        if (qcol < nq) {
+            uint32_t *dst = (uint32_t *)(regs + qcol * p.reg_bytes);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int pp = blk * 16 + 4 * lq + v;
+                if (pp < nc) dst[pp] = score_key(acc[v]);
+            }
+        }
+    }
+    __syncthreads();
+    if (w >= nq) return;
+
+    // this wavefront's query: exact sorted top_k of its nc candidate scores
+    unsigned char *my = regs + w * p.reg_bytes;
+    uint32_t key[REF_E];
+#pragma unroll
+    for (int e = 0; e < REF_E; ++e) {
+        const int pp = e * 64 + l;
+        key[e] = pp < nc ? ((const uint32_t *)my)[pp] : 0u;
+    }
+    wave_lds_sync();
+    uint32_t *hist = (uint32_t *)my;                  // 1024 words
+    uint32_t *vars = hist + (1 << REF_LOG2NB);
+    uint32_t *red = vars + 8;
+    uint32_t *bufk = red + 16;                        // top_k words
+    uint16_t *bufp = (uint16_t *)(bufk + p.top_k);    // top_k positions
+    Group<1> G{l, red};
+    Selector<1, REF_LOG2NB> sel{G, hist, vars};
+    auto fe = [&](auto f) {
+#pragma unroll
+        for (int e = 0; e < REF_E; ++e)
+            if (e * 64 + l < nc) f(key[e], (uint32_t)(e * 64 + l));
+    };
+    auto idx_of = [&](uint32_t pos) { return cl[pos]; };
+    const uint32_t msel = (uint32_t)min(p.top_k, nc);
+    const Rule rule = sel.select(fe, idx_of, (uint32_t)nc, msel);
+    auto fs = [&](auto f) {
+#pragma unroll
+        for (int e = 0; e < REF_E; ++e) {
+            const uint32_t pos = e * 64 + l;
+            if (pos < (uint32_t)nc && rule.sel(key[e], cl[pos])) f(key[e], pos);
+        }
+    };
+    const int64_t obase = ((qrow0 + q0 + w) * p.H + h) * (int64_t)p.top_k;
+    sel.sort_selected(fs, idx_of, msel, bufk, bufp,
+                      [&](uint32_t pos, uint32_t k, uint32_t pl) {
+                          p.out_idx[obase + pos] = (int32_t)cl[pl];
+                          if (p.out_score) p.out_score[obase + pos] = key_score(k);
+                      });
+    for (int pos = msel + l; pos < p.top_k; pos += 64) {
+        p.out_idx[obase + pos] = -1;
+        if (p.out_score) p.out_score[obase + pos] = -INFINITY;
+    }
+}
+
+// ==================================================================== host
+
+struct Plan {
+    int64_t S;
+    int H, D, top_k, g, mode, dtype;
+    bool dense;
+    int64_t K, Ksel, G, n_max;
+    int kstride;
+    int64_t rsel;
+    int cap_half, samp_half;
+    int64_t keep_all_n;
+    int n_tiles;
+    size_t esz;
+    // per-head bytes of each workspace array
+    size_t b_P, b_tau, b_cnt, b_scnt, b_surv, b_samp, b_cand, b_fbl;
+    size_t fixed;  // fb_count + fallback scratch
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t pow2_floor(int64_t x) {
+    int64_t p = 1;
+    while (p * 2 <= x) p *= 2;
+    return p;
+}
+
+int candidate_count(int32_t top_k, double ratio, int64_t *K) {
+    if (top_k < 1 || !(ratio > 0.0) || !std::isfinite(ratio)) return PIVOT_EINVAL;
+    const double prod = (double)top_k * ratio;
+    if (!(prod < 9.0e18)) return PIVOT_EINVAL;
+    const int64_t k = (int64_t)floor(prod);
+    if (k < top_k) return PIVOT_EINVAL;
+    *K = k;
+    return PIVOT_OK;
+}
+
+int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio, int mode,
+              int dtype, bool dense) {
+    if (S < 1 || S > (int64_t)INT32_MAX - 1 || H < 1 || g < 1) return PIVOT_EINVAL;
+    if (dtype != PIVOT_F32 && dtype != PIVOT_BF16) return PIVOT_EINVAL;
+    if (mode != PIVOT_REFINE && mode != PIVOT_REUSE) return PIVOT_EINVAL;
+    if (top_k < 1) return PIVOT_EINVAL;
+    int64_t K = top_k;
+    if (!dense) {
+        int rc = candidate_count(top_k, ratio, &K);
+        if (rc) return rc;
+    }
+    if (D != 64 && D != 128) return PIVOT_EUNSUPPORTED;
+    if (top_k > MAX_TOPK || K > MAX_K) return PIVOT_EUNSUPPORTED;
+    pl.S = S;
+    pl.H = H;
+    pl.D = D;
+    pl.top_k = top_k;
+    pl.g = dense ? 1 : g;
+    pl.mode = dense ? PIVOT_REUSE : mode;
+    pl.dtype = dtype;
+    pl.dense = dense;
+    pl.K = K;
+    pl.Ksel = (pl.mode == PIVOT_REFINE) ? K : top_k;
+    pl.G = (S + pl.g - 1) / pl.g;
+    pl.n_max = std::max<int64_t>((pl.G - 1) * pl.g, 1);
+    pl.esz = dtype == PIVOT_BF16 ? 2 : 4;
+    // sampling: about 64 expected samples above the Ksel-th best key
+    int64_t s = std::min<int64_t>(64, std::max<int64_t>(1, pow2_floor(std::max<int64_t>(1, pl.Ksel / 64))));
+    while ((pl.n_max + s - 1) / s > 4096 - 16) s *= 2;  // samples fit the registers of k_tau
+    pl.kstride = (int)s;
+    const double mu = (double)pl.Ksel / (double)s;
+    const double z = 4.0;
+    const double root = (z + sqrt(z * z + 4.0 * mu)) / 2.0;
+    pl.rsel = (int64_t)ceil(root * root) + 1;
+    const double X = (double)pl.rsel * s, sig = sqrt((double)pl.rsel) * s;
+    int64_t ch = (int64_t)ceil((X + 5.0 * sig) / 2.0 + 4.0 * sqrt(X / 2.0)) + 16;
+    ch = (ch + 63) / 64 * 64;
+    ch = std::min<int64_t>(ch, (int64_t)SEL_E * SEL_THREADS / 2);
+    pl.cap_half = (int)ch;
+    pl.keep_all_n = 2 * (int64_t)pl.cap_half - 16;
+    const int64_t vmax = (pl.n_max + s - 1) / s;
+    pl.samp_half = (int)((vmax + 1) / 2 + 8);
+    pl.n_tiles = (int)((pl.G + SCAN_ROWS - 1) / SCAN_ROWS);
+    const size_t rows = (size_t)pl.G;
+    pl.b_P = dense ? 0 : align256(rows * D * pl.esz);
+    pl.b_tau = align256(rows * 4);
+    pl.b_cnt = align256(rows * 8);
+    pl.b_scnt = align256(rows * 8);
+    pl.b_surv = align256(rows * 2 * (size_t)pl.cap_half * 8);
+    pl.b_samp = pl.n_max > pl.keep_all_n ? align256(rows * 2 * (size_t)pl.samp_half * 8) : 0;
+    pl.b_cand = pl.mode == PIVOT_REFINE ? align256(rows * (size_t)K * 4) : 0;
+    pl.b_fbl = align256(rows * 4);
+    pl.fixed = 256 + align256((size_t)FB_BLOCKS * (size_t)pl.n_max * 4);
+    return PIVOT_OK;
+}
+
+size_t per_head_bytes(const Plan &pl) {
+    return pl.b_P + pl.b_tau + pl.b_cnt + pl.b_scnt + pl.b_surv + pl.b_samp + pl.b_cand + pl.b_fbl;
+}
+
+hipError_t set_lds(const void *fn, size_t bytes) {
+    if (bytes <= 65536) return hipSuccess;
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+#define HIP_TRY(x)                                    \
+    do {                                              \
+        if ((x) != hipSuccess) return PIVOT_EHIP;     \
+    } while (0)
+
+size_t sel_lds_bytes(int D) {
+    return ((size_t)(1 << SEL_LOG2NB) + 8 + 16 + 4 + 2 * MAX_TOPK) * 4 + (size_t)D * 4;
+}
+
+size_t ref_reg_bytes(int64_t K, int top_k) {
+    size_t a = (size_t)K * 4;
+    size_t b = ((size_t)(1 << REF_LOG2NB) + 8 + 16) * 4 + (size_t)top_k * 6;
+    return (std::max(a, b) + 15) & ~(size_t)15;
+}
+
+template <typename T, int D>
+int launch_refine(const RefParams &rp, int nblocks, size_t lds, hipStream_t st) {
+    HIP_TRY(set_lds((const void *)k_refine<T, D>, lds));
+    hipLaunchKernelGGL((k_refine<T, D>), dim3(nblocks), dim3(64 * rp.nqw), lds, st, rp);
+    HIP_TRY(hipGetLastError());
+    return PIVOT_OK;
+}
+
+template <typename T>
+int dispatch_refine(int D, const RefParams &rp, int nblocks, size_t lds, hipStream_t st) {
+    return D == 64 ? launch_refine<T, 64>(rp, nblocks, lds, st) : launch_refine<T, 128>(rp, nblocks, lds, st);
+}
+
+template <typename T, int D>
+int launch_scan(const ScanParams &sp, hipStream_t st) {
+    const size_t lds = 2 * SCAN_KEYS * ((size_t)D * sizeof(T) + 16);
+    HIP_TRY(set_lds((const void *)k_scan<T, D>, lds));
+    hipLaunchKernelGGL((k_scan<T, D>), dim3(sp.Hc * sp.n_tiles), dim3(SCAN_THREADS), lds, st, sp);
+    HIP_TRY(hipGetLastError());
+    return PIVOT_OK;
+}
+
+template <typename T>
+int dispatch_scan(int D, const ScanParams &sp, hipStream_t st) {
+    return D == 64 ? launch_scan<T, 64>(sp, st) : launch_scan<T, 128>(sp, st);
+}
+
+template <typename T>
+int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float *out_score,
+                unsigned char *ws, size_t ws_bytes, hipStream_t st) {
+    const size_t phb = per_head_bytes(pl);
+    if (ws_bytes < pl.fixed + phb) return PIVOT_EWORKSPACE;
+    const int Hc_max = (int)std::min<size_t>((size_t)pl.H, (ws_bytes - pl.fixed) / phb);
+    uint32_t *fb_count = (uint32_t *)ws;
+    uint32_t *scratch = (uint32_t *)(ws + 256);
+    unsigned char *base = ws + pl.fixed;
+    const int64_t D = pl.D;
+
+    for (int h0 = 0; h0 < pl.H; h0 += Hc_max) {
+        const int Hc = std::min(Hc_max, pl.H - h0);
+        const int64_t rows = (int64_t)Hc * pl.G;
+        unsigned char *cur = base;
+        auto take = [&](size_t per_head) {
+            unsigned char *r = cur;
+            cur += per_head * Hc;
+            return r;
+        };
+        T *P = (T *)take(pl.b_P);
+        float *tau = (float *)take(pl.b_tau);
+        int *cnt = (int *)take(pl.b_cnt);
+        int *scnt = (int *)take(pl.b_scnt);
+        uint2 *surv = (uint2 *)take(pl.b_surv);
+        uint2 *samp = (uint2 *)take(pl.b_samp);
+        uint32_t *cand = (uint32_t *)take(pl.b_cand);
+        uint32_t *fbl = (uint32_t *)take(pl.b_fbl);
+
+        ScanParams sp{};
+        if (pl.dense) {
+            sp.P = q + (int64_t)h0 * D;
+            sp.p_row = (int64_t)pl.H * D;
+            sp.p_head = D;
+        } else {
+            const int64_t total = rows * D;
+            const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+            hipLaunchKernelGGL((k_proxy<T>), dim3(blocks), dim3(256), 0, st, q, pl.S, pl.H, pl.D, pl.g,
+                               h0, Hc, pl.G, P);
+            HIP_TRY(hipGetLastError());
+            sp.P = P;
+            sp.p_row = D;
+            sp.p_head = pl.G * D;
+        }
+        sp.K = k;
+        sp.k_row = (int64_t)pl.H * D;
+        sp.k_head0 = (int64_t)h0 * D;
+        sp.k_head = D;
+        sp.G = pl.G;
+        sp.g = pl.g;
+        sp.n_tiles = pl.n_tiles;
+        sp.Hc = Hc;
+        hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, st, fb_count, (int64_t)1);
+        HIP_TRY(hipGetLastError());
+
+        // sample pass + thresholds
+        if (pl.n_max > pl.keep_all_n) {
+            ScanParams ss = sp;
+            ss.kstride = pl.kstride;
+            ss.koff = pl.kstride - 1;
+            ss.tau = nullptr;
+            ss.out = samp;
+            ss.cap_half = pl.samp_half;
+            ss.cnt = scnt;
+            ss.min_n = pl.keep_all_n;
+            int rc = dispatch_scan<T>(pl.D, ss, st);
+            if (rc) return rc;
+        }
+        {
+            TauParams tp{samp, scnt, pl.samp_half, tau, pl.G, pl.g, pl.keep_all_n, pl.rsel};
+            const size_t lds = ((size_t)(1 << SEL_LOG2NB) + 8 + 16) * 4;
+            hipLaunchKernelGGL(k_tau, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, tp);
+            HIP_TRY(hipGetLastError());
+        }
+        // main pass
+        {
+            ScanParams sm = sp;
+            sm.kstride = 1;
+            sm.koff = 0;
+            sm.tau = tau;
+            sm.out = surv;
+            sm.cap_half = pl.cap_half;
+            sm.cnt = cnt;
+            sm.min_n = 0;
+            int rc = dispatch_scan<T>(pl.D, sm, st);
+            if (rc) return rc;
+        }
+        RowOut ro{};
+        ro.cand = cand;
+        ro.K = pl.K;
+        ro.out_idx = out_idx;
+        ro.out_score = out_score;
+        ro.top_k = pl.top_k;
+        ro.H = pl.H;
+        ro.h0 = h0;
+        ro.S = pl.S;
+        ro.g = pl.g;
+        const int sorted_out = pl.mode == PIVOT_REUSE ? 1 : 0;
+        {
+            SelParams se{surv, cnt, pl.cap_half, pl.G, pl.g, pl.Ksel, sorted_out, ro, fbl, fb_count};
+            const size_t lds = sel_lds_bytes(0);
+            hipLaunchKernelGGL(k_select, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, se);
+            HIP_TRY(hipGetLastError());
+        }
+        {
+            FbParams fp{};
+            fp.fb_list = fbl;
+            fp.fb_count = fb_count;
+            fp.P = sp.P;
+            fp.p_row = sp.p_row;
+            fp.p_head = sp.p_head;
+            fp.K = k;
+            fp.k_row = sp.k_row;
+            fp.k_head0 = sp.k_head0;
+            fp.k_head = sp.k_head;
+            fp.G = pl.G;
+            fp.g = pl.g;
+            fp.scratch = scratch;
+            fp.n_max = pl.n_max;
+            fp.decode = 0;
+            fp.Ksel = pl.Ksel;
+            fp.sorted_out = sorted_out;
+            fp.o = ro;
+            fp.D = pl.D;
+            const size_t lds = sel_lds_bytes(pl.D);
+            hipLaunchKernelGGL((k_fallback<T>), dim3(FB_BLOCKS), dim3(SEL_THREADS), lds, st, fp);
+            HIP_TRY(hipGetLastError());
+        }
+        if (pl.mode == PIVOT_REFINE) {
+            RefParams rp{};
+            rp.q = q;
+            rp.K = k;
+            rp.cand = cand;
+            rp.Kc = pl.K;
+            rp.H = pl.H;
+            rp.h0 = h0;
+            rp.Hc = Hc;
+            rp.NG = pl.G;
+            rp.g = pl.g;
+            rp.S = pl.S;
+            rp.decode = 0;
+            rp.offs = nullptr;
+            rp.nqw = std::min(pl.g, 8);
+            rp.nqb = (pl.g + rp.nqw - 1) / rp.nqw;
+            rp.top_k = pl.top_k;
+            rp.reg_bytes = (int)ref_reg_bytes(pl.K, pl.top_k);
+            rp.out_idx = out_idx;
+            rp.out_score = out_score;
+            const size_t lds = ((size_t)pl.K * 4 + 15) / 16 * 16 + (size_t)rp.nqw * rp.reg_bytes;
+            const int nblocks = (int)(rows * rp.nqb);
+            int rc = dispatch_refine<T>(pl.D, rp, nblocks, lds, st);
+            if (rc) return rc;
+        }
+    }
+    return PIVOT_OK;
+}
+
+struct DecPlan {
+    int B, g, H, D, top_k, mode, dtype;
+    int64_t K, Ksel, total, max_ctx;
+    size_t esz;
+    size_t o_offs, o_P, o_dense, o_cand, bytes;
+};
+
+int make_dec_plan(DecPlan &dp, int B, const int64_t *ctx, int g, int H, int D, int top_k,
+                  double ratio, int mode, int dtype) {
+    if (B < 1 || g < 1 || H < 1 || top_k < 1 || !ctx) return PIVOT_EINVAL;
+    if (dtype != PIVOT_F32 && dtype != PIVOT_BF16) return PIVOT_EINVAL;
+    if (mode != PIVOT_REFINE && mode != PIVOT_REUSE) return PIVOT_EINVAL;
+    int64_t K;
+    int rc = candidate_count(top_k, ratio, &K);
+    if (rc) return rc;
+    int64_t total = 0, mx = 0;
+    for (int b = 0; b < B; ++b) {
+        if (ctx[b] < 1 || ctx[b] > (int64_t)INT32_MAX) return PIVOT_EINVAL;
+        total += ctx[b];
+        mx = std::max(mx, ctx[b]);
+    }
+    if ((int64_t)B * g > (int64_t)INT32_MAX) return PIVOT_EINVAL;
+    if (D != 64 && D != 128) return PIVOT_EUNSUPPORTED;
+    if (top_k > MAX_TOPK || K > MAX_K) return PIVOT_EUNSUPPORTED;
+    dp.B = B;
+    dp.g = g;
+    dp.H = H;
+    dp.D = D;
+    dp.top_k = top_k;
+    dp.mode = mode;
+    dp.dtype = dtype;
+    dp.K = K;
+    dp.Ksel = mode == PIVOT_REFINE ? K : top_k;
+    dp.total = total;
+    dp.max_ctx = mx;
+    dp.esz = dtype == PIVOT_BF16 ? 2 : 4;
+    size_t off = 0;
+    dp.o_offs = off;
+    off += align256((size_t)(B + 1) * 8);
+    dp.o_P = off;
+    off += align256((size_t)H * B * D * dp.esz);
+    dp.o_dense = off;
+    off += align256((size_t)total * H * 4);
+    dp.o_cand = off;
+    off += mode == PIVOT_REFINE ? align256((size_t)H * B * K * 4) : 0;
+    dp.bytes = off;
+    return PIVOT_OK;
+}
+
+template <typename T, int D>
+int launch_dec_scan(const DecScanParams &ds, int nblocks, int H, hipStream_t st) {
+    const size_t lds = (size_t)H * D * 4;
+    HIP_TRY(set_lds((const void *)k_decode_scan<T, D>, lds));
+    hipLaunchKernelGGL((k_decode_scan<T, D>), dim3(nblocks), dim3(DEC_THREADS), lds, st, ds);
+    HIP_TRY(hipGetLastError());
+    return PIVOT_OK;
+}
+
+template <typename T>
+int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, int32_t *out_idx,
+               float *out_score, unsigned char *ws, hipStream_t st) {
+    int64_t *offs = (int64_t *)(ws + dp.o_offs);
+    T *P = (T *)(ws + dp.o_P);
+    uint32_t *dense = (uint32_t *)(ws + dp.o_dense);
+    uint32_t *cand = (uint32_t *)(ws + dp.o_cand);
+    // prefix offsets travel as kernel arguments, 64 per launch
+    {
+        int64_t run = 0;
+        for (int s0 = 0; s0 <= dp.B; s0 += 64) {
+            Offsets64 a{};
+            a.start = s0;
+            a.count = std::min(64, dp.B + 1 - s0);
+            for (int t = 0; t < a.count; ++t) {
+                const int b = s0 + t;
+                if (b == 0) run = 0;
+                a.v[t] = run;
+                if (b < dp.B) run += ctx[b];
+            }
+            hipLaunchKernelGGL(k_put_offsets, dim3(1), dim3(64), 0, st, offs, a);
+            HIP_TRY(hipGetLastError());
+        }
+    }
+    {
+        const int64_t total = (int64_t)dp.H * dp.B * dp.D;
+        const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+        hipLaunchKernelGGL((k_proxy<T>), dim3(blocks), dim3(256), 0, st, q, (int64_t)dp.B * dp.g, dp.H,
+                           dp.D, dp.g, 0, dp.H, (int64_t)dp.B, P);
+        HIP_TRY(hipGetLastError());
+    }
+    {
+        DecScanParams ds{P, kc, offs, dp.B, dp.H, (dp.max_ctx + DEC_TOKENS - 1) / DEC_TOKENS, dense};
+        const int nblocks = (int)(dp.B * ds.max_chunks);
+        int rc = dp.D == 64 ? launch_dec_scan<T, 64>(ds, nblocks, dp.H, st)
+                            : launch_dec_scan<T, 128>(ds, nblocks, dp.H, st);
+        if (rc) return rc;
+    }
+    RowOut ro{};
+    ro.cand = cand;
+    ro.K = dp.K;
+    ro.out_idx = out_idx;
+    ro.out_score = out_score;
+    ro.top_k = dp.top_k;
+    ro.H = dp.H;
+    ro.h0 = 0;
+    ro.S = (int64_t)dp.B * dp.g;
+    ro.g = dp.g;
+    {
+        FbParams fp{};
+        fp.decode = 1;
+        fp.dense = dense;
+        fp.offs = offs;
+        fp.B = dp.B;
+        fp.H = dp.H;
+        fp.Ksel = dp.Ksel;
+        fp.sorted_out = dp.mode == PIVOT_REUSE ? 1 : 0;
+        fp.o = ro;
+        fp.D = dp.D;
+        const size_t lds = sel_lds_bytes(dp.D);
+        const int nrows = dp.B * dp.H;
+        hipLaunchKernelGGL((k_fallback<T>), dim3(nrows), dim3(SEL_THREADS), lds, st, fp);
+        HIP_TRY(hipGetLastError());
+    }
+    if (dp.mode == PIVOT_REFINE) {
+        RefParams rp{};
+        rp.q = q;
+        rp.K = kc;
+        rp.cand = cand;
+        rp.Kc = dp.K;
+        rp.H = dp.H;
+        rp.h0 = 0;
+        rp.Hc = dp.H;
+        rp.NG = dp.B;
+        rp.g = dp.g;
+        rp.S = (int64_t)dp.B * dp.g;
+        rp.decode = 1;
+        rp.offs = offs;
+        rp.nqw = std::min(dp.g, 8);
+        rp.nqb = (dp.g + rp.nqw - 1) / rp.nqw;
+        rp.top_k = dp.top_k;
+        rp.reg_bytes = (int)ref_reg_bytes(dp.K, dp.top_k);
+        rp.out_idx = out_idx;
+        rp.out_score = out_score;
+        const size_t lds = ((size_t)dp.K * 4 + 15) / 16 * 16 + (size_t)rp.nqw * rp.reg_bytes;
+        const int nblocks = dp.B * dp.H * rp.nqb;
+        int rc = dispatch_refine<T>(dp.D, rp, nblocks, lds, st);
+        if (rc) return rc;
+    }
+    return PIVOT_OK;
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+
+extern "C" {
+
+const char *pivot_status_string(int status) {
+    switch (status) {
+    case PIVOT_OK: return "ok";
+    case PIVOT_EINVAL: return "invalid argument";
+    case PIVOT_EUNSUPPORTED: return "unsupported size or parameter";
+    case PIVOT_EWORKSPACE: return "workspace too small";
+    case PIVOT_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int pivot_candidate_count(int32_t top_k, double candidate_ratio, int64_t *K_out) {
+    if (!K_out) return PIVOT_EINVAL;
+    int64_t K;
+    int rc = candidate_count(top_k, candidate_ratio, &K);
+    if (rc) return rc;
+    *K_out = K;
+    return PIVOT_OK;
+}
+
+size_t pivot_prefill_workspace_bytes(int64_t S, int32_t H, int32_t D, int32_t top_k, int32_t g,
+                                     double candidate_ratio, int32_t mode, int32_t dtype) {
+    Plan pl;
+    if (make_plan(pl, S, H, D, top_k, g, candidate_ratio, mode, dtype, false)) return 0;
+    return pl.fixed + per_head_bytes(pl) * (size_t)H;
+}
+
+size_t dense_index_workspace_bytes(int64_t S, int32_t H, int32_t D, int32_t top_k, int32_t dtype) {
+    Plan pl;
+    if (make_plan(pl, S, H, D, top_k, 1, 1.0, PIVOT_REUSE, dtype, true)) return 0;
+    return pl.fixed + per_head_bytes(pl) * (size_t)H;
+}
+
+static int prefill_common(const void *q, const void *k, int32_t dtype, int64_t S, int32_t H, int32_t D,
+                          int32_t top_k, int32_t g, double ratio, int32_t mode, int32_t *out_idx,
+                          float *out_score, void *workspace, size_t workspace_bytes, void *stream,
+                          bool dense) {
+    Plan pl;
+    int rc = make_plan(pl, S, H, D, top_k, g, ratio, mode, dtype, dense);
+    if (rc) return rc;
+    if (!q || !k || !out_idx) return PIVOT_EINVAL;
+    if (!workspace) return PIVOT_EWORKSPACE;
+    if (workspace_bytes < pl.fixed + per_head_bytes(pl)) return PIVOT_EWORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == PIVOT_BF16)
+        return run_prefill<bf16_t>(pl, (const bf16_t *)q, (const bf16_t *)k, out_idx, out_score,
+                                   (unsigned char *)workspace, workspace_bytes, st);
+    return run_prefill<float>(pl, (const float *)q, (const float *)k, out_idx, out_score,
+                              (unsigned char *)workspace, workspace_bytes, st);
+}
+
+int pivot_index_prefill(const void *q, const void *k, int32_t dtype, int64_t S, int32_t H, int32_t D,
+                        int32_t top_k, int32_t g, double candidate_ratio, int32_t mode, int32_t *out_idx,
+                        float *out_score, void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_common(q, k, dtype, S, H, D, top_k, g, candidate_ratio, mode, out_idx, out_score,
+                          workspace, workspace_bytes, stream, false);
+}
+
+int dense_index(const void *q, const void *k, int32_t dtype, int64_t S, int32_t H, int32_t D, int32_t top_k,
+                int32_t *out_idx, float *out_score, void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_common(q, k, dtype, S, H, D, top_k, 1, 1.0, PIVOT_REUSE, out_idx, out_score, workspace,
+                          workspace_bytes, stream, true);
+}
+
+size_t pivot_decode_workspace_bytes(int32_t B, const int64_t *ctx_lens_host, int32_t g, int32_t H, int32_t D,
+                                    int32_t top_k, double candidate_ratio, int32_t mode, int32_t dtype) {
+    DecPlan dp;
+    if (make_dec_plan(dp, B, ctx_lens_host, g, H, D, top_k, candidate_ratio, mode, dtype)) return 0;
+    return dp.bytes;
+}
+
+int pivot_index_decode(const void *q, const void *k_cache, int32_t dtype, const int64_t *ctx_lens_host,
+                       int32_t B, int32_t g, int32_t H, int32_t D, int32_t top_k, double candidate_ratio,
+                       int32_t mode, int32_t *out_idx, float *out_score, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    DecPlan dp;
+    int rc = make_dec_plan(dp, B, ctx_lens_host, g, H, D, top_k, candidate_ratio, mode, dtype);
+    if (rc) return rc;
+    if (!q || !k_cache || !out_idx) return PIVOT_EINVAL;
+    if (!workspace || workspace_bytes < dp.bytes) return PIVOT_EWORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == PIVOT_BF16)
+        return run_decode<bf16_t>(dp, ctx_lens_host, (const bf16_t *)q, (const bf16_t *)k_cache, out_idx,
+                                  out_score, (unsigned char *)workspace, st);
+    return run_decode<float>(dp, ctx_lens_host, (const float *)q, (const float *)k_cache, out_idx, out_score,
+                             (unsigned char *)workspace, st);
+}
+
+}  // extern "C"
