@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the PIVOT indexer on one MI355X.
+
+Workload (the metric's): prefill S=65536, H=64, D=128 bf16, AR(1) queries
+(rho=0.95) and Pareto(alpha=2)-norm keys, top_k=2048, g=8, K=4096. A step is
+one PIVOT-Refine prefill call (proxy, sample scan, thresholds, main scan,
+candidate select, fallback, refine), inputs resident in HBM. The JSON line
+also carries PIVOT-Reuse on the same inputs, the decode workload (64
+sequences, contexts U[32768, 131072], H=8, g in {2, 4}), per-kernel times
+from HIP events recorded on the library's stream, the roofline of the
+dominant kernel, recall@top_k against the dense indexer on sampled rows and
+the CPU oracle timed on this host.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+BF16_PEAK = 2.5e15         # flop/s, MI355X dense bf16 MFMA
+
+
+def log(msg: str):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def prefix_sums(S: int, g: int, K: int):
+    """Sum over groups of the prefix length n_j = max(j*g, 1) and of
+    min(K, n_j)."""
+    import numpy as np
+    j = np.arange((S + g - 1) // g, dtype=np.int64)
+    n = np.maximum(j * g, 1)
+    return int(n.sum()), int(np.minimum(n, K).sum())
+
+
+def time_calls(fn, steps: int, warmup: int, pv):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    pv.profile_read()
+    pv.profile_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = pv.profile_read()
+    pv.profile_enable(False)
+    ms = e0.elapsed_time(e1) / steps
+    per_stage = {k: v[0] / steps for k, v in stages.items()}
+    launches = {k: v[1] // steps for k, v in stages.items()}
+    return ms, wall / steps * 1e3, per_stage, launches
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-reuse", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
+    ap.add_argument("--recall-rows", type=int, default=256)
+    ap.add_argument("--long", action="store_true", help="S=131072, H=32, g=16 instead")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the indexer runs on a single MI355X; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic as syn
+    import top_token_selection_amd as pv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S, H, g = (131072, 32, 16) if args.long else (65536, 64, 8)
+    D, top_k, ratio = 128, 2048, 2.0
+    K = pv.candidate_count(top_k, ratio)
+    seed = 1004 if args.long else 1003
+    log(f"drawing prefill S={S} H={H} D={D} on the device")
+    cfg = syn.long_prefill_device(dev, S=S, H=H, g=g, seed=seed)
+    q, k = cfg["q"], cfg["k"]
+    torch.cuda.synchronize()
+
+    ws_bytes = max(pv.prefill_workspace_bytes(S, H, D, top_k, g, ratio, m, torch.bfloat16)
+                   for m in ("refine", "reuse"))
+    log(f"workspace {ws_bytes / 2**30:.1f} GiB, output {S * H * top_k * 4 / 2**30:.1f} GiB")
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((S, H, top_k), dtype=torch.int32, device=dev)
+
+    def refine():
+        pv.index_prefill(q, k, top_k, g, ratio, "refine", workspace=ws, out=out)
+
+    rng = np.random.default_rng(7)
+    ri = rng.integers(g, S, max(args.recall_rows, 1))
+    rh = rng.integers(0, H, max(args.recall_rows, 1)).astype(np.int32)
+    ri_d = torch.from_numpy(ri).to(dev)
+    rh_d = torch.from_numpy(rh.astype(np.int64)).to(dev)
+
+    log("timing Refine")
+    ms, wall_ms, stages, launches = time_calls(refine, args.steps, args.warmup, pv)
+    qps = S * H / (ms / 1e3)
+    log(f"Refine {ms:.2f} ms/step ({qps:.3e} queries/s); stages {stages}")
+    ref_rows = out[ri_d, rh_d].cpu().numpy()
+
+    reuse_ms = reuse_stages = None
+    if not args.no_reuse:
+        def reuse():
+            pv.index_prefill(q, k, top_k, g, ratio, "reuse", workspace=ws, out=out)
+        log("timing Reuse")
+        reuse_ms, _, reuse_stages, _ = time_calls(reuse, args.steps, args.warmup, pv)
+        log(f"Reuse {reuse_ms:.2f} ms/step")
+
+    # ------------------------------------------------------------ roofline
+    sum_n, sum_nk = prefix_sums(S, g, K)
+    scan_flops = 2.0 * D * H * sum_n
+    gather_bytes = float(H * D * 2 * sum_nk)
+    out_bytes = float(S * H * top_k * 4)
+    work = {
+        # algorithmic work per launch of each kernel stage
+        "scan": ("mfma", scan_flops, "TFLOP/s", BF16_PEAK),
+        "refine": ("hbm", gather_bytes + out_bytes + S * H * D * 2 + H * sum_nk * 4, "GB/s", HBM_PEAK),
+    }
+    dom = max(stages, key=lambda s: stages[s])
+    roof = None
+    if dom in work:
+        bound, amount, unit, peak = work[dom]
+        t = stages[dom] / 1e3 / max(1, launches.get(dom, 1))
+        achieved = amount / max(1, launches.get(dom, 1)) / t
+        scale = 1e12 if unit == "TFLOP/s" else 1e9
+        roof = {"bound": bound, "kernel": dom, "achieved": achieved / scale, "peak": peak / scale,
+                "unit": unit, "frac": achieved / peak, "traffic": None}
+    scan_t = stages.get("scan", 0.0) / 1e3
+    scan_roof = {"bound": "mfma", "achieved": scan_flops / scan_t / 1e12 if scan_t else None,
+                 "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                 "frac": scan_flops / scan_t / BF16_PEAK if scan_t else None}
+
+    # ---------------------------------------------------------------- recall
+    recall = None
+    qh = kh = None
+    if args.recall_rows > 0 or not args.no_cpu_baseline:
+        log("copying inputs to the host for the oracle")
+        qh = syn.bf16_tensor_to_bits(q)
+        kh = syn.bf16_tensor_to_bits(k)
+    if args.recall_rows > 0:
+        import oracle
+        log(f"dense oracle on {args.recall_rows} sampled rows")
+        t0 = time.perf_counter()
+        dense_rows, _ = oracle.dense_rows(qh, kh, ri, rh, top_k)
+        dense_s = time.perf_counter() - t0
+        pv.index_prefill(q, k, top_k, g, ratio, "reuse", workspace=ws, out=out)
+        reu_rows = out[ri_d, rh_d].cpu().numpy()
+
+        def rec(rows):
+            vals = []
+            for a, b in zip(rows, dense_rows):
+                bs = set(b[b >= 0].tolist())
+                vals.append(len(set(a[a >= 0].tolist()) & bs) / len(bs))
+            return float(np.mean(vals))
+        recall = {"refine": rec(ref_rows), "reuse": rec(reu_rows), "rows": int(args.recall_rows),
+                  "sample": "positions uniform in [g, S), heads uniform, seed 7", "oracle_s": dense_s}
+        log(f"recall@{top_k}: {recall}")
+
+    # ---------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rng = np.random.default_rng(11)
+        G = (S + g - 1) // g
+        done_rows = 0
+        t0 = time.perf_counter()
+        ngroups = 0
+        log(f"timing the oracle for about {args.cpu_seconds:.0f} s")
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            hh = rng.integers(0, H, 1).astype(np.int32)
+            jj = rng.integers(0, G, 1)
+            oracle.prefill_groups(qh, kh, hh, jj, top_k, g, ratio, "refine")
+            done_rows += int(min(g, S - jj[0] * g))
+            ngroups += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": done_rows / el, "unit": "queries/s", "cores": 1, "kind": "oracle",
+               "sample": f"{ngroups} PIVOT-Refine groups (all {g} members each) drawn uniformly over "
+                         f"(head, group) of this workload, seed 11, single-threaded C oracle, {el:.1f} s"}
+        log(f"oracle {cpu['value']:.2f} queries/s")
+    del ws, out, q, k, cfg
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- decode
+    decode = None
+    if not args.no_decode:
+        decode = {}
+        for gd in (2, 4):
+            log(f"drawing decode g={gd}")
+            dc = syn.decode_step_device(dev, g=gd)
+            ctx = dc["ctx_lens"]
+            nbytes = float(ctx.sum()) * 8 * D * 2
+            dws = torch.empty(max(pv.decode_workspace_bytes(ctx, gd, 8, D, top_k, ratio, m, torch.bfloat16)
+                                  for m in ("refine", "reuse")), dtype=torch.uint8, device=dev)
+            dout = torch.empty((len(ctx) * gd, 8, top_k), dtype=torch.int32, device=dev)
+            for mode in ("refine", "reuse"):
+                def step():
+                    pv.index_decode(dc["q"], dc["k_cache"], ctx, gd, top_k, ratio, mode, workspace=dws, out=dout)
+                dms, _, dst, _ = time_calls(step, args.steps * 4, args.warmup, pv)
+                t_scan = dst.get("decode_scan", 0.0) / 1e3
+                decode[f"g{gd}_{mode}"] = {
+                    "us_per_step": dms * 1e3, "stage_ms": dst,
+                    "scan_GBps": nbytes / t_scan / 1e9 if t_scan else None,
+                    "scan_hbm_frac": nbytes / t_scan / HBM_PEAK if t_scan else None,
+                    "key_bytes": nbytes}
+                log(f"decode g={gd} {mode}: {dms * 1e3:.0f} us/step, scan {nbytes / t_scan / 1e9:.0f} GB/s")
+            del dc, dws, dout
+            torch.cuda.empty_cache()
+
+    line = {
+        "metric": "indexed queries/s (Refine, S=64K prefill) + decode us/step; % MFMA/HBM roofline",
+        "value": qps,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (device-drawn AR(1) queries, Pareto-norm keys; seeds in synthetic/)",
+        "config": {"workload": f"PIVOT-Refine prefill S={S} H={H} D={D} bf16 top_k={top_k} g={g} K={K}",
+                   "mode": "refine", "S": S, "H": H, "D": D, "top_k": top_k, "g": g, "K": K},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": {
+            "wall_ms_per_step": wall_ms,
+            "stage_ms": stages,
+            "stage_launches": launches,
+            "scan_roofline": scan_roof,
+            "scan_flops": scan_flops,
+            "refine_gather_bytes": gather_bytes,
+            "output_bytes": out_bytes,
+            "reuse_ms_per_step": reuse_ms,
+            "reuse_queries_per_s": S * H / (reuse_ms / 1e3) if reuse_ms else None,
+            "reuse_stage_ms": reuse_stages,
+            "decode": decode,
+            "recall": recall,
+            "host": {"cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count(),
+                     "gpu": torch.cuda.get_device_name(dev)},
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

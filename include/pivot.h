@@ -42,7 +42,8 @@
  *   dense min(top_k, max(i, 1)), with n the group's prefix length.
  *
  * Ownership and execution: the caller owns every buffer; the library never
- * allocates device memory and keeps no state between calls. Work is
+ * allocates device memory and keeps no state between calls (apart from the
+ * optional stage-timing records below). Work is
  * enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
  * call returns once it is enqueued. Calls are reentrant for distinct
  * workspaces. The workspace is scratch device memory of at least the size
@@ -140,6 +141,20 @@ int dense_index(const void *q, const void *k, int32_t dtype, int64_t S,
                 int32_t H, int32_t D, int32_t top_k, int32_t *out_idx,
                 float *out_score, void *workspace, size_t workspace_bytes,
                 void *stream);
+
+/* Stage timing, for benchmarking and tracing. While enabled, every call
+ * records a pair of HIP events on its stream around each kernel stage.
+ * pivot_profile_read waits for the recorded events, adds each stage's
+ * elapsed milliseconds and launch count into ms_out[stage] / count_out[stage]
+ * (arrays of n_stages entries, first zeroed by the call) and forgets the
+ * records. Stages: 0 proxy mean, 1 sample scan, 2 thresholds, 3 main scan,
+ * 4 select, 5 exact fallback, 6 refine, 7 decode scan, 8 decode select.
+ * At most 8192 records are kept between reads (later ones are dropped).
+ * Not thread-safe: one benchmarking thread only. Returns PIVOT_OK, or
+ * PIVOT_EINVAL / PIVOT_EHIP. */
+#define PIVOT_N_STAGES 9
+int pivot_profile_enable(int on);
+int pivot_profile_read(double *ms_out, int64_t *count_out, int n_stages);
 
 #ifdef __cplusplus
 }

@@ -57,6 +57,8 @@ def _load():
     lib.oracle_prefill.restype = ci
     lib.oracle_prefill_rows.argtypes = [vp, vp, ci, i64, i32, i32, i32, i32, f64, ci, i64, vp, vp, vp, vp]
     lib.oracle_prefill_rows.restype = ci
+    lib.oracle_prefill_groups.argtypes = [vp, vp, ci, i64, i32, i32, i32, i32, f64, ci, i64, vp, vp, vp, vp]
+    lib.oracle_prefill_groups.restype = ci
     lib.oracle_prefill_candidates.argtypes = [vp, vp, ci, i64, i32, i32, i32, i32, f64, i32, i64, vp, vp]
     lib.oracle_prefill_candidates.restype = i64
     lib.oracle_dense.argtypes = [vp, vp, ci, i64, i32, i32, i32, i32, i32, vp, vp]
@@ -135,6 +137,22 @@ def prefill_rows(q, k, rows_i, rows_h, top_k=64, g=8, candidate_ratio=2.0, mode=
     _check(_load().oracle_prefill_rows(_ptr(q), _ptr(k), dt, S, H, D, top_k, g, candidate_ratio,
                                        MODES[mode], n, _ptr(ri), _ptr(rh), _ptr(idx), _ptr(sc)),
            "oracle_prefill_rows")
+    return idx, sc
+
+
+def prefill_groups(q, k, heads, groups, top_k=64, g=8, candidate_ratio=2.0, mode="refine"):
+    """Whole groups (head heads[t], group groups[t]): (n, g, top_k) rows of
+    all members, each group computed once."""
+    q, k, dt = _prep(q, k)
+    S, H, D = q.shape
+    hh = np.ascontiguousarray(heads, np.int32)
+    gg = np.ascontiguousarray(groups, np.int64)
+    n = hh.shape[0]
+    idx = np.empty((n, g, top_k), np.int32)
+    sc = np.empty((n, g, top_k), np.float32)
+    _check(_load().oracle_prefill_groups(_ptr(q), _ptr(k), dt, S, H, D, top_k, g, candidate_ratio,
+                                         MODES[mode], n, _ptr(hh), _ptr(gg), _ptr(idx), _ptr(sc)),
+           "oracle_prefill_groups")
     return idx, sc
 
 

@@ -378,6 +378,55 @@ int oracle_prefill_rows(const void *q, const void *k, int dt, int64_t S,
     return rc;
 }
 
+/* Whole groups of a prefill: group (heads[t], groups[t]) for t < n_groups,
+ * every member row written to out_idx / out_score shaped (n_groups, g,
+ * top_k) (rows past a ragged last group stay -1 / -inf). */
+int oracle_prefill_groups(const void *q, const void *k, int dt, int64_t S,
+                          int32_t H, int32_t D, int32_t top_k, int32_t g,
+                          double candidate_ratio, int mode, int64_t n_groups,
+                          const int32_t *heads, const int64_t *groups,
+                          int32_t *out_idx, float *out_score)
+{
+    int rc = check_common(q, k, dt, S, H, D, top_k);
+    if (rc)
+        return rc;
+    int64_t K = oracle_candidate_count(top_k, candidate_ratio);
+    if (K < 0 || g < 1 || !out_idx || !heads || !groups || n_groups < 0 ||
+        (mode != OR_REFINE && mode != OR_REUSE))
+        return OR_EINVAL;
+    size_t one = (size_t)g * H * top_k;
+    int32_t *tmp_idx = (int32_t *)malloc(sizeof(int32_t) * one);
+    float *tmp_sc = (float *)malloc(sizeof(float) * one);
+    if (!tmp_idx || !tmp_sc) {
+        free(tmp_idx);
+        free(tmp_sc);
+        return OR_ENOMEM;
+    }
+    for (int64_t t = 0; t < n_groups && rc == OR_OK; ++t) {
+        int32_t h = heads[t];
+        int64_t i0 = groups[t] * (int64_t)g;
+        if (h < 0 || h >= H || groups[t] < 0 || i0 >= S) {
+            rc = OR_EINVAL;
+            break;
+        }
+        int64_t m = min64(g, S - i0);
+        rc = one_group(q, k, dt, H, D, top_k, K, mode, h, i0, m, 0, max64(i0, 1),
+                       tmp_idx, tmp_sc, 0, NULL, NULL);
+        for (int64_t u = 0; u < g && rc == OR_OK; ++u) {
+            size_t dst = ((size_t)t * g + u) * (size_t)top_k;
+            size_t src = ((size_t)u * H + h) * (size_t)top_k;
+            for (int c = 0; c < top_k; ++c) {
+                out_idx[dst + c] = u < m ? tmp_idx[src + c] : -1;
+                if (out_score)
+                    out_score[dst + c] = u < m ? tmp_sc[src + c] : -INFINITY;
+            }
+        }
+    }
+    free(tmp_idx);
+    free(tmp_sc);
+    return rc;
+}
+
 /* Candidate set C of group j, head h of a prefill, in total order: writes
  * min(K, n_j) indices (and their proxy scores) and returns that count, or a
  * negative error. */

@@ -122,3 +122,68 @@ def decode_step(g: int = 2, B: int = 64, H: int = 8, lo: int = 32768, hi: int = 
     qs = [ar1_queries(g, H, D, seed + 2000 + b, dtype="f32") for b in range(B)]
     q = to_bf16_bits(np.concatenate(qs, axis=0))
     return dict(q=q, k_cache=kc, ctx_lens=ctx, g=g, top_k=2048, candidate_ratio=2.0)
+
+
+# ------------------------------------------------------------ device draws
+# The long workloads are drawn on the device with torch's seeded generator
+# (same distributions and recipe as above; different random streams). The
+# AR(1) recursion runs blockwise in float64: inside a block of B steps,
+#   q_{t0+u} = rho^u * (rho * q_{t0-1} + sum_{v<=u} rho^{-v} e_{t0+v}).
+
+def ar1_queries_device(S: int, H: int, D: int, seed: int, device, rho: float = 0.95, block: int = 128):
+    import torch
+    gen = torch.Generator(device=device).manual_seed(seed)
+    e = torch.randn((S, H, D), generator=gen, device=device, dtype=torch.float32)
+    out = torch.empty((S, H, D), device=device, dtype=torch.bfloat16)
+    carry = e[0].double() / float(np.sqrt(1.0 - rho * rho))
+    out[0] = carry.to(torch.bfloat16)
+    u = torch.arange(block, device=device, dtype=torch.float64)
+    pw = rho ** u
+    ipw = rho ** (-u)
+    t = 1
+    while t < S:
+        n = min(block, S - t)
+        c = torch.cumsum(e[t:t + n].double() * ipw[:n, None, None], dim=0)
+        blk = pw[:n, None, None] * (rho * carry + c)
+        out[t:t + n] = blk.to(torch.bfloat16)
+        carry = blk[-1]
+        t += n
+    return out
+
+
+def pareto_keys_device(S: int, H: int, D: int, seed: int, device, alpha: float = 2.0, chunk: int = 1 << 16):
+    import torch
+    gen = torch.Generator(device=device).manual_seed(seed)
+    out = torch.empty((S, H, D), device=device, dtype=torch.bfloat16)
+    for s0 in range(0, S, chunk):
+        n = min(chunk, S - s0)
+        z = torch.randn((n, H, D), generator=gen, device=device, dtype=torch.float32)
+        u = torch.rand((n, H, 1), generator=gen, device=device, dtype=torch.float64)
+        r = ((1.0 - u) ** (-1.0 / alpha)).float()
+        out[s0:s0 + n] = (z * (r / torch.linalg.vector_norm(z, dim=2, keepdim=True))).to(torch.bfloat16)
+    return out
+
+
+def long_prefill_device(device, S: int = 65536, H: int = 64, g: int = 8, seed: int = 1003):
+    """Device tensors of the AR(1) / Pareto-norm prefill workload."""
+    D = 128
+    return dict(q=ar1_queries_device(S, H, D, seed, device), k=pareto_keys_device(S, H, D, seed + 1000, device),
+                top_k=2048, g=g, candidate_ratio=2.0)
+
+
+def decode_step_device(device, g: int = 2, B: int = 64, H: int = 8, lo: int = 32768, hi: int = 131072,
+                       seed: int = 1005):
+    """Device tensors of the decode workload: B sequences, contexts uniform
+    in [lo, hi], Pareto-norm bf16 cache, g AR(1) queries per sequence."""
+    import torch
+    D = 128
+    ctx = decode_lengths(B, lo, hi, seed)
+    kc = pareto_keys_device(int(ctx.sum()), H, D, seed + 1000, device)
+    q = torch.cat([ar1_queries_device(g, H, D, seed + 2000 + b, device) for b in range(B)], dim=0)
+    return dict(q=q.contiguous(), k_cache=kc, ctx_lens=ctx, g=g, top_k=2048, candidate_ratio=2.0)
+
+
+def bf16_tensor_to_bits(t) -> np.ndarray:
+    """Host uint16 bf16 bits of a device bfloat16 tensor (for the oracle)."""
+    import torch
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)

@@ -409,3 +409,20 @@ def test_rows_api_matches_full():
     fd, _ = oracle.dense(q, k, top_k)
     rd, _ = oracle.dense_rows(q, k, ri, rh, top_k)
     np.testing.assert_array_equal(rd, fd[ri, rh])
+
+
+def test_groups_api_matches_full():
+    S, H, D, top_k, g = 90, 2, 16, 6, 8   # ragged last group
+    q = syn.gaussian((S, H, D), 141, "bf16")
+    k = syn.gaussian((S, H, D), 142, "bf16")
+    heads = np.array([0, 1, 1, 0], np.int32)
+    groups = np.array([0, 5, 11, 7], np.int64)
+    for mode in ("refine", "reuse"):
+        full, fs = oracle.prefill(q, k, top_k, g, 2.0, mode)
+        gi, gs = oracle.prefill_groups(q, k, heads, groups, top_k, g, 2.0, mode)
+        for t in range(len(heads)):
+            i0 = groups[t] * g
+            m = min(g, S - i0)
+            np.testing.assert_array_equal(gi[t, :m], full[i0:i0 + m, heads[t]])
+            np.testing.assert_array_equal(gs[t, :m], fs[i0:i0 + m, heads[t]])
+            assert (gi[t, m:] == -1).all()

@@ -32,8 +32,12 @@ _MODES = {"refine": PIVOT_REFINE, "reuse": PIVOT_REUSE}
 EXPORTED = (
     "pivot_status_string", "pivot_candidate_count", "pivot_prefill_workspace_bytes",
     "pivot_index_prefill", "pivot_decode_workspace_bytes", "pivot_index_decode",
-    "dense_index_workspace_bytes", "dense_index",
+    "dense_index_workspace_bytes", "dense_index", "pivot_profile_enable", "pivot_profile_read",
 )
+
+#: kernel stages reported by the stage timer (include/pivot.h)
+STAGES = ("proxy", "sample_scan", "thresholds", "scan", "select", "fallback", "refine",
+          "decode_scan", "decode_select")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -59,6 +63,10 @@ lib.dense_index_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, _i32]
 lib.dense_index_workspace_bytes.restype = _sz
 lib.dense_index.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
 lib.dense_index.restype = ctypes.c_int
+lib.pivot_profile_enable.argtypes = [ctypes.c_int]
+lib.pivot_profile_enable.restype = ctypes.c_int
+lib.pivot_profile_read.argtypes = [_vp, _vp, ctypes.c_int]
+lib.pivot_profile_read.restype = ctypes.c_int
 
 
 class PivotError(RuntimeError):
@@ -93,6 +101,21 @@ def _ptr(t):
 
 def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def profile_enable(on: bool = True) -> None:
+    """Start (or stop) recording HIP events around every kernel stage."""
+    _check(lib.pivot_profile_enable(1 if on else 0), "pivot_profile_enable")
+
+
+def profile_read() -> dict:
+    """{stage: (milliseconds, launches)} since the last read (waits for the
+    recorded events)."""
+    n = len(STAGES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(lib.pivot_profile_read(ctypes.cast(ms, _vp), ctypes.cast(cnt, _vp), n), "pivot_profile_read")
+    return {name: (ms[i], cnt[i]) for i, name in enumerate(STAGES) if cnt[i]}
 
 
 def candidate_count(top_k: int, candidate_ratio: float) -> int:
@@ -136,9 +159,23 @@ def _per_pass_bytes(full: int, one_head: int, H: int, max_bytes):
     return fixed + per * heads
 
 
+def _outputs(shape, device, return_scores, out, out_scores):
+    if out is None:
+        out = torch.empty(shape, dtype=torch.int32, device=device)
+    elif out.shape != shape or out.dtype != torch.int32 or out.device != device or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous int32 {tuple(shape)} tensor on {device}")
+    sc = None
+    if return_scores:
+        sc = out_scores if out_scores is not None else torch.empty(shape, dtype=torch.float32, device=device)
+        if sc.shape != shape or sc.dtype != torch.float32 or sc.device != device or not sc.is_contiguous():
+            raise ValueError(f"out_scores must be a contiguous float32 {tuple(shape)} tensor on {device}")
+    return out, sc
+
+
 def index_prefill(q, k, top_k=64, g=8, candidate_ratio=2.0, mode="refine", return_scores=False,
-                  workspace=None, max_workspace_bytes=None):
-    """PIVOT prefill indexer: int32 (S, H, top_k) (and scores)."""
+                  workspace=None, max_workspace_bytes=None, out=None, out_scores=None):
+    """PIVOT prefill indexer: int32 (S, H, top_k) (and scores). `out`,
+    `out_scores` and `workspace` may be given to avoid allocations."""
     _dev(q, "q")
     _dev(k, "k")
     if q.shape != k.shape or q.dim() != 3 or q.dtype != k.dtype or q.device != k.device:
@@ -152,15 +189,15 @@ def index_prefill(q, k, top_k=64, g=8, candidate_ratio=2.0, mode="refine", retur
                                        None, None, None, 0, None), "pivot_index_prefill")
     one = int(lib.pivot_prefill_workspace_bytes(S, 1, D, top_k, g, candidate_ratio, _MODES[mode], code))
     ws = _workspace(_per_pass_bytes(full, one, H, max_workspace_bytes), q.device, workspace)
-    out = torch.empty((S, H, top_k), dtype=torch.int32, device=q.device)
-    sc = torch.empty((S, H, top_k), dtype=torch.float32, device=q.device) if return_scores else None
+    out, sc = _outputs((S, H, top_k), q.device, return_scores, out, out_scores)
     _check(lib.pivot_index_prefill(_ptr(q), _ptr(k), code, S, H, D, top_k, g, candidate_ratio, _MODES[mode],
                                    _ptr(out), _ptr(sc), _ptr(ws), ws.numel(), _stream(q.device)),
            "pivot_index_prefill")
     return (out, sc) if return_scores else out
 
 
-def dense_index(q, k, top_k=64, return_scores=False, workspace=None, max_workspace_bytes=None):
+def dense_index(q, k, top_k=64, return_scores=False, workspace=None, max_workspace_bytes=None, out=None,
+                out_scores=None):
     """Dense indexer (comparison): int32 (S, H, top_k) (and scores)."""
     _dev(q, "q")
     _dev(k, "k")
@@ -173,15 +210,14 @@ def dense_index(q, k, top_k=64, return_scores=False, workspace=None, max_workspa
         _check(lib.dense_index(None, None, code, S, H, D, top_k, None, None, None, 0, None), "dense_index")
     one = int(lib.dense_index_workspace_bytes(S, 1, D, top_k, code))
     ws = _workspace(_per_pass_bytes(full, one, H, max_workspace_bytes), q.device, workspace)
-    out = torch.empty((S, H, top_k), dtype=torch.int32, device=q.device)
-    sc = torch.empty((S, H, top_k), dtype=torch.float32, device=q.device) if return_scores else None
+    out, sc = _outputs((S, H, top_k), q.device, return_scores, out, out_scores)
     _check(lib.dense_index(_ptr(q), _ptr(k), code, S, H, D, top_k, _ptr(out), _ptr(sc), _ptr(ws), ws.numel(),
                            _stream(q.device)), "dense_index")
     return (out, sc) if return_scores else out
 
 
 def index_decode(q, k_cache, ctx_lens, g, top_k=2048, candidate_ratio=2.0, mode="refine", return_scores=False,
-                 workspace=None):
+                 workspace=None, out=None, out_scores=None):
     """PIVOT decode indexer for one MTP step of B sequences:
     q (B*g, H, D), k_cache (sum ctx, H, D), ctx_lens B host ints ->
     int32 (B*g, H, top_k) (and scores)."""
@@ -201,8 +237,7 @@ def index_decode(q, k_cache, ctx_lens, g, top_k=2048, candidate_ratio=2.0, mode=
         _check(lib.pivot_index_decode(None, None, code, cp, B, g, H, D, top_k, candidate_ratio, _MODES[mode],
                                       None, None, None, 0, None), "pivot_index_decode")
     ws = _workspace(need, q.device, workspace)
-    out = torch.empty((rows, H, top_k), dtype=torch.int32, device=q.device)
-    sc = torch.empty((rows, H, top_k), dtype=torch.float32, device=q.device) if return_scores else None
+    out, sc = _outputs((rows, H, top_k), q.device, return_scores, out, out_scores)
     _check(lib.pivot_index_decode(_ptr(q), _ptr(k_cache), code, cp, B, g, H, D, top_k, candidate_ratio,
                                   _MODES[mode], _ptr(out), _ptr(sc), _ptr(ws), ws.numel(), _stream(q.device)),
            "pivot_index_decode")

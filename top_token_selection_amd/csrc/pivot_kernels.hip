@@ -808,6 +808,44 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
 
 // ==================================================================== host
 
+enum Stage { ST_PROXY = 0, ST_SAMPLE, ST_TAU, ST_SCAN, ST_SELECT, ST_FALLBACK, ST_REFINE,
+             ST_DSCAN, ST_DSELECT, ST_COUNT };
+static_assert(ST_COUNT == PIVOT_N_STAGES, "stage list matches the header");
+
+constexpr int PROF_MAX = 8192;
+struct ProfRec {
+    int stage;
+    hipEvent_t a, b;
+};
+bool g_prof_on = false;
+int g_prof_used = 0;     // records filled since the last read
+int g_prof_created = 0;  // records whose events exist
+ProfRec g_prof[PROF_MAX];
+
+// Records events around one kernel stage on `st` while profiling is on.
+struct StageTimer {
+    int slot = -1;
+    hipStream_t st;
+    StageTimer(int stage, hipStream_t s) : st(s) {
+        if (!g_prof_on || g_prof_used >= PROF_MAX) return;
+        ProfRec &r = g_prof[g_prof_used];
+        if (g_prof_used >= g_prof_created) {
+            if (hipEventCreate(&r.a) != hipSuccess) return;
+            if (hipEventCreate(&r.b) != hipSuccess) {
+                (void)hipEventDestroy(r.a);
+                return;
+            }
+            ++g_prof_created;
+        }
+        r.stage = stage;
+        if (hipEventRecord(r.a, st) != hipSuccess) return;
+        slot = g_prof_used++;
+    }
+    ~StageTimer() {
+        if (slot >= 0) (void)hipEventRecord(g_prof[slot].b, st);
+    }
+};
+
 struct Plan {
     int64_t S;
     int H, D, top_k, g, mode, dtype;
@@ -986,6 +1024,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
         } else {
             const int64_t total = rows * D;
             const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+            StageTimer tm(ST_PROXY, st);
             hipLaunchKernelGGL((k_proxy<T>), dim3(blocks), dim3(256), 0, st, q, pl.S, pl.H, pl.D, pl.g,
                                h0, Hc, pl.G, P);
             HIP_TRY(hipGetLastError());
@@ -1014,12 +1053,14 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             ss.cap_half = pl.samp_half;
             ss.cnt = scnt;
             ss.min_n = pl.keep_all_n;
+            StageTimer tm(ST_SAMPLE, st);
             int rc = dispatch_scan<T>(pl.D, ss, st);
             if (rc) return rc;
         }
         {
             TauParams tp{samp, scnt, pl.samp_half, tau, pl.G, pl.g, pl.keep_all_n, pl.rsel};
             const size_t lds = ((size_t)(1 << SEL_LOG2NB) + 8 + 16) * 4;
+            StageTimer tm(ST_TAU, st);
             hipLaunchKernelGGL(k_tau, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, tp);
             HIP_TRY(hipGetLastError());
         }
@@ -1033,6 +1074,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             sm.cap_half = pl.cap_half;
             sm.cnt = cnt;
             sm.min_n = 0;
+            StageTimer tm(ST_SCAN, st);
             int rc = dispatch_scan<T>(pl.D, sm, st);
             if (rc) return rc;
         }
@@ -1050,6 +1092,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
         {
             SelParams se{surv, cnt, pl.cap_half, pl.G, pl.g, pl.Ksel, sorted_out, ro, fbl, fb_count};
             const size_t lds = sel_lds_bytes(0);
+            StageTimer tm(ST_SELECT, st);
             hipLaunchKernelGGL(k_select, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, se);
             HIP_TRY(hipGetLastError());
         }
@@ -1074,6 +1117,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             fp.o = ro;
             fp.D = pl.D;
             const size_t lds = sel_lds_bytes(pl.D);
+            StageTimer tm(ST_FALLBACK, st);
             hipLaunchKernelGGL((k_fallback<T>), dim3(FB_BLOCKS), dim3(SEL_THREADS), lds, st, fp);
             HIP_TRY(hipGetLastError());
         }
@@ -1099,6 +1143,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             rp.out_score = out_score;
             const size_t lds = ((size_t)pl.K * 4 + 15) / 16 * 16 + (size_t)rp.nqw * rp.reg_bytes;
             const int nblocks = (int)(rows * rp.nqb);
+            StageTimer tm(ST_REFINE, st);
             int rc = dispatch_refine<T>(pl.D, rp, nblocks, lds, st);
             if (rc) return rc;
         }
@@ -1191,6 +1236,7 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
     {
         const int64_t total = (int64_t)dp.H * dp.B * dp.D;
         const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+        StageTimer tm(ST_PROXY, st);
         hipLaunchKernelGGL((k_proxy<T>), dim3(blocks), dim3(256), 0, st, q, (int64_t)dp.B * dp.g, dp.H,
                            dp.D, dp.g, 0, dp.H, (int64_t)dp.B, P);
         HIP_TRY(hipGetLastError());
@@ -1198,6 +1244,7 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
     {
         DecScanParams ds{P, kc, offs, dp.B, dp.H, (dp.max_ctx + DEC_TOKENS - 1) / DEC_TOKENS, dense};
         const int nblocks = (int)(dp.B * ds.max_chunks);
+        StageTimer tm(ST_DSCAN, st);
         int rc = dp.D == 64 ? launch_dec_scan<T, 64>(ds, nblocks, dp.H, st)
                             : launch_dec_scan<T, 128>(ds, nblocks, dp.H, st);
         if (rc) return rc;
@@ -1225,6 +1272,7 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
         fp.D = dp.D;
         const size_t lds = sel_lds_bytes(dp.D);
         const int nrows = dp.B * dp.H;
+        StageTimer tm(ST_DSELECT, st);
         hipLaunchKernelGGL((k_fallback<T>), dim3(nrows), dim3(SEL_THREADS), lds, st, fp);
         HIP_TRY(hipGetLastError());
     }
@@ -1250,6 +1298,7 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
         rp.out_score = out_score;
         const size_t lds = ((size_t)dp.K * 4 + 15) / 16 * 16 + (size_t)rp.nqw * rp.reg_bytes;
         const int nblocks = dp.B * dp.H * rp.nqb;
+        StageTimer tm(ST_REFINE, st);
         int rc = dispatch_refine<T>(dp.D, rp, nblocks, lds, st);
         if (rc) return rc;
     }
@@ -1348,6 +1397,35 @@ int pivot_index_decode(const void *q, const void *k_cache, int32_t dtype, const 
                                   out_score, (unsigned char *)workspace, st);
     return run_decode<float>(dp, ctx_lens_host, (const float *)q, (const float *)k_cache, out_idx, out_score,
                              (unsigned char *)workspace, st);
+}
+
+int pivot_profile_enable(int on) {
+    g_prof_on = on != 0;
+    g_prof_used = 0;
+    return PIVOT_OK;
+}
+
+int pivot_profile_read(double *ms_out, int64_t *count_out, int n_stages) {
+    if (!ms_out || !count_out || n_stages < 0) return PIVOT_EINVAL;
+    for (int i = 0; i < n_stages; ++i) {
+        ms_out[i] = 0.0;
+        count_out[i] = 0;
+    }
+    int rc = PIVOT_OK;
+    for (int i = 0; i < g_prof_used; ++i) {
+        const ProfRec &r = g_prof[i];
+        float ms = 0.f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+            rc = PIVOT_EHIP;
+            continue;
+        }
+        if (r.stage < n_stages) {
+            ms_out[r.stage] += ms;
+            count_out[r.stage] += 1;
+        }
+    }
+    g_prof_used = 0;
+    return rc;
 }
 
 }  // extern "C"
