@@ -79,6 +79,21 @@ def test_prefill_bit_exact_integer_inputs(pv, mode, S, H, D, top_k, g, ratio, dt
         np.testing.assert_allclose(gs, os_, rtol=4 * 2.0 ** -23, atol=0)
 
 
+@pytest.mark.parametrize("S,H,D,top_k,g,ratio,dtype", EXACT_CASES)
+def test_refine_index_only_bit_exact(pv, S, H, D, top_k, g, ratio, dtype):
+    """Indices without scores take the per-query bucket sort; they must equal
+    the oracle's rows exactly as well."""
+    print(f"\n[refine index-only] S={S} H={H} D={D} k={top_k} g={g} r={ratio} {dtype}", flush=True)
+    a = 8 if dtype == "f32" else 4
+    q = syn.integers((S, H, D), 7000 + S + g, a, dtype)
+    k = syn.integers((S, H, D), 8000 + S + g, a, dtype)
+    idx = pv.index_prefill(dev_tensor(q), dev_tensor(k), top_k=top_k, g=g, candidate_ratio=ratio,
+                           mode="refine")
+    torch.cuda.synchronize()
+    oi, _ = oracle.prefill(q, k, top_k, g, ratio, "refine")
+    np.testing.assert_array_equal(parity.to_host(idx), oi)
+
+
 @pytest.mark.parametrize("S,H,D,top_k,dtype", [(1024, 8, 64, 64, "f32"), (700, 3, 128, 32, "bf16")])
 def test_dense_bit_exact_integer_inputs(pv, S, H, D, top_k, dtype):
     print(f"\n[dense exact] S={S} H={H} D={D} k={top_k} {dtype}", flush=True)
@@ -121,6 +136,9 @@ def test_all_scores_equal_ties_by_index(pv, mode):
     oi, os_ = oracle.prefill(q, k, top_k, g, 2.0, mode)
     np.testing.assert_array_equal(gi, oi)
     np.testing.assert_array_equal(gs, os_)
+    only = pv.index_prefill(dev_tensor(q), dev_tensor(k), top_k=top_k, g=g, mode=mode)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(parity.to_host(only), oi)
 
 
 def test_tiny_and_degenerate_shapes(pv):
@@ -133,6 +151,9 @@ def test_tiny_and_degenerate_shapes(pv):
             oi, os_ = oracle.prefill(q, k, top_k, g, 2.0, mode)
             np.testing.assert_array_equal(gi, oi)
             np.testing.assert_array_equal(gs, os_)
+            only = pv.index_prefill(dev_tensor(q), dev_tensor(k), top_k=top_k, g=g, mode=mode)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(parity.to_host(only), oi)
 
 
 def test_refine_with_K_covering_prefix_equals_group_prefix_dense(pv):

@@ -107,7 +107,7 @@ struct Group {
     }
     __device__ __forceinline__ int wave() const { return tid >> 6; }
 
-    __device__ uint32_t reduce_min(uint32_t v) const {
+    __device__ __forceinline__ uint32_t reduce_min(uint32_t v) const {
         v = wave_min(v);
         if constexpr (NW == 1) return v;
         if (lane_id() == 0) red[wave()] = v;
@@ -117,7 +117,7 @@ struct Group {
         sync();
         return r;
     }
-    __device__ uint32_t reduce_max(uint32_t v) const {
+    __device__ __forceinline__ uint32_t reduce_max(uint32_t v) const {
         v = wave_max(v);
         if constexpr (NW == 1) return v;
         if (lane_id() == 0) red[wave()] = v;
@@ -127,7 +127,7 @@ struct Group {
         sync();
         return r;
     }
-    __device__ uint32_t reduce_sum(uint32_t v) const {
+    __device__ __forceinline__ uint32_t reduce_sum(uint32_t v) const {
         v = wave_sum(v);
         if constexpr (NW == 1) return v;
         if (lane_id() == 0) red[wave()] = v;
@@ -138,7 +138,7 @@ struct Group {
         return r;
     }
     // Exclusive prefix sum over the group in thread order.
-    __device__ uint32_t excl_scan(uint32_t v) const {
+    __device__ __forceinline__ uint32_t excl_scan(uint32_t v) const {
         uint32_t inc = wave_incl_scan(v);
         if constexpr (NW == 1) return inc - v;
         if (lane_id() == 63) red[wave()] = inc;
@@ -177,14 +177,14 @@ struct Selector {
     uint32_t *hist;
     uint32_t *vars;
 
-    __device__ void clear_hist() const {
+    __device__ __forceinline__ void clear_hist() const {
         for (int b = G.tid; b < NB; b += NT) hist[b] = 0;
     }
 
     // Bucket holding the need-th largest element: bins are scanned from the
     // top (largest keys) down. Returns the bucket, the count above it and
     // its own count.
-    __device__ void crossing(uint32_t need, uint32_t &b_out, uint32_t &above,
+    __device__ __forceinline__ void crossing(uint32_t need, uint32_t &b_out, uint32_t &above,
                              uint32_t &cnt) const {
         if (G.tid == 0) {
             vars[0] = 0;
@@ -220,7 +220,7 @@ struct Selector {
     // `whole` -> the selection is exactly {k >= T}; otherwise it is
     // {k > T} plus `rem` of the elements with k == T.
     template <class FE, class EXT>
-    __device__ void narrow(FE fe, EXT ext, uint32_t lo, uint32_t hi,
+    __device__ __forceinline__ void narrow(FE fe, EXT ext, uint32_t lo, uint32_t hi,
                            uint32_t need, uint32_t &T, uint32_t &rem,
                            bool &whole) const {
         // each pass shrinks the range by 2^LOG2NB; the bound only guards
@@ -273,7 +273,7 @@ struct Selector {
 
     // The rule selecting the m best of the n elements (1 <= m).
     template <class FE, class IDX>
-    __device__ Rule select(FE fe, IDX idx, uint32_t n, uint32_t m) const {
+    __device__ __forceinline__ Rule select(FE fe, IDX idx, uint32_t n, uint32_t m) const {
         if (m >= n) return Rule{0u, 0u};
         uint32_t mn = 0xFFFFFFFFu, mx = 0u;
         fe([&](uint32_t key, uint32_t) {
@@ -312,13 +312,81 @@ struct Selector {
         return Rule{T, T2};
     }
 
+    // Bucket sort of the msel selected elements (fs(f) calls f(key,
+    // payload) for each selected element the thread owns) by (key desc,
+    // index asc); returns in registers, for t < MAXPER and
+    // tid + t*NT < msel, one element's final position rpos[t], key rkey[t]
+    // and payload rpl[t]. The group is synchronised on return, so bufk /
+    // bufp (msel entries of LDS) may then be reused to stage the output.
+    template <int MAXPER, class FS, class IDX, class PL>
+    __device__ __forceinline__ void sort_ranks(FS fs, IDX idx, uint32_t msel, uint32_t *bufk,
+                                               PL *bufp, uint32_t (&rpos)[MAXPER],
+                                               uint32_t (&rkey)[MAXPER],
+                                               uint32_t (&rpl)[MAXPER]) const {
+        if (msel == 0) return;
+        uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+        fs([&](uint32_t key, uint32_t) {
+            mn = min(mn, key);
+            mx = max(mx, key);
+        });
+        mn = G.reduce_min(mn);
+        mx = G.reduce_max(mx);
+        const uint32_t range = mx - mn;
+        const int bw = bit_width(range);
+        const int shift = bw > LOG2NB ? bw - LOG2NB : 0;
+        clear_hist();
+        G.sync();
+        fs([&](uint32_t key, uint32_t) { atomicAdd(&hist[(mx - key) >> shift], 1u); });
+        G.sync();
+        {
+            uint32_t loc = 0;
+            for (int i = 0; i < BPT; ++i) loc += hist[G.tid * BPT + i];
+            uint32_t run = G.excl_scan(loc);
+            for (int i = 0; i < BPT; ++i) {
+                uint32_t h = hist[G.tid * BPT + i];
+                hist[G.tid * BPT + i] = run;
+                run += h;
+            }
+        }
+        G.sync();
+        fs([&](uint32_t key, uint32_t pl) {
+            uint32_t slot = atomicAdd(&hist[(mx - key) >> shift], 1u);
+            if (slot < msel) {
+                bufk[slot] = key;
+                bufp[slot] = (PL)pl;
+            }
+        });
+        G.sync();
+#pragma unroll
+        for (int t = 0; t < MAXPER; ++t) {
+            const uint32_t s = G.tid + t * NT;
+            if (s < msel) {
+                const uint32_t key = bufk[s];
+                const uint32_t pl = bufp[s];
+                const uint32_t myidx = idx(pl);
+                const uint32_t b = (mx - key) >> shift;
+                const uint32_t end = min(hist[b], msel);
+                const uint32_t beg = b ? hist[b - 1] : 0u;
+                uint32_t rank = 0;
+                for (uint32_t u = beg; u < end; ++u) {
+                    const uint32_t k2 = bufk[u];
+                    rank += (k2 > key) || (k2 == key && idx(bufp[u]) < myidx);
+                }
+                rpos[t] = beg + rank;
+                rkey[t] = key;
+                rpl[t] = pl;
+            }
+        }
+        G.sync();
+    }
+
     // Order the msel selected elements (fs(f) calls f(key, payload) for each
     // selected element the thread owns) by (key desc, index asc) through a
     // bucket sort: bufk/bufp (LDS, msel entries) receive the bucketed
     // elements; out(pos, key, payload) is then called once per element with
     // its final rank pos in [0, msel).
     template <class FS, class IDX, class PL, class OUT>
-    __device__ void sort_selected(FS fs, IDX idx, uint32_t msel, uint32_t *bufk,
+    __device__ __forceinline__ void sort_selected(FS fs, IDX idx, uint32_t msel, uint32_t *bufk,
                                   PL *bufp, OUT out) const {
         if (msel == 0) return;
         uint32_t mn = 0xFFFFFFFFu, mx = 0u;

@@ -51,6 +51,11 @@ constexpr int SEL_E = 48;          // survivors per thread held in registers
 constexpr int TAU_E = 16;          // samples per thread held in registers
 constexpr int REF_LOG2NB = 10;
 constexpr int REF_E = 64;          // candidates per lane (K <= 4096)
+constexpr int REF_FIX = 48;        // staging entries per lane at most (top_k + slack <= 3072)
+constexpr int REF_LOG2 = 11;       // fused select: 2048 buckets
+constexpr int REF_NB = 1 << REF_LOG2;
+constexpr int REF_LOG2C = 10;      // fused select: coarse bins
+constexpr int REF_HDR = ((1 << REF_LOG2C) + 64 + REF_NB / 2 + 64 + 16) * 4;  // bytes before the staged entries
 constexpr int MAX_K = 4096;
 constexpr int MAX_TOPK = 4096;
 constexpr int FB_BLOCKS = 256;
@@ -302,7 +307,8 @@ struct TauParams {
 
 // Per row: tau = the rsel-th best sample score (-inf when the row keeps
 // every key or has too few samples -- then k_select finds the overflow and
-// the row takes the exact fallback).
+// the row takes the exact fallback). Register slots past the samples hold
+// key 0, which no finite score maps to, so they never rank.
 __global__ void __launch_bounds__(SEL_THREADS) k_tau(TauParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t *hist = (uint32_t *)smem;
@@ -323,23 +329,23 @@ __global__ void __launch_bounds__(SEL_THREADS) k_tau(TauParams p) {
     }
     Group<4> G{(int)threadIdx.x, red};
     Selector<4, SEL_LOG2NB> sel{G, hist, vars};
-    uint32_t key[TAU_E], pl[TAU_E];
+    const int elim = (int)((ns + SEL_THREADS - 1) / SEL_THREADS);
+    uint32_t key[TAU_E];
     const uint2 *b0 = p.samp + (2 * r) * (int64_t)p.samp_half;
     const uint2 *b1 = p.samp + (2 * r + 1) * (int64_t)p.samp_half;
 #pragma unroll
     for (int e = 0; e < TAU_E; ++e) {
         const uint32_t gi = e * SEL_THREADS + threadIdx.x;
-        uint2 x = make_uint2(0u, 0u);
-        if (gi < ns) x = gi < (uint32_t)c0 ? b0[gi] : b1[gi - c0];
-        key[e] = x.x;
-        pl[e] = x.y;
+        key[e] = 0u;
+        if (e < elim && gi < ns) key[e] = gi < (uint32_t)c0 ? b0[gi].x : b1[gi - c0].x;
     }
     auto fe = [&](auto f) {
 #pragma unroll
         for (int e = 0; e < TAU_E; ++e)
-            if (e * SEL_THREADS + threadIdx.x < ns) f(key[e], pl[e]);
+            if (e < elim) f(key[e], e * SEL_THREADS + threadIdx.x);
     };
-    const Rule rule = sel.select(fe, [](uint32_t x) { return x; }, ns, (uint32_t)p.rsel);
+    const Rule rule = sel.select(fe, [](uint32_t x) { return x; }, (uint32_t)elim * SEL_THREADS,
+                                 (uint32_t)p.rsel);
     if (threadIdx.x == 0) p.tau[r] = key_score(rule.T);
 }
 
@@ -396,9 +402,26 @@ struct SelParams {
     uint32_t *fb_count;
 };
 
+// Copies a staged row (LDS, msel valid entries) into every member row of
+// group (hl, j), -1 / -inf past msel; coalesced stores.
+__device__ __forceinline__ void write_member_rows(const RowOut &o, int hl, int64_t j,
+                                                  const uint32_t *stage, uint32_t msel,
+                                                  bool scores) {
+    const int64_t i0 = j * o.g;
+    const int64_t m = min((int64_t)o.g, o.S - i0);
+    for (int64_t t = 0; t < m; ++t) {
+        const int64_t base = ((i0 + t) * o.H + o.h0 + hl) * (int64_t)o.top_k;
+        for (uint32_t c = threadIdx.x; c < (uint32_t)o.top_k; c += SEL_THREADS) {
+            if (scores) o.out_score[base + c] = c < msel ? key_score(stage[c]) : -INFINITY;
+            else o.out_idx[base + c] = c < msel ? (int32_t)stage[c] : -1;
+        }
+    }
+}
+
 // One block per row: the survivors of the main scan (a superset of the
 // row's best Ksel keys when the row is not queued) are held in registers and
-// the exact best min(Ksel, n) of them selected.
+// the exact best min(Ksel, n) of them selected. Slots past the survivors
+// hold key 0 (below every score) and never rank.
 __global__ void __launch_bounds__(SEL_THREADS) k_select(SelParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t *hist = (uint32_t *)smem;
@@ -422,6 +445,7 @@ __global__ void __launch_bounds__(SEL_THREADS) k_select(SelParams p) {
         return;
     }
     const uint32_t ns = (uint32_t)(c0 + c1);
+    const int elim = (int)((ns + SEL_THREADS - 1) / SEL_THREADS);
     Group<4> G{(int)threadIdx.x, red};
     Selector<4, SEL_LOG2NB> sel{G, hist, vars};
     uint32_t key[SEL_E], pl[SEL_E];
@@ -430,22 +454,23 @@ __global__ void __launch_bounds__(SEL_THREADS) k_select(SelParams p) {
 #pragma unroll
     for (int e = 0; e < SEL_E; ++e) {
         const uint32_t gi = e * SEL_THREADS + threadIdx.x;
-        uint2 x = make_uint2(0u, 0u);
-        if (gi < ns) x = gi < (uint32_t)c0 ? b0[gi] : b1[gi - c0];
+        uint2 x = make_uint2(0u, 0xFFFFFFFFu);
+        if (e < elim && gi < ns) x = gi < (uint32_t)c0 ? b0[gi] : b1[gi - c0];
         key[e] = x.x;
         pl[e] = x.y;
     }
     auto fe = [&](auto f) {
 #pragma unroll
         for (int e = 0; e < SEL_E; ++e)
-            if (e * SEL_THREADS + threadIdx.x < ns) f(key[e], pl[e]);
+            if (e < elim) f(key[e], pl[e]);
     };
     auto ident = [](uint32_t x) { return x; };
-    const Rule rule = sel.select(fe, ident, ns, msel);
+    const Rule rule = msel >= ns ? Rule{0u, 0u}
+                                 : sel.select(fe, ident, (uint32_t)elim * SEL_THREADS, msel);
     auto fs = [&](auto f) {
 #pragma unroll
         for (int e = 0; e < SEL_E; ++e)
-            if (e * SEL_THREADS + threadIdx.x < ns && rule.sel(key[e], pl[e])) f(key[e], pl[e]);
+            if (e < elim && key[e] != 0u && rule.sel(key[e], pl[e])) f(key[e], pl[e]);
     };
     if (!p.sorted_out) {
         if (threadIdx.x == 0) ctr[0] = 0;
@@ -456,11 +481,22 @@ __global__ void __launch_bounds__(SEL_THREADS) k_select(SelParams p) {
             if (slot < msel) dst[slot] = idx;
         });
     } else {
-        sel.sort_selected(fs, ident, msel, bufk, bufp,
-                          [&](uint32_t pos, uint32_t k, uint32_t idx) {
-                              put_member_rows(p.o, hl, j, pos, k, idx);
-                          });
-        pad_member_rows(p.o, hl, j, msel, threadIdx.x, SEL_THREADS);
+        constexpr int MP = MAX_TOPK / SEL_THREADS;
+        uint32_t rpos[MP], rkey[MP], rpl[MP];
+        sel.template sort_ranks<MP>(fs, ident, msel, bufk, bufp, rpos, rkey, rpl);
+#pragma unroll
+        for (int t = 0; t < MP; ++t)
+            if (threadIdx.x + t * SEL_THREADS < msel) bufk[rpos[t]] = rpl[t];
+        __syncthreads();
+        write_member_rows(p.o, hl, j, bufk, msel, false);
+        if (p.o.out_score) {
+            __syncthreads();
+#pragma unroll
+            for (int t = 0; t < MP; ++t)
+                if (threadIdx.x + t * SEL_THREADS < msel) bufk[rpos[t]] = rkey[t];
+            __syncthreads();
+            write_member_rows(p.o, hl, j, bufk, msel, true);
+        }
     }
 }
 
@@ -667,6 +703,7 @@ struct RefParams {
     int nqb;               // blocks per group
     int top_k;
     int reg_bytes;         // per-wave LDS region
+    int ref_cap;           // staged entries of the fused select (top_k + slack)
     int32_t *out_idx;
     float *out_score;
 };
@@ -725,53 +762,348 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     }
     __syncthreads();
 
+    // gather + MFMA, four 16-candidate blocks per step so that 4*NKS row
+    // loads per lane are in flight together
     const int nblocks = (nc + 15) / 16;
-    for (int blk = w; blk < nblocks; blk += p.nqw) {
-        const int pidx = blk * 16 + qcol;
-        const bool pv = pidx < nc;
-        // a candidate list entry is always a key of the prefix; the clamp
-        // keeps the gather inside the tensor whatever the list holds
-        const uint32_t c = pv ? min(cl[pidx], (uint32_t)(n - 1)) : 0u;
-        const T *kr = Kx + ((kbase + c) * p.H + h) * (int64_t)D;
-        frag_t a[NKS];
+    for (int b0 = 4 * w; b0 < nblocks; b0 += 4 * p.nqw) {
+        frag_t a[4][NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int dofs = F32 ? 16 * ks + 4 * lq : 32 * ks + 8 * lq;
-            a[ks] = pv ? *(const frag_t *)(kr + dofs) : frag_t{};
-        }
-        f32x4_t acc = f32x4_t{};
+        for (int u = 0; u < 4; ++u) {
+            const int pidx = (b0 + u) * 16 + qcol;
+            const bool pv = pidx < nc;
+            // a candidate list entry is always a key of the prefix; the clamp
+            // keeps the gather inside the tensor whatever the list holds
+            const uint32_t c = pv ? min(cl[pidx], (uint32_t)(n - 1)) : 0u;
+            const T *kr = Kx + ((kbase + c) * p.H + h) * (int64_t)D;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            if constexpr (F32) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ks][v], bq[ks][v], acc, 0, 0, 0);
-            } else {
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bq[ks], acc, 0, 0, 0);
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int dofs = F32 ? 16 * ks + 4 * lq : 32 * ks + 8 * lq;
+                a[u][ks] = pv ? *(const frag_t *)(kr + dofs) : frag_t{};
             }
         }
-        // lane holds query column qcol, candidates blk*16 + 4*lq + v
-        if (qcol < nq) {
-            uint32_t *dst = (uint32_t *)(regs + qcol * p.reg_bytes);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int pp = blk * 16 + 4 * lq + v;
-                if (pp < nc) dst[pp] = score_key(acc[v]);
+        for (int u = 0; u < 4; ++u) {
+            f32x4_t acc = f32x4_t{};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                if constexpr (F32) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][ks][v], bq[ks][v], acc, 0, 0, 0);
+                } else {
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][ks], bq[ks], acc, 0, 0, 0);
+                }
+            }
+            // lane holds query column qcol, candidates (b0+u)*16 + 4*lq + v
+            const int pp = (b0 + u) * 16 + 4 * lq;
+            if (qcol < nq && pp < nc) {
+                uint32_t *dst = (uint32_t *)(regs + qcol * p.reg_bytes) + pp;
+                if (pp + 3 < nc) {
+                    *(uint4 *)dst = make_uint4(score_key(acc[0]), score_key(acc[1]), score_key(acc[2]),
+                                               score_key(acc[3]));
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (pp + v < nc) dst[v] = score_key(acc[v]);
+                }
             }
         }
     }
     __syncthreads();
     if (w >= nq) return;
 
-    // this wavefront's query: exact sorted top_k of its nc candidate scores
+    // this wavefront's query: exact sorted top_k of its nc candidate scores.
+    // Lane l holds positions 4*(e*64 + l) + v; slots past nc hold key 0,
+    // below every score, so they never rank.
     unsigned char *my = regs + w * p.reg_bytes;
+    const int e4 = (nc + 255) / 256;
     uint32_t key[REF_E];
 #pragma unroll
-    for (int e = 0; e < REF_E; ++e) {
-        const int pp = e * 64 + l;
-        key[e] = pp < nc ? ((const uint32_t *)my)[pp] : 0u;
+    for (int e = 0; e < REF_E / 4; ++e) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (e < e4) v = *(const uint4 *)(my + (e * 64 + l) * 16);
+        const int b = (e * 64 + l) * 4;
+        key[4 * e + 0] = b + 0 < nc ? v.x : 0u;
+        key[4 * e + 1] = b + 1 < nc ? v.y : 0u;
+        key[4 * e + 2] = b + 2 < nc ? v.z : 0u;
+        key[4 * e + 3] = b + 3 < nc ? v.w : 0u;
     }
     wave_lds_sync();
+    const uint32_t msel = (uint32_t)min(p.top_k, nc);
+    const int64_t obase = ((qrow0 + q0 + w) * p.H + h) * (int64_t)p.top_k;
+
+    // ---- fused bucket select + sort ------------------------------------
+    // 1. A coarse histogram (1024 bins over [min, max] of this query's keys)
+    //    finds the bin holding the msel-th best key.
+    // 2. Equi-depth refinement: every coarse bin at or above it gets a
+    //    power-of-two number of fine buckets roughly proportional to its
+    //    count (2048 fine buckets in all, numbered from the best down), so a
+    //    fine bucket holds one or two keys on average whatever the shape of
+    //    the score distribution.
+    // 3. A fine histogram (16-bit counters, two per word); its scan finds
+    //    the fine bucket holding the msel-th key and gives every fine bucket
+    //    its output offset.
+    // 4. Fine buckets up to that one are scattered as packed words (key bits
+    //    inside the bucket, position); each element then counts the entries
+    //    of its bucket ranking above it (score desc, index asc).
+    // Out-of-range keys use per-lane trash bins / slots: no branches, no
+    // single hot address.
+    {
+        constexpr int NC = 1 << REF_LOG2C;            // coarse bins
+        uint32_t *h1 = (uint32_t *)my;                // coarse counts, then the table
+        uint32_t *h2 = h1 + NC + 64;                  // fine counters, two per word
+        uint32_t *vars = h2 + REF_NB / 2 + 64;
+        uint32_t *buf = (uint32_t *)(my + REF_HDR);   // ref_cap entries + 64 trash slots
+        const uint32_t cap = (uint32_t)p.ref_cap;
+        uint32_t mx = 0u, mnm1 = 0xFFFFFFFFu;
+#pragma unroll
+        for (int e = 0; e < REF_E / 4; ++e)
+            if (e < e4) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint32_t k = key[4 * e + v];
+                    mx = max(mx, k);
+                    mnm1 = min(mnm1, k - 1u);  // empty slots (0) wrap to the top
+                }
+            }
+        mx = wave_max(mx);
+        const uint32_t mn = wave_min(mnm1) + 1u;
+        const int bw1 = bit_width(mx - mn);
+        const int sh1 = bw1 > REF_LOG2C ? bw1 - REF_LOG2C : 0;
+        constexpr int CPL = NC / 64;  // coarse bins per lane
+        // -- 1. coarse histogram
+        for (int i = l; i < NC + 64 + REF_NB / 2 + 64; i += 64) h1[i] = 0u;
+        wave_lds_sync();
+#pragma unroll
+        for (int e = 0; e < REF_E / 4; ++e)
+            if (e < e4) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint32_t k = key[4 * e + v];
+                    atomicAdd(&h1[k != 0u ? (k - mn) >> sh1 : (uint32_t)(NC + l)], 1u);
+                }
+            }
+        wave_lds_sync();
+        // lane l owns coarse bins [NC - CPL (l + 1), NC - CPL l), the top first
+        uint32_t *mine = h1 + NC - CPL * (l + 1);
+        {
+            uint32_t loc = 0;
+#pragma unroll
+            for (int i = 0; i < CPL / 4; ++i) {
+                const uint4 c4 = *(const uint4 *)(mine + 4 * i);
+                loc += c4.x + c4.y + c4.z + c4.w;
+            }
+            uint32_t run = wave_incl_scan(loc) - loc;
+#pragma unroll
+            for (int i = CPL - 1; i >= 0; --i) {
+                const uint32_t c = mine[i];
+                if (run < msel && msel <= run + c) {
+                    vars[0] = (uint32_t)(NC - CPL * (l + 1) + i);
+                    vars[1] = run + c;
+                }
+                run += c;
+            }
+        }
+        wave_lds_sync();
+        const uint32_t b1 = vars[0];
+        const uint32_t nt = vars[1];  // keys in coarse bins >= b1
+        // -- 2. fine buckets per coarse bin: n = the power of two nearest to
+        //    0.9 * count * 2048 / nt (rounded down instead when that
+        //    overshoots 2048 in all), at least 2^(sh1 - 20) so that a key's
+        //    bits inside its fine bucket fit 20 bits, at most 2^sh1. Table
+        //    word = fine base | log2(n) << 12.
+        const uint32_t lgmin = sh1 > 20 ? (uint32_t)(sh1 - 20) : 0u;
+        for (int round_down = 0; round_down < 2; ++round_down) {
+            uint32_t lgs[CPL], loc = 0;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const uint32_t bin = NC - CPL * (l + 1) + i;
+                const uint32_t c = h1[bin];
+                uint32_t lg = 0xFFu;  // no fine buckets
+                if (bin >= b1 && c != 0u) {
+                    const uint32_t want = max(1u, (uint32_t)(((uint64_t)c * (REF_NB * 9 / 10)) / nt));
+                    lg = (uint32_t)(31 - __clz((int)want));
+                    // nearest: round up when want >= 1.5 * 2^lg
+                    if (!round_down && 2u * want >= 3u << lg) ++lg;
+                    lg = min(lg, (uint32_t)sh1);
+                    lg = max(lg, lgmin);
+                    loc += 1u << lg;
+                }
+                lgs[i] = lg;
+            }
+            const uint32_t total = wave_sum(loc);
+            if (total > (uint32_t)REF_NB && !round_down) continue;
+            uint32_t run = wave_incl_scan(loc) - loc;
+            wave_lds_sync();
+#pragma unroll
+            for (int i = CPL - 1; i >= 0; --i) {
+                const uint32_t lg = lgs[i];
+                mine[i] = lg == 0xFFu ? 0xFFFFFFFFu : (run | (lg << 12));
+                if (lg != 0xFFu) run += 1u << lg;
+            }
+            if (l == 63) vars[2] = run;  // fine buckets in use
+            break;
+        }
+        wave_lds_sync();
+        if (vars[2] <= (uint32_t)REF_NB && !p.out_score) {
+            // packed word of a key: fine bucket << 20 | its bits inside the
+            // fine bucket (0 = best bucket); 0xFFFFFFFF when not wanted
+            // (branch-free: the table is read for every key, so the reads of
+            // many keys overlap instead of waiting one by one)
+            auto packed = [&](uint32_t k) -> uint32_t {
+                const uint32_t rel = k - mn;
+                const uint32_t bin = rel >> sh1;
+                const uint32_t t = h1[min(bin, (uint32_t)(NC - 1))];
+                const uint32_t lg = (t >> 12) & 31u;
+                const uint32_t sub = ((uint32_t)sh1 - lg) & 31u;
+                const uint32_t low = rel & ((1u << sh1) - 1u);
+                const uint32_t w =
+                    (((t & 0xFFFu) + ((1u << lg) - 1u - (low >> sub))) << 20) | (low & ((1u << sub) - 1u));
+                return (k == 0u || bin < b1) ? 0xFFFFFFFFu : w;
+            };
+            const uint32_t trashf = (uint32_t)(REF_NB + 2 * l);
+            // -- 3. fine histogram, crossing, offsets
+#pragma unroll
+            for (int e = 0; e < REF_E / 4; ++e)
+                if (e < e4) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const uint32_t w = packed(key[4 * e + v]);
+                        const uint32_t f = w == 0xFFFFFFFFu ? trashf : (w >> 20);
+                        atomicAdd(&h2[f >> 1], 1u << ((f & 1u) << 4));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);  // bound the loads in flight
+                }
+            wave_lds_sync();
+            {
+                uint32_t *fw = h2 + (REF_NB / 128) * l;  // lane l: fine buckets 32 l .. 32 l + 31
+                uint32_t loc = 0;
+#pragma unroll
+                for (int i = 0; i < REF_NB / 512; ++i) {
+                    const uint4 c4 = *(const uint4 *)(fw + 4 * i);
+                    loc += (c4.x & 0xFFFFu) + (c4.x >> 16) + (c4.y & 0xFFFFu) + (c4.y >> 16) +
+                           (c4.z & 0xFFFFu) + (c4.z >> 16) + (c4.w & 0xFFFFu) + (c4.w >> 16);
+                }
+                uint32_t run = wave_incl_scan(loc) - loc;
+#pragma unroll
+                for (int i = 0; i < REF_NB / 512; ++i) {
+                    const uint4 c4 = *(const uint4 *)(fw + 4 * i);
+                    const uint32_t w4[4] = {c4.x, c4.y, c4.z, c4.w};
+                    uint32_t o4[4];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const uint32_t c = (w4[t >> 1] >> ((t & 1) << 4)) & 0xFFFFu;
+                        if (t & 1) o4[t >> 1] |= run << 16;
+                        else o4[t >> 1] = run;
+                        if (run < msel && msel <= run + c) {
+                            vars[3] = (uint32_t)(32 * l + 8 * i + t);
+                            vars[4] = run + c;
+                        }
+                        run += c;
+                    }
+                    *(uint4 *)(fw + 4 * i) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+                }
+            }
+            wave_lds_sync();
+            const uint32_t fstar = vars[3];
+            const uint32_t nsc = vars[4];
+            if (nsc <= cap) {
+                // from here on each key register holds its packed word (every
+                // slot, so empty ones read as "not wanted" in all passes)
+#pragma unroll
+                for (int e = 0; e < REF_E / 4; ++e) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) key[4 * e + v] = e < e4 ? packed(key[4 * e + v]) : 0xFFFFFFFFu;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // -- 4. scatter fine buckets 0 .. fstar (slots of 8 keys
+                //    claimed before any is stored, so the atomics overlap)
+#pragma clang loop unroll(full)
+                for (int e0 = 0; e0 < REF_E / 4; e0 += 2)
+                    if (e0 < e4) {
+                        uint32_t got[8], fb[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const uint32_t w = key[4 * e0 + i];
+                            fb[i] = (w == 0xFFFFFFFFu || (w >> 20) > fstar) ? trashf : (w >> 20);
+                            got[i] = atomicAdd(&h2[fb[i] >> 1], 1u << ((fb[i] & 1u) << 4));
+                        }
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const int e = e0 + i / 4, v = i % 4;
+                            const bool take = fb[i] < (uint32_t)REF_NB && e < e4;
+                            const uint32_t slot = (got[i] >> ((fb[i] & 1u) << 4)) & 0xFFFFu;
+                            buf[take ? slot : cap + l] =
+                                ((key[4 * e0 + i] & 0xFFFFFu) << 12) | (uint32_t)((e * 64 + l) * 4 + v);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                wave_lds_sync();
+                // counter f now ends fine bucket f; it starts where f-1 ends.
+                // Each element counts the entries of its bucket ranking above
+                // it: the first eight in one go, any further ones, and equal
+                // keys (by key index), in a counted loop.
+                auto fend = [&](uint32_t f) { return (h2[f >> 1] >> ((f & 1u) << 4)) & 0xFFFFu; };
+#pragma clang loop unroll(full)
+                for (int e = 0; e < REF_E / 4; ++e)
+                    if (e < e4) {
+#pragma clang loop unroll(full)
+                        for (int v = 0; v < 4; ++v) {
+                            const uint32_t w = key[4 * e + v];
+                            const bool sel = w != 0xFFFFFFFFu && (w >> 20) <= fstar;
+                            const uint32_t f = sel ? (w >> 20) : 0u;
+                            const uint32_t pos = (e * 64 + l) * 4 + v;
+                            const uint32_t lo = (w & 0xFFFFFu) << 12;  // my key bits, any position
+                            const uint32_t hi = lo | 4095u;
+                            // both counters read unconditionally (f - 1 wraps to a
+                            // valid bucket when f == 0), then masked
+                            const uint32_t e1 = fend(f), e0 = fend(min(f - 1u, (uint32_t)REF_NB - 1u));
+                            const uint32_t end = sel ? e1 : 0u;
+                            const uint32_t beg = f == 0u ? 0u : e0;
+                            const uint32_t cnt = end - beg;
+                            // entries ranking above me: key bits > mine (packed
+                            // word > hi); entries with my key bits: lo <= word <= hi
+                            // (one of them is me). Slots past the bucket are read
+                            // (they exist: 64 trash slots follow the buffer) and
+                            // masked to 0.
+                            const uint32_t *bp = buf + beg;
+                            uint32_t above = 0, same = 0;
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                const uint32_t raw = bp[i];
+                                const uint32_t en = (uint32_t)i < cnt ? raw : 0u;
+                                above += en > hi;
+                                same += en >= lo;
+                            }
+                            same -= above;
+                            // masked slots (0) count as "same" when lo == 0
+                            if (lo == 0u) same -= 8u - min(cnt, 8u);
+                            uint32_t rank = above;
+                            if (cnt > 8u || same > 1u) {
+                                // long bucket or equal keys: count exactly, equal
+                                // keys ranked by key index
+                                rank = 0;
+                                const uint32_t myidx = cl[pos];
+                                for (uint32_t u = beg; u < end; ++u) {
+                                    const uint32_t en = buf[u];
+                                    if (en > hi) ++rank;
+                                    else if (en >= lo && (en & 4095u) != pos) rank += cl[en & 4095u] < myidx;
+                                }
+                            }
+                            const uint32_t fin = beg + rank;
+                            if (sel && fin < msel) p.out_idx[obase + fin] = (int32_t)cl[pos];
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                for (int c = (int)msel + l; c < p.top_k; c += 64) p.out_idx[obase + c] = -1;
+                return;
+            }
+        }
+        wave_lds_sync();
+    }
+
+    // ---- general path: the boundary bucket is too large to stage (heavy
+    // ties); exact narrowing selection, then a bucket sort of the selection
     uint32_t *hist = (uint32_t *)my;                  // 1024 words
     uint32_t *vars = hist + (1 << REF_LOG2NB);
     uint32_t *red = vars + 8;
@@ -781,20 +1113,28 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     Selector<1, REF_LOG2NB> sel{G, hist, vars};
     auto fe = [&](auto f) {
 #pragma unroll
-        for (int e = 0; e < REF_E; ++e)
-            if (e * 64 + l < nc) f(key[e], (uint32_t)(e * 64 + l));
+        for (int e = 0; e < REF_E / 4; ++e)
+            if (e < e4) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) f(key[4 * e + v], (uint32_t)((e * 64 + l) * 4 + v));
+            }
     };
     auto idx_of = [&](uint32_t pos) { return cl[pos]; };
-    const uint32_t msel = (uint32_t)min(p.top_k, nc);
-    const Rule rule = sel.select(fe, idx_of, (uint32_t)nc, msel);
+    const Rule rule = msel >= (uint32_t)nc ? Rule{0u, 0u} : sel.select(fe, idx_of, (uint32_t)e4 * 256u, msel);
     auto fs = [&](auto f) {
 #pragma unroll
-        for (int e = 0; e < REF_E; ++e) {
-            const uint32_t pos = e * 64 + l;
-            if (pos < (uint32_t)nc && rule.sel(key[e], cl[pos])) f(key[e], pos);
-        }
+        for (int e = 0; e < REF_E / 4; ++e)
+            if (e < e4) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint32_t k = key[4 * e + v];
+                    const uint32_t pos = (e * 64 + l) * 4 + v;
+                    bool take = k > rule.T;
+                    if (k == rule.T) take = (~cl[pos]) >= rule.I;
+                    if (k != 0u && take) f(k, pos);
+                }
+            }
     };
-    const int64_t obase = ((qrow0 + q0 + w) * p.H + h) * (int64_t)p.top_k;
     sel.sort_selected(fs, idx_of, msel, bufk, bufp,
                       [&](uint32_t pos, uint32_t k, uint32_t pl) {
                           p.out_idx[obase + pos] = (int32_t)cl[pl];
@@ -954,10 +1294,36 @@ size_t sel_lds_bytes(int D) {
     return ((size_t)(1 << SEL_LOG2NB) + 8 + 16 + 4 + 2 * MAX_TOPK) * 4 + (size_t)D * 4;
 }
 
-size_t ref_reg_bytes(int64_t K, int top_k) {
-    size_t a = (size_t)K * 4;
-    size_t b = ((size_t)(1 << REF_LOG2NB) + 8 + 16) * 4 + (size_t)top_k * 6;
-    return (std::max(a, b) + 15) & ~(size_t)15;
+// LDS layout of k_refine: candidate list + one region per query wavefront.
+// A region holds the query's scores first, then either the fused select
+// (header + staged keys/positions) or the general selector's arrays; spare
+// LDS becomes staging slack for the boundary bucket.
+struct RefLayout {
+    int nqw, reg_bytes, cap;
+    size_t lds;
+};
+constexpr size_t LDS_MAX = 163840;
+
+RefLayout refine_layout(int64_t K, int top_k, int g) {
+    RefLayout L{};
+    const size_t clb = ((size_t)K * 4 + 15) & ~(size_t)15;
+    const size_t r_scores = (size_t)((K + 255) / 256) * 1024;
+    const size_t r_general = ((size_t)(1 << REF_LOG2NB) + 8 + 16) * 4 + (size_t)top_k * 6;
+    const size_t r_fused = (size_t)REF_HDR + 4 * ((size_t)top_k + 64 + 64);
+    const size_t r_full = (size_t)REF_HDR + 4 * ((size_t)REF_FIX * 64 + 64);
+    size_t need = std::max(r_scores, r_general);
+    L.nqw = std::min(g, 8);
+    // prefer room for the fused path; give up queries per block before it
+    while (L.nqw > 1 && clb + (size_t)L.nqw * std::max(need, r_fused) > LDS_MAX) --L.nqw;
+    size_t spare = ((LDS_MAX - clb) / (size_t)L.nqw) & ~(size_t)15;
+    size_t r = std::min(spare, r_full);
+    r = std::max(r, need);
+    r = (r + 15) & ~(size_t)15;
+    L.reg_bytes = (int)r;
+    // entries of the staging buffer, less the 64 trash slots at its end
+    L.cap = r > (size_t)REF_HDR + 256 ? (int)std::min<size_t>((r - REF_HDR) / 4 - 64, (size_t)REF_FIX * 64) : 0;
+    L.lds = clb + (size_t)L.nqw * r;
+    return L;
 }
 
 template <typename T, int D>
@@ -1135,13 +1501,15 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             rp.S = pl.S;
             rp.decode = 0;
             rp.offs = nullptr;
-            rp.nqw = std::min(pl.g, 8);
+            const RefLayout lay = refine_layout(pl.K, pl.top_k, pl.g);
+            rp.nqw = lay.nqw;
             rp.nqb = (pl.g + rp.nqw - 1) / rp.nqw;
             rp.top_k = pl.top_k;
-            rp.reg_bytes = (int)ref_reg_bytes(pl.K, pl.top_k);
+            rp.reg_bytes = lay.reg_bytes;
+            rp.ref_cap = lay.cap;
             rp.out_idx = out_idx;
             rp.out_score = out_score;
-            const size_t lds = ((size_t)pl.K * 4 + 15) / 16 * 16 + (size_t)rp.nqw * rp.reg_bytes;
+            const size_t lds = lay.lds;
             const int nblocks = (int)(rows * rp.nqb);
             StageTimer tm(ST_REFINE, st);
             int rc = dispatch_refine<T>(pl.D, rp, nblocks, lds, st);
@@ -1290,13 +1658,15 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
         rp.S = (int64_t)dp.B * dp.g;
         rp.decode = 1;
         rp.offs = offs;
-        rp.nqw = std::min(dp.g, 8);
+        const RefLayout lay = refine_layout(dp.K, dp.top_k, dp.g);
+        rp.nqw = lay.nqw;
         rp.nqb = (dp.g + rp.nqw - 1) / rp.nqw;
         rp.top_k = dp.top_k;
-        rp.reg_bytes = (int)ref_reg_bytes(dp.K, dp.top_k);
+        rp.reg_bytes = lay.reg_bytes;
+        rp.ref_cap = lay.cap;
         rp.out_idx = out_idx;
         rp.out_score = out_score;
-        const size_t lds = ((size_t)dp.K * 4 + 15) / 16 * 16 + (size_t)rp.nqw * rp.reg_bytes;
+        const size_t lds = lay.lds;
         const int nblocks = dp.B * dp.H * rp.nqb;
         StageTimer tm(ST_REFINE, st);
         int rc = dispatch_refine<T>(dp.D, rp, nblocks, lds, st);
