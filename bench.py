@@ -43,6 +43,38 @@ def prefix_sums(S: int, g: int, K: int):
     return int(n.sum()), int(np.minimum(n, K).sum())
 
 
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "top_token_selection_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def counted_traffic(stage: str, S: int, H: int, g: int):
+    """HBM bytes per launch of a stage's kernel, as counted by FETCH_SIZE and
+    WRITE_SIZE (scaled by a copy kernel of known size) in a committed counter
+    summary; None when there is none for this workload or the kernel sources
+    have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{stage}_hbm_traffic_S{S}_H{H}_g{g}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith(" "):
+                key, _, v = ln.partition(":")
+                vals[key.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return float(vals["read_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def time_calls(fn, steps: int, warmup: int, pv):
     import torch
     for _ in range(warmup):
@@ -78,6 +110,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     ap.add_argument("--recall-rows", type=int, default=256)
     ap.add_argument("--long", action="store_true", help="S=131072, H=32, g=16 instead")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run one plain float32 copy kernel (1 GiB read, 1 GiB written) so that "
+                         "a counter run can scale FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -94,6 +129,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calib_copy:
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n * 4} bytes read, {n * 4} bytes written")
+        del src, dst
     S, H, g = (131072, 32, 16) if args.long else (65536, 64, 8)
     D, top_k, ratio = 128, 2048, 2.0
     K = pv.candidate_count(top_k, ratio)
@@ -150,7 +194,7 @@ def main():
         achieved = amount / max(1, launches.get(dom, 1)) / t
         scale = 1e12 if unit == "TFLOP/s" else 1e9
         roof = {"bound": bound, "kernel": dom, "achieved": achieved / scale, "peak": peak / scale,
-                "unit": unit, "frac": achieved / peak, "traffic": None}
+                "unit": unit, "frac": achieved / peak, "traffic": counted_traffic(dom, S, H, g)}
     scan_t = stages.get("scan", 0.0) / 1e3
     scan_roof = {"bound": "mfma", "achieved": scan_flops / scan_t / 1e12 if scan_t else None,
                  "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
