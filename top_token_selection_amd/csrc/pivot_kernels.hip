@@ -913,6 +913,7 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
         //    bits inside its fine bucket fit 20 bits, at most 2^sh1. Table
         //    word = fine base | log2(n) << 12.
         const uint32_t lgmin = sh1 > 20 ? (uint32_t)(sh1 - 20) : 0u;
+        const float scl = (float)(REF_NB * 9 / 10) / (float)nt;
         for (int round_down = 0; round_down < 2; ++round_down) {
             uint32_t lgs[CPL], loc = 0;
 #pragma unroll
@@ -921,7 +922,7 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
                 const uint32_t c = h1[bin];
                 uint32_t lg = 0xFFu;  // no fine buckets
                 if (bin >= b1 && c != 0u) {
-                    const uint32_t want = max(1u, (uint32_t)(((uint64_t)c * (REF_NB * 9 / 10)) / nt));
+                    const uint32_t want = max(1u, (uint32_t)((float)c * scl));
                     lg = (uint32_t)(31 - __clz((int)want));
                     // nearest: round up when want >= 1.5 * 2^lg
                     if (!round_down && 2u * want >= 3u << lg) ++lg;
@@ -1007,7 +1008,13 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
             wave_lds_sync();
             const uint32_t fstar = vars[3];
             const uint32_t nsc = vars[4];
-            if (nsc <= cap) {
+            // h1 (the table, dead once every key is packed) then holds a 16-bit
+            // bucket tag per staged entry; h1..h2 (dead once every rank is
+            // known) then hold the finished row.
+            constexpr uint32_t STG = (uint32_t)(NC + 64 + REF_NB / 2 + 64);
+            constexpr uint32_t TAGS = 2u * (uint32_t)(NC + 64) - 64u;  // + 64 trash tags
+            constexpr int NSL = (int)(TAGS / 64u);                      // staged slots per lane
+            if (nsc <= cap && nsc <= TAGS && msel <= STG) {
                 // from here on each key register holds its packed word (every
                 // slot, so empty ones read as "not wanted" in all passes)
 #pragma unroll
@@ -1016,8 +1023,12 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
                     for (int v = 0; v < 4; ++v) key[4 * e + v] = e < e4 ? packed(key[4 * e + v]) : 0xFFFFFFFFu;
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                // -- 4. scatter fine buckets 0 .. fstar (slots of 8 keys
-                //    claimed before any is stored, so the atomics overlap)
+                wave_lds_sync();
+                uint16_t *tag = (uint16_t *)h1;
+                // -- 4. scatter fine buckets 0 .. fstar as (key bits in the
+                //    bucket << 12 | position) with the bucket as a tag (slots
+                //    of 8 keys claimed before any is stored, so the atomics
+                //    overlap)
 #pragma clang loop unroll(full)
                 for (int e0 = 0; e0 < REF_E / 4; e0 += 2)
                     if (e0 < e4) {
@@ -1035,67 +1046,71 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
                             const uint32_t slot = (got[i] >> ((fb[i] & 1u) << 4)) & 0xFFFFu;
                             buf[take ? slot : cap + l] =
                                 ((key[4 * e0 + i] & 0xFFFFFu) << 12) | (uint32_t)((e * 64 + l) * 4 + v);
+                            tag[take ? slot : TAGS + l] = (uint16_t)fb[i];
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 wave_lds_sync();
-                // counter f now ends fine bucket f; it starts where f-1 ends.
-                // Each element counts the entries of its bucket ranking above
-                // it: the first eight in one go, any further ones, and equal
-                // keys (by key index), in a counted loop.
+                // -- 5. rank inside the bucket, one staged entry per lane and
+                //    step: counter f now ends fine bucket f, which starts where
+                //    f-1 ends; the entry counts the entries of its bucket that
+                //    rank above it (the first eight in one go; longer buckets
+                //    and equal keys, by key index, in a counted loop). The
+                //    final (slot, position) pairs wait in the key registers.
                 auto fend = [&](uint32_t f) { return (h2[f >> 1] >> ((f & 1u) << 4)) & 0xFFFFu; };
 #pragma clang loop unroll(full)
-                for (int e = 0; e < REF_E / 4; ++e)
-                    if (e < e4) {
-#pragma clang loop unroll(full)
-                        for (int v = 0; v < 4; ++v) {
-                            const uint32_t w = key[4 * e + v];
-                            const bool sel = w != 0xFFFFFFFFu && (w >> 20) <= fstar;
-                            const uint32_t f = sel ? (w >> 20) : 0u;
-                            const uint32_t pos = (e * 64 + l) * 4 + v;
-                            const uint32_t lo = (w & 0xFFFFFu) << 12;  // my key bits, any position
-                            const uint32_t hi = lo | 4095u;
-                            // both counters read unconditionally (f - 1 wraps to a
-                            // valid bucket when f == 0), then masked
-                            const uint32_t e1 = fend(f), e0 = fend(min(f - 1u, (uint32_t)REF_NB - 1u));
-                            const uint32_t end = sel ? e1 : 0u;
-                            const uint32_t beg = f == 0u ? 0u : e0;
-                            const uint32_t cnt = end - beg;
-                            // entries ranking above me: key bits > mine (packed
-                            // word > hi); entries with my key bits: lo <= word <= hi
-                            // (one of them is me). Slots past the bucket are read
-                            // (they exist: 64 trash slots follow the buffer) and
-                            // masked to 0.
-                            const uint32_t *bp = buf + beg;
-                            uint32_t above = 0, same = 0;
+                for (int i = 0; i < NSL; ++i) {
+                    const uint32_t u = (uint32_t)(i * 64 + l);
+                    key[i] = 0xFFFFFFFFu;
+                    if ((uint32_t)(i * 64) < nsc) {
+                        const bool act = u < nsc;
+                        const uint32_t uc = act ? u : 0u;
+                        const uint32_t w = buf[uc];
+                        const uint32_t f = tag[uc];
+                        const uint32_t pos = w & 4095u;
+                        const uint32_t lo = w & ~4095u;
+                        const uint32_t hi = lo | 4095u;
+                        const uint32_t end = fend(f);
+                        const uint32_t beg = f == 0u ? 0u : fend(min(f - 1u, (uint32_t)REF_NB - 1u));
+                        const uint32_t cnt = end - beg;
+                        // slots past the bucket are read (64 trash slots follow
+                        // the buffer) and masked to 0
+                        const uint32_t *bp = buf + beg;
+                        uint32_t above = 0, same = 0;
 #pragma unroll
-                            for (int i = 0; i < 8; ++i) {
-                                const uint32_t raw = bp[i];
-                                const uint32_t en = (uint32_t)i < cnt ? raw : 0u;
-                                above += en > hi;
-                                same += en >= lo;
-                            }
-                            same -= above;
-                            // masked slots (0) count as "same" when lo == 0
-                            if (lo == 0u) same -= 8u - min(cnt, 8u);
-                            uint32_t rank = above;
-                            if (cnt > 8u || same > 1u) {
-                                // long bucket or equal keys: count exactly, equal
-                                // keys ranked by key index
-                                rank = 0;
-                                const uint32_t myidx = cl[pos];
-                                for (uint32_t u = beg; u < end; ++u) {
-                                    const uint32_t en = buf[u];
-                                    if (en > hi) ++rank;
-                                    else if (en >= lo && (en & 4095u) != pos) rank += cl[en & 4095u] < myidx;
-                                }
-                            }
-                            const uint32_t fin = beg + rank;
-                            if (sel && fin < msel) p.out_idx[obase + fin] = (int32_t)cl[pos];
+                        for (int t = 0; t < 8; ++t) {
+                            const uint32_t raw = bp[t];
+                            const uint32_t en = (uint32_t)t < cnt ? raw : 0u;
+                            above += en > hi;
+                            same += en >= lo;
                         }
-                        __builtin_amdgcn_sched_barrier(0);
+                        same -= above;
+                        // masked slots (0) count as "same" when lo == 0
+                        if (lo == 0u) same -= 8u - min(cnt, 8u);
+                        uint32_t rank = above;
+                        if (act && (cnt > 8u || same > 1u)) {
+                            rank = 0;
+                            const uint32_t myidx = cl[pos];
+                            for (uint32_t x = beg; x < end; ++x) {
+                                const uint32_t en = buf[x];
+                                if (en > hi) ++rank;
+                                else if (en >= lo && (en & 4095u) != pos) rank += cl[en & 4095u] < myidx;
+                            }
+                        }
+                        const uint32_t fin = beg + rank;
+                        if (act && fin < msel) key[i] = (fin << 12) | pos;
                     }
-                for (int c = (int)msel + l; c < p.top_k; c += 64) p.out_idx[obase + c] = -1;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                wave_lds_sync();
+                // -- 6. finished row into LDS, then out with whole-line stores
+                uint32_t *row = h1;
+#pragma unroll
+                for (int i = 0; i < NSL; ++i)
+                    if (key[i] != 0xFFFFFFFFu) row[key[i] >> 12] = cl[key[i] & 4095u];
+                wave_lds_sync();
+                int32_t *dst = p.out_idx + obase;
+                for (int c = l; c < p.top_k; c += 64) dst[c] = c < (int)msel ? (int32_t)row[c] : -1;
                 return;
             }
         }
