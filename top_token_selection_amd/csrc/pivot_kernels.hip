@@ -130,20 +130,28 @@ struct ScanParams {
     int g;                  // group size (prefix of row j = max(j*g, 1))
     int kstride, koff;      // key sampling
     const float *tau;       // per-row threshold, nullptr = keep all
-    uint2 *out;             // survivors (key, index) [(row*2+half)*cap + slot]
-    int cap_half;
-    int *cnt;               // survivors per (row, half), may exceed cap
+    uint32_t *out;          // survivors [(row*2+half)*stride + slot]: (float bits, key)
+                            // pairs, or float bits alone in the sample pass
+    int cap_half;           // more than this many in a half = overflow
+    int stride;             // slots per (row, half): cap_half + 32
+    int *cnt;               // survivors per (row, half); > cap_half = overflow
     int64_t min_n;          // rows with prefix <= min_n are skipped
+    int scores_only;        // sample pass: any kstride, no keys stored
     int n_tiles, Hc;
 };
 
 // One block: 256 consecutive groups of one head against every key of their
-// prefixes, 64 keys per step. MFMA 32x32 with keys as the A operand (rows)
+// prefixes, 64 keys per step. MFMA 32x32x16 with keys as the A operand (rows)
 // and proxies as B (columns): lane l holds column l%32 of each 32x32 tile,
 // i.e. one group, for 16 keys -- its threshold and running survivor count
-// stay in registers. Keys stream through double-buffered LDS tiles.
-template <typename T, int D>
-__global__ void __launch_bounds__(SCAN_THREADS) k_scan(ScanParams p) {
+// stay in registers. Keys stream through double-buffered LDS tiles. Two
+// blocks share a CU so that one block's filtering overlaps the other's
+// matrix work. Survivors are stored as raw float bits; a half that passes
+// cap_half survivors stops storing (its row takes the exact fallback).
+// STRIDED: the sample pass (every kstride-th key; scores only, no keys);
+// otherwise kstride is 1 and each survivor is a (float bits, key) pair.
+template <typename T, int D, bool STRIDED>
+__global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     constexpr int RB = D * (int)sizeof(T);     // bytes per key row
     constexpr int KROW = RB + 16;              // LDS row stride (bank spread)
     constexpr int NCH = RB / 64;               // 16-byte chunks per thread per tile
@@ -160,23 +168,37 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_scan(ScanParams p) {
     const int64_t jlast = min(j0 + SCAN_ROWS - 1, p.G - 1);
     const int64_t vmax = virt_count(prefix_len(jlast, p.g) > p.min_n ? prefix_len(jlast, p.g) : 0,
                                     p.kstride, p.koff);
+    // keys below every row's count in this wavefront need no causal test
+    // (rows past the last group store nothing: the whole wavefront then
+    // takes the causal test)
+    int64_t vfull = 0;
+    {
+        const int64_t jw = j0 + 64 * w;
+        if (jw + 63 < p.G && prefix_len(jw, p.g) > p.min_n)
+            vfull = virt_count(prefix_len(jw, p.g), p.kstride, p.koff);
+    }
+    const float never = __builtin_nanf("");  // s >= NaN is false for every s
 
-    // this lane's two groups
-    int64_t row[2];
-    int64_t vcount[2];
+    // this lane's two groups; survivors go to byte offset soff[gb] from
+    // the block's part of the survivor arrays (uniform base + 32-bit offset)
+    constexpr uint32_t ESZ = STRIDED ? 4u : 8u;  // bytes per survivor
+    const int64_t bslot = ((int64_t)hl * p.G + j0) * 2 * (int64_t)p.stride;
+    unsigned char *sb = (unsigned char *)p.out + bslot * ESZ;
+    uint32_t soff[2], soff0[2];
+    int vcount[2];
     float tau[2];
-    int cntl[2] = {0, 0};
     for (int gb = 0; gb < 2; ++gb) {
-        const int64_t j = j0 + 64 * w + 32 * gb + (l & 31);
-        row[gb] = (int64_t)hl * p.G + j;
+        const int jl = 64 * w + 32 * gb + (l & 31);
+        const int64_t j = j0 + jl;
+        soff[gb] = soff0[gb] = (uint32_t)((jl * 2 + half) * p.stride) * ESZ;
         int64_t vc = 0;
-        tau[gb] = -INFINITY;
+        tau[gb] = never;  // rows past the end never store
         if (j < p.G) {
             const int64_t n = prefix_len(j, p.g);
             if (n > p.min_n) vc = virt_count(n, p.kstride, p.koff);
-            if (p.tau) tau[gb] = p.tau[row[gb]];
+            tau[gb] = p.tau ? p.tau[(int64_t)hl * p.G + j] : -INFINITY;
         }
-        vcount[gb] = vc;
+        vcount[gb] = (int)vc;
     }
 
     // proxies as resident B fragments
@@ -198,17 +220,20 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_scan(ScanParams p) {
         }
     }
 
-    const int64_t ntiles_k = (vmax + SCAN_KEYS - 1) / SCAN_KEYS;
+    const int ntiles_k = (int)((vmax + SCAN_KEYS - 1) / SCAN_KEYS);
     const T *Kb = (const T *)p.K + p.k_head0 + (int64_t)hl * p.k_head;
     unsigned char *buf0 = smem;
     unsigned char *buf1 = smem + SCAN_KEYS * KROW;
+    const uint32_t kstr = (uint32_t)p.kstride;
+    const uint32_t lane_key = (uint32_t)p.koff + kstr * (uint32_t)(4 * half);
 
     uint4 pre[NCH];
-    auto gload = [&](int64_t kt) {
+    auto gload = [&](int kt) {
+#pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int ch = tid + SCAN_THREADS * i;
             const int r = ch / (RB / 16), c16 = ch % (RB / 16);
-            const int64_t v = kt * SCAN_KEYS + r;
+            const int64_t v = (int64_t)kt * SCAN_KEYS + r;
             if (v < vmax) {
                 const int64_t key = p.koff + (int64_t)p.kstride * v;
                 pre[i] = *(const uint4 *)((const unsigned char *)(Kb + key * p.k_row) + c16 * 16);
@@ -218,6 +243,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_scan(ScanParams p) {
         }
     };
     auto lstore = [&](unsigned char *dst) {
+#pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int ch = tid + SCAN_THREADS * i;
             const int r = ch / (RB / 16), c16 = ch % (RB / 16);
@@ -225,16 +251,21 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_scan(ScanParams p) {
         }
     };
 
+    // Order inside a step: matrix work on tile kt, then tile kt+1 (loaded
+    // during the previous step) into LDS, then the survivor stores, then the
+    // loads of tile kt+2. The wait for those loads (next step, after the
+    // matrix work) also covers the stores issued before them, which by then
+    // have had the whole matrix phase to complete.
     if (ntiles_k > 0) {
         gload(0);
         lstore(buf0);
+        if (ntiles_k > 1) gload(1);
     }
     __syncthreads();
 
-    for (int64_t kt = 0; kt < ntiles_k; ++kt) {
+    for (int kt = 0; kt < ntiles_k; ++kt) {
         unsigned char *cur = (kt & 1) ? buf1 : buf0;
         unsigned char *nxt = (kt & 1) ? buf0 : buf1;
-        if (kt + 1 < ntiles_k) gload(kt + 1);
 
         f32x16_t acc[2][2];
         for (int a = 0; a < 2; ++a)
@@ -262,42 +293,54 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_scan(ScanParams p) {
             }
         }
 
-        // keep the scores that reach the row's threshold
+        // a half past its capacity stops storing (its count stays above cap)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int gb = 0; gb < 2; ++gb)
+            if (soff[gb] - soff0[gb] > ESZ * (uint32_t)p.cap_half) tau[gb] = never;
+        // keep the scores that reach the row's threshold; at most 32 per
+        // half and tile, so a count <= cap_half leaves room in the stride.
+        // Tiles below every row's prefix end skip the causal test.
+        const uint32_t tkey = (uint32_t)(kt * SCAN_KEYS) + lane_key;  // used when kstride == 1
+        auto filter = [&](auto causal) {
 #pragma unroll
-            for (int gb = 0; gb < 2; ++gb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int64_t vk = kt * SCAN_KEYS + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                    const float s = acc[kb][gb][v];
-                    const bool keep = (vk < vcount[gb]) && (s >= tau[gb]);
-                    if (keep) {
-                        if (cntl[gb] < p.cap_half) {
-                            const int64_t key = p.koff + (int64_t)p.kstride * vk;
-                            p.out[(row[gb] * 2 + half) * (int64_t)p.cap_half + cntl[gb]] =
-                                make_uint2(score_key(s), (uint32_t)key);
+                for (int gb = 0; gb < 2; ++gb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int vo = kb * 32 + 8 * (v >> 2) + (v & 3);  // + 4 * half
+                        const float s = acc[kb][gb][v];
+                        bool keep = s >= tau[gb];
+                        if constexpr (decltype(causal)::value)
+                            keep = keep && (kt * SCAN_KEYS + vo + 4 * half < vcount[gb]);
+                        if (keep) {
+                            if constexpr (STRIDED)
+                                *(uint32_t *)(sb + soff[gb]) = __float_as_uint(s);
+                            else
+                                *(uint2 *)(sb + soff[gb]) = make_uint2(__float_as_uint(s), tkey + (uint32_t)vo);
+                            soff[gb] += ESZ;
                         }
-                        cntl[gb] += 1;
                     }
-                }
-
+        };
         if (kt + 1 < ntiles_k) lstore(nxt);
+        if ((int64_t)(kt + 1) * SCAN_KEYS <= vfull) filter(std::false_type{});
+        else filter(std::true_type{});
+        if (kt + 2 < ntiles_k) gload(kt + 2);
         __syncthreads();
     }
 
     for (int gb = 0; gb < 2; ++gb) {
         const int64_t j = j0 + 64 * w + 32 * gb + (l & 31);
-        if (j < p.G) p.cnt[row[gb] * 2 + half] = cntl[gb];
+        if (j < p.G) p.cnt[((int64_t)hl * p.G + j) * 2 + half] = (int)((soff[gb] - soff0[gb]) / ESZ);
     }
 }
 
 // -------------------------------------------------------------------- tau
 
 struct TauParams {
-    const uint2 *samp;
+    const uint32_t *samp;   // sample scores' float bits
     const int *scnt;
-    int samp_half;
+    int samp_half, samp_stride;
     float *tau;
     int64_t G;
     int g;
@@ -331,14 +374,17 @@ __global__ void __launch_bounds__(SEL_THREADS) k_tau(TauParams p) {
     Selector<4, SEL_LOG2NB> sel{G, hist, vars};
     const int elim = (int)((ns + SEL_THREADS - 1) / SEL_THREADS);
     uint32_t key[TAU_E];
-    const uint2 *b0 = p.samp + (2 * r) * (int64_t)p.samp_half;
-    const uint2 *b1 = p.samp + (2 * r + 1) * (int64_t)p.samp_half;
+    const uint32_t *b0 = p.samp + (2 * r) * (int64_t)p.samp_stride;
+    const uint32_t *b1 = p.samp + (2 * r + 1) * (int64_t)p.samp_stride;
+    bool has[TAU_E];
 #pragma unroll
     for (int e = 0; e < TAU_E; ++e) {
         const uint32_t gi = e * SEL_THREADS + threadIdx.x;
-        key[e] = 0u;
-        if (e < elim && gi < ns) key[e] = gi < (uint32_t)c0 ? b0[gi].x : b1[gi - c0].x;
+        has[e] = e < elim && gi < ns;
+        key[e] = has[e] ? (gi < (uint32_t)c0 ? b0[gi] : b1[gi - c0]) : 0u;
     }
+#pragma unroll
+    for (int e = 0; e < TAU_E; ++e) key[e] = has[e] ? score_key(__uint_as_float(key[e])) : 0u;
     auto fe = [&](auto f) {
 #pragma unroll
         for (int e = 0; e < TAU_E; ++e)
@@ -392,7 +438,7 @@ __device__ void pad_member_rows(const RowOut &o, int hl, int64_t j, uint32_t fro
 struct SelParams {
     const uint2 *surv;
     const int *cnt;
-    int cap_half;
+    int cap_half, stride;
     int64_t G;
     int g;
     int64_t Ksel;     // how many to select (K for Refine, top_k otherwise)
@@ -449,8 +495,9 @@ __global__ void __launch_bounds__(SEL_THREADS) k_select(SelParams p) {
     Group<4> G{(int)threadIdx.x, red};
     Selector<4, SEL_LOG2NB> sel{G, hist, vars};
     uint32_t key[SEL_E], pl[SEL_E];
-    const uint2 *b0 = p.surv + (2 * r) * (int64_t)p.cap_half;
-    const uint2 *b1 = p.surv + (2 * r + 1) * (int64_t)p.cap_half;
+    const uint2 *b0 = p.surv + (2 * r) * (int64_t)p.stride;
+    const uint2 *b1 = p.surv + (2 * r + 1) * (int64_t)p.stride;
+    // all loads first (independent, in flight together), then the keys
 #pragma unroll
     for (int e = 0; e < SEL_E; ++e) {
         const uint32_t gi = e * SEL_THREADS + threadIdx.x;
@@ -459,6 +506,9 @@ __global__ void __launch_bounds__(SEL_THREADS) k_select(SelParams p) {
         key[e] = x.x;
         pl[e] = x.y;
     }
+#pragma unroll
+    for (int e = 0; e < SEL_E; ++e)
+        key[e] = pl[e] == 0xFFFFFFFFu ? 0u : score_key(__uint_as_float(key[e]));
     auto fe = [&](auto f) {
 #pragma unroll
         for (int e = 0; e < SEL_E; ++e)
@@ -1283,8 +1333,8 @@ int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio,
     pl.b_tau = align256(rows * 4);
     pl.b_cnt = align256(rows * 8);
     pl.b_scnt = align256(rows * 8);
-    pl.b_surv = align256(rows * 2 * (size_t)pl.cap_half * 8);
-    pl.b_samp = pl.n_max > pl.keep_all_n ? align256(rows * 2 * (size_t)pl.samp_half * 8) : 0;
+    pl.b_surv = align256(rows * 2 * (size_t)(pl.cap_half + 32) * 8);
+    pl.b_samp = pl.n_max > pl.keep_all_n ? align256(rows * 2 * (size_t)(pl.samp_half + 32) * 4) : 0;
     pl.b_cand = pl.mode == PIVOT_REFINE ? align256(rows * (size_t)K * 4) : 0;
     pl.b_fbl = align256(rows * 4);
     pl.fixed = 256 + align256((size_t)FB_BLOCKS * (size_t)pl.n_max * 4);
@@ -1357,8 +1407,13 @@ int dispatch_refine(int D, const RefParams &rp, int nblocks, size_t lds, hipStre
 template <typename T, int D>
 int launch_scan(const ScanParams &sp, hipStream_t st) {
     const size_t lds = 2 * SCAN_KEYS * ((size_t)D * sizeof(T) + 16);
-    HIP_TRY(set_lds((const void *)k_scan<T, D>, lds));
-    hipLaunchKernelGGL((k_scan<T, D>), dim3(sp.Hc * sp.n_tiles), dim3(SCAN_THREADS), lds, st, sp);
+    if (!sp.scores_only) {  // main pass: every key (kstride 1), keys stored
+        HIP_TRY(set_lds((const void *)k_scan<T, D, false>, lds));
+        hipLaunchKernelGGL((k_scan<T, D, false>), dim3(sp.Hc * sp.n_tiles), dim3(SCAN_THREADS), lds, st, sp);
+    } else {
+        HIP_TRY(set_lds((const void *)k_scan<T, D, true>, lds));
+        hipLaunchKernelGGL((k_scan<T, D, true>), dim3(sp.Hc * sp.n_tiles), dim3(SCAN_THREADS), lds, st, sp);
+    }
     HIP_TRY(hipGetLastError());
     return PIVOT_OK;
 }
@@ -1392,8 +1447,8 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
         float *tau = (float *)take(pl.b_tau);
         int *cnt = (int *)take(pl.b_cnt);
         int *scnt = (int *)take(pl.b_scnt);
-        uint2 *surv = (uint2 *)take(pl.b_surv);
-        uint2 *samp = (uint2 *)take(pl.b_samp);
+        uint32_t *surv = (uint32_t *)take(pl.b_surv);
+        uint32_t *samp = (uint32_t *)take(pl.b_samp);
         uint32_t *cand = (uint32_t *)take(pl.b_cand);
         uint32_t *fbl = (uint32_t *)take(pl.b_fbl);
 
@@ -1431,7 +1486,9 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             ss.koff = pl.kstride - 1;
             ss.tau = nullptr;
             ss.out = samp;
+            ss.scores_only = 1;
             ss.cap_half = pl.samp_half;
+            ss.stride = pl.samp_half + 32;
             ss.cnt = scnt;
             ss.min_n = pl.keep_all_n;
             StageTimer tm(ST_SAMPLE, st);
@@ -1439,7 +1496,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             if (rc) return rc;
         }
         {
-            TauParams tp{samp, scnt, pl.samp_half, tau, pl.G, pl.g, pl.keep_all_n, pl.rsel};
+            TauParams tp{samp, scnt, pl.samp_half, pl.samp_half + 32, tau, pl.G, pl.g, pl.keep_all_n, pl.rsel};
             const size_t lds = ((size_t)(1 << SEL_LOG2NB) + 8 + 16) * 4;
             StageTimer tm(ST_TAU, st);
             hipLaunchKernelGGL(k_tau, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, tp);
@@ -1452,7 +1509,9 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             sm.koff = 0;
             sm.tau = tau;
             sm.out = surv;
+            sm.scores_only = 0;
             sm.cap_half = pl.cap_half;
+            sm.stride = pl.cap_half + 32;
             sm.cnt = cnt;
             sm.min_n = 0;
             StageTimer tm(ST_SCAN, st);
@@ -1471,7 +1530,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
         ro.g = pl.g;
         const int sorted_out = pl.mode == PIVOT_REUSE ? 1 : 0;
         {
-            SelParams se{surv, cnt, pl.cap_half, pl.G, pl.g, pl.Ksel, sorted_out, ro, fbl, fb_count};
+            SelParams se{(const uint2 *)surv, cnt, pl.cap_half, pl.cap_half + 32, pl.G, pl.g, pl.Ksel, sorted_out, ro, fbl, fb_count};
             const size_t lds = sel_lds_bytes(0);
             StageTimer tm(ST_SELECT, st);
             hipLaunchKernelGGL(k_select, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, se);
