@@ -44,7 +44,9 @@ namespace {
 
 constexpr int SCAN_THREADS = 256;  // 4 wavefronts
 constexpr int SCAN_ROWS = 256;     // groups per scan block (64 per wave)
-constexpr int SCAN_KEYS = 64;      // keys per k-tile
+constexpr int SCAN_KEYS = 32;      // keys per k-tile
+constexpr int RING = 16;           // staged survivors per (row, half) stream
+constexpr int FLUSH = 8;           // survivors written per flush (64 bytes)
 constexpr int SEL_THREADS = 256;
 constexpr int SEL_LOG2NB = 11;
 constexpr int SEL_E = 48;          // survivors per thread held in registers
@@ -130,32 +132,45 @@ struct ScanParams {
     int g;                  // group size (prefix of row j = max(j*g, 1))
     int kstride, koff;      // key sampling
     const float *tau;       // per-row threshold, nullptr = keep all
-    uint32_t *out;          // survivors [(row*2+half)*stride + slot]: (float bits, key)
-                            // pairs, or float bits alone in the sample pass
+    uint32_t *out;          // survivors [(row*2+half)*stride + slot]: (float bits, key) pairs
     int cap_half;           // more than this many in a half = overflow
     int stride;             // slots per (row, half): cap_half + 32
     int *cnt;               // survivors per (row, half); > cap_half = overflow
     int64_t min_n;          // rows with prefix <= min_n are skipped
-    int scores_only;        // sample pass: any kstride, no keys stored
     int n_tiles, Hc;
 };
 
 // One block: 256 consecutive groups of one head against every key of their
-// prefixes, 64 keys per step. MFMA 32x32x16 with keys as the A operand (rows)
+// prefixes, 32 keys per step. MFMA 32x32x16 with keys as the A operand (rows)
 // and proxies as B (columns): lane l holds column l%32 of each 32x32 tile,
 // i.e. one group, for 16 keys -- its threshold and running survivor count
-// stay in registers. Keys stream through double-buffered LDS tiles. Two
-// blocks share a CU so that one block's filtering overlaps the other's
-// matrix work. Survivors are stored as raw float bits; a half that passes
-// cap_half survivors stops storing (its row takes the exact fallback).
-// STRIDED: the sample pass (every kstride-th key; scores only, no keys);
-// otherwise kstride is 1 and each survivor is a (float bits, key) pair.
-template <typename T, int D, bool STRIDED>
+// stay in registers. Two blocks share a CU.
+//
+// Key tiles go from global memory straight into LDS (global_load_lds, lane i
+// of an instruction lands at base + 16 i), double-buffered, with the 16-byte
+// chunks of a key row XOR-swizzled by the row so that the fragment reads
+// spread over the banks. One step, for tile kt:
+//   wait for own loads/stores, barrier      (tile kt is in LDS)
+//   filter tile kt-1's scores
+//   issue the loads of tile kt+1            (into the buffer of tile kt-1)
+//   matrix work on tile kt
+// so loads and stores have a whole matrix phase to complete before the wait.
+//
+// Survivors ((float bits, key) pairs) of each (row, half) stream are staged
+// in an LDS ring of RING entries and leave in whole 64-byte chunks of FLUSH
+// entries, so the survivor array is written line by line instead of 8 bytes
+// at a time. A stream that passes cap_half survivors stops keeping (its row
+// takes the exact fallback).
+template <typename T, int D>
 __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     constexpr int RB = D * (int)sizeof(T);     // bytes per key row
-    constexpr int KROW = RB + 16;              // LDS row stride (bank spread)
-    constexpr int NCH = RB / 64;               // 16-byte chunks per thread per tile
+    constexpr int NCK = RB / 16;               // 16-byte chunks per key row
+    constexpr int SWZ = (NCK < 16 ? NCK : 16) - 1;
+    constexpr int TILE = SCAN_KEYS * RB;       // bytes per LDS tile
+    constexpr int NLD = SCAN_KEYS * NCK / SCAN_THREADS;  // loads per thread per tile
+    constexpr int NSTREAM = 2 * SCAN_THREADS;  // (row, half) streams per block
     extern __shared__ __align__(16) unsigned char smem[];
+    uint2 *ring = (uint2 *)(smem + 2 * TILE);  // [RING][NSTREAM]
 
     const int nb = p.Hc * p.n_tiles;
     const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)nb);
@@ -169,7 +184,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     const int64_t vmax = virt_count(prefix_len(jlast, p.g) > p.min_n ? prefix_len(jlast, p.g) : 0,
                                     p.kstride, p.koff);
     // keys below every row's count in this wavefront need no causal test
-    // (rows past the last group store nothing: the whole wavefront then
+    // (rows past the last group keep nothing: the whole wavefront then
     // takes the causal test)
     int64_t vfull = 0;
     {
@@ -179,20 +194,19 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     }
     const float never = __builtin_nanf("");  // s >= NaN is false for every s
 
-    // this lane's two groups; survivors go to byte offset soff[gb] from
-    // the block's part of the survivor arrays (uniform base + 32-bit offset)
-    constexpr uint32_t ESZ = STRIDED ? 4u : 8u;  // bytes per survivor
-    const int64_t bslot = ((int64_t)hl * p.G + j0) * 2 * (int64_t)p.stride;
-    unsigned char *sb = (unsigned char *)p.out + bslot * ESZ;
-    uint32_t soff[2], soff0[2];
+    // this lane's two streams: survivors cnt[gb] kept so far, fl[gb] of
+    // them already written to the stream's buffer at byte offset soff0[gb]
+    // from the block's part of the survivor array
+    unsigned char *sb = (unsigned char *)p.out + ((int64_t)hl * p.G + j0) * 2 * (int64_t)p.stride * 8;
+    uint32_t soff0[2], cnt[2] = {0u, 0u}, fl[2] = {0u, 0u};
     int vcount[2];
     float tau[2];
     for (int gb = 0; gb < 2; ++gb) {
         const int jl = 64 * w + 32 * gb + (l & 31);
         const int64_t j = j0 + jl;
-        soff[gb] = soff0[gb] = (uint32_t)((jl * 2 + half) * p.stride) * ESZ;
+        soff0[gb] = (uint32_t)((jl * 2 + half) * p.stride) * 8u;
         int64_t vc = 0;
-        tau[gb] = never;  // rows past the end never store
+        tau[gb] = never;  // rows past the end never keep
         if (j < p.G) {
             const int64_t n = prefix_len(j, p.g);
             if (n > p.min_n) vc = virt_count(n, p.kstride, p.koff);
@@ -200,6 +214,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
         }
         vcount[gb] = (int)vc;
     }
+    const int stream0 = w * 64 + l;  // stream of gb is gb * SCAN_THREADS + stream0
 
     // proxies as resident B fragments
     typedef typename std::conditional<std::is_same<T, float>::value, f32x4_t, bf16x8_t>::type frag_t;
@@ -221,124 +236,141 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     }
 
     const int ntiles_k = (int)((vmax + SCAN_KEYS - 1) / SCAN_KEYS);
-    const T *Kb = (const T *)p.K + p.k_head0 + (int64_t)hl * p.k_head;
-    unsigned char *buf0 = smem;
-    unsigned char *buf1 = smem + SCAN_KEYS * KROW;
+    const unsigned char *Kb = (const unsigned char *)((const T *)p.K + p.k_head0 + (int64_t)hl * p.k_head);
+    const int64_t krow_bytes = p.k_row * (int64_t)sizeof(T);
     const uint32_t kstr = (uint32_t)p.kstride;
     const uint32_t lane_key = (uint32_t)p.koff + kstr * (uint32_t)(4 * half);
 
-    uint4 pre[NCH];
-    auto gload = [&](int kt) {
+    // tile kt into LDS buffer kt & 1: instruction i of wavefront w fills
+    // slots (i*4 + w)*64 .. +63; slot q holds chunk (q % NCK) ^ swz(row) of
+    // key row q / NCK. Keys past the last row's prefix repeat the last key:
+    // their scores are never kept (that tile takes the causal test).
+    auto issue_tile = [&](int kt) {
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int ch = tid + SCAN_THREADS * i;
-            const int r = ch / (RB / 16), c16 = ch % (RB / 16);
-            const int64_t v = (int64_t)kt * SCAN_KEYS + r;
-            if (v < vmax) {
-                const int64_t key = p.koff + (int64_t)p.kstride * v;
-                pre[i] = *(const uint4 *)((const unsigned char *)(Kb + key * p.k_row) + c16 * 16);
-            } else {
-                pre[i] = make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-    };
-    auto lstore = [&](unsigned char *dst) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int ch = tid + SCAN_THREADS * i;
-            const int r = ch / (RB / 16), c16 = ch % (RB / 16);
-            *(uint4 *)(dst + r * KROW + c16 * 16) = pre[i];
+        for (int i = 0; i < NLD; ++i) {
+            const int blk = i * (SCAN_THREADS / 64) + w;
+            const int q = blk * 64 + l;
+            const int r = q / NCK, pos = q % NCK;
+            const int c = pos ^ (r & SWZ);
+            const int64_t v = min((int64_t)kt * SCAN_KEYS + r, vmax - 1);
+            const int64_t key = p.koff + (int64_t)p.kstride * v;
+            __builtin_amdgcn_global_load_lds((const void *)(Kb + key * krow_bytes + c * 16),
+                                             (__attribute__((address_space(3))) void *)(smem + (kt & 1) * TILE + blk * 1024),
+                                             16, 0, 0);
         }
     };
 
-    // Order inside a step: matrix work on tile kt, then tile kt+1 (loaded
-    // during the previous step) into LDS, then the survivor stores, then the
-    // loads of tile kt+2. The wait for those loads (next step, after the
-    // matrix work) also covers the stores issued before them, which by then
-    // have had the whole matrix phase to complete.
-    if (ntiles_k > 0) {
-        gload(0);
-        lstore(buf0);
-        if (ntiles_k > 1) gload(1);
-    }
-    __syncthreads();
-
-    for (int kt = 0; kt < ntiles_k; ++kt) {
-        unsigned char *cur = (kt & 1) ? buf1 : buf0;
-        unsigned char *nxt = (kt & 1) ? buf0 : buf1;
-
-        f32x16_t acc[2][2];
-        for (int a = 0; a < 2; ++a)
-            for (int b = 0; b < 2; ++b) acc[a][b] = f32x16_t{};
+    typedef f32x16_t acc_t[2];
+    auto matrix = [&](int kt, acc_t &acc) {
+        const unsigned char *cur = smem + (kt & 1) * TILE;
+        acc[0] = f32x16_t{};
+        acc[1] = f32x16_t{};
+        const int r = l & 31;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const unsigned char *ap = cur + (kb * 32 + (l & 31)) * KROW;
-                if constexpr (std::is_same<T, float>::value) {
-                    const f32x4_t a = *(const f32x4_t *)(ap + (8 * ks + 4 * half) * 4);
-#pragma unroll
-                    for (int gb = 0; gb < 2; ++gb)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            acc[kb][gb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                a[v], bq[gb][ks][v], acc[kb][gb], 0, 0, 0);
-                } else {
-                    const bf16x8_t a = *(const bf16x8_t *)(ap + (16 * ks + 8 * half) * 2);
-#pragma unroll
-                    for (int gb = 0; gb < 2; ++gb)
-                        acc[kb][gb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            a, bq[gb][ks], acc[kb][gb], 0, 0, 0);
-                }
-            }
-        }
-
-        // a half past its capacity stops storing (its count stays above cap)
-#pragma unroll
-        for (int gb = 0; gb < 2; ++gb)
-            if (soff[gb] - soff0[gb] > ESZ * (uint32_t)p.cap_half) tau[gb] = never;
-        // keep the scores that reach the row's threshold; at most 32 per
-        // half and tile, so a count <= cap_half leaves room in the stride.
-        // Tiles below every row's prefix end skip the causal test.
-        const uint32_t tkey = (uint32_t)(kt * SCAN_KEYS) + lane_key;  // used when kstride == 1
-        auto filter = [&](auto causal) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            const unsigned char *ap = cur + r * RB + (((2 * ks + half) ^ (r & SWZ)) * 16);
+            if constexpr (std::is_same<T, float>::value) {
+                const f32x4_t a = *(const f32x4_t *)ap;
 #pragma unroll
                 for (int gb = 0; gb < 2; ++gb)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int vo = kb * 32 + 8 * (v >> 2) + (v & 3);  // + 4 * half
-                        const float s = acc[kb][gb][v];
-                        bool keep = s >= tau[gb];
-                        if constexpr (decltype(causal)::value)
-                            keep = keep && (kt * SCAN_KEYS + vo + 4 * half < vcount[gb]);
-                        if (keep) {
-                            if constexpr (STRIDED)
-                                *(uint32_t *)(sb + soff[gb]) = __float_as_uint(s);
-                            else
-                                *(uint2 *)(sb + soff[gb]) = make_uint2(__float_as_uint(s), tkey + (uint32_t)vo);
-                            soff[gb] += ESZ;
-                        }
+                    for (int v = 0; v < 4; ++v)
+                        acc[gb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[v], bq[gb][ks][v], acc[gb], 0, 0, 0);
+            } else {
+                const bf16x8_t a = *(const bf16x8_t *)ap;
+#pragma unroll
+                for (int gb = 0; gb < 2; ++gb)
+                    acc[gb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[gb][ks], acc[gb], 0, 0, 0);
+            }
+        }
+    };
+
+    // the FLUSH oldest staged survivors of stream gb leave as one chunk
+    // (entries fl .. fl+7 sit in ring slots fl % RING .. +7); at most
+    // cap_half + 16 are ever kept, inside the stream's stride
+    auto flush = [&](int gb) {
+        if (cnt[gb] - fl[gb] >= (uint32_t)FLUSH) {
+            const uint2 *src = ring + (fl[gb] % RING) * NSTREAM + gb * SCAN_THREADS + stream0;
+            uint2 e[FLUSH];
+#pragma unroll
+            for (int i = 0; i < FLUSH; ++i) e[i] = src[i * NSTREAM];
+            uint4 *dst = (uint4 *)(sb + soff0[gb] + fl[gb] * 8u);
+#pragma unroll
+            for (int i = 0; i < FLUSH / 2; ++i) dst[i] = make_uint4(e[2 * i].x, e[2 * i].y, e[2 * i + 1].x, e[2 * i + 1].y);
+            fl[gb] += FLUSH;
+        }
+    };
+
+    // keep the scores of tile kt that reach the row's threshold; at most 16
+    // per stream and tile. Tiles below every row's prefix end skip the causal
+    // test. A flush check after every 8 scores keeps the ring from filling.
+    auto filter = [&](int kt, const acc_t &acc) {
+#pragma unroll
+        for (int gb = 0; gb < 2; ++gb)
+            if (cnt[gb] > (uint32_t)p.cap_half) tau[gb] = never;
+        const uint32_t tkey = kstr * (uint32_t)(kt * SCAN_KEYS) + lane_key;
+        auto run = [&](auto causal) {
+#pragma unroll
+            for (int gb = 0; gb < 2; ++gb) {
+                uint2 *rs = ring + gb * SCAN_THREADS + stream0;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int vo = 8 * (v >> 2) + (v & 3);  // + 4 * half
+                    const float s = acc[gb][v];
+                    bool keep = s >= tau[gb];
+                    if constexpr (decltype(causal)::value)
+                        keep = keep && (kt * SCAN_KEYS + vo + 4 * half < vcount[gb]);
+                    if (keep) {
+                        rs[(cnt[gb] % RING) * NSTREAM] = make_uint2(__float_as_uint(s), tkey + kstr * (uint32_t)vo);
+                        cnt[gb] += 1u;
                     }
+                    if ((v & 7) == 7) flush(gb);
+                }
+            }
         };
-        if (kt + 1 < ntiles_k) lstore(nxt);
-        if ((int64_t)(kt + 1) * SCAN_KEYS <= vfull) filter(std::false_type{});
-        else filter(std::true_type{});
-        if (kt + 2 < ntiles_k) gload(kt + 2);
+        if ((int64_t)(kt + 1) * SCAN_KEYS <= vfull) run(std::false_type{});
+        else run(std::true_type{});
+    };
+
+    auto step = [&](int kt, const acc_t &prev, acc_t &cur) {
+        __builtin_amdgcn_s_waitcnt(0);  // tile kt (and older stores) complete
         __syncthreads();
+        if (kt > 0) filter(kt - 1, prev);
+        if (kt + 1 < ntiles_k) issue_tile(kt + 1);
+        matrix(kt, cur);
+    };
+    // every proxy fragment has arrived before the loop: the loop then waits
+    // on its own loads and stores only. Even tiles accumulate in accA, odd
+    // ones in accB (two steps per iteration keep the names static).
+    __builtin_amdgcn_s_waitcnt(0);
+    acc_t accA, accB;
+    if (ntiles_k > 0) issue_tile(0);
+    int kt = 0;
+    for (; kt + 2 <= ntiles_k; kt += 2) {
+        step(kt, accB, accA);
+        step(kt + 1, accA, accB);
+    }
+    if (kt < ntiles_k) {
+        step(kt, accB, accA);
+        filter(kt, accA);
+    } else if (ntiles_k > 0) {
+        filter(ntiles_k - 1, accB);
     }
 
+    // the rest of each ring (fewer than FLUSH entries) one by one
     for (int gb = 0; gb < 2; ++gb) {
+        const uint2 *rs = ring + gb * SCAN_THREADS + stream0;
+        for (uint32_t e = fl[gb]; e < cnt[gb]; ++e)
+            *(uint2 *)(sb + soff0[gb] + e * 8u) = rs[(e % RING) * NSTREAM];
         const int64_t j = j0 + 64 * w + 32 * gb + (l & 31);
-        if (j < p.G) p.cnt[((int64_t)hl * p.G + j) * 2 + half] = (int)((soff[gb] - soff0[gb]) / ESZ);
+        if (j < p.G) p.cnt[((int64_t)hl * p.G + j) * 2 + half] = (int)cnt[gb];
     }
 }
 
 // -------------------------------------------------------------------- tau
 
 struct TauParams {
-    const uint32_t *samp;   // sample scores' float bits
+    const uint2 *samp;      // samples: (float bits, key)
     const int *scnt;
     int samp_half, samp_stride;
     float *tau;
@@ -374,14 +406,14 @@ __global__ void __launch_bounds__(SEL_THREADS) k_tau(TauParams p) {
     Selector<4, SEL_LOG2NB> sel{G, hist, vars};
     const int elim = (int)((ns + SEL_THREADS - 1) / SEL_THREADS);
     uint32_t key[TAU_E];
-    const uint32_t *b0 = p.samp + (2 * r) * (int64_t)p.samp_stride;
-    const uint32_t *b1 = p.samp + (2 * r + 1) * (int64_t)p.samp_stride;
+    const uint2 *b0 = p.samp + (2 * r) * (int64_t)p.samp_stride;
+    const uint2 *b1 = p.samp + (2 * r + 1) * (int64_t)p.samp_stride;
     bool has[TAU_E];
 #pragma unroll
     for (int e = 0; e < TAU_E; ++e) {
         const uint32_t gi = e * SEL_THREADS + threadIdx.x;
         has[e] = e < elim && gi < ns;
-        key[e] = has[e] ? (gi < (uint32_t)c0 ? b0[gi] : b1[gi - c0]) : 0u;
+        key[e] = has[e] ? (gi < (uint32_t)c0 ? b0[gi].x : b1[gi - c0].x) : 0u;
     }
 #pragma unroll
     for (int e = 0; e < TAU_E; ++e) key[e] = has[e] ? score_key(__uint_as_float(key[e])) : 0u;
@@ -1334,7 +1366,7 @@ int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio,
     pl.b_cnt = align256(rows * 8);
     pl.b_scnt = align256(rows * 8);
     pl.b_surv = align256(rows * 2 * (size_t)(pl.cap_half + 32) * 8);
-    pl.b_samp = pl.n_max > pl.keep_all_n ? align256(rows * 2 * (size_t)(pl.samp_half + 32) * 4) : 0;
+    pl.b_samp = pl.n_max > pl.keep_all_n ? align256(rows * 2 * (size_t)(pl.samp_half + 32) * 8) : 0;
     pl.b_cand = pl.mode == PIVOT_REFINE ? align256(rows * (size_t)K * 4) : 0;
     pl.b_fbl = align256(rows * 4);
     pl.fixed = 256 + align256((size_t)FB_BLOCKS * (size_t)pl.n_max * 4);
@@ -1406,14 +1438,9 @@ int dispatch_refine(int D, const RefParams &rp, int nblocks, size_t lds, hipStre
 
 template <typename T, int D>
 int launch_scan(const ScanParams &sp, hipStream_t st) {
-    const size_t lds = 2 * SCAN_KEYS * ((size_t)D * sizeof(T) + 16);
-    if (!sp.scores_only) {  // main pass: every key (kstride 1), keys stored
-        HIP_TRY(set_lds((const void *)k_scan<T, D, false>, lds));
-        hipLaunchKernelGGL((k_scan<T, D, false>), dim3(sp.Hc * sp.n_tiles), dim3(SCAN_THREADS), lds, st, sp);
-    } else {
-        HIP_TRY(set_lds((const void *)k_scan<T, D, true>, lds));
-        hipLaunchKernelGGL((k_scan<T, D, true>), dim3(sp.Hc * sp.n_tiles), dim3(SCAN_THREADS), lds, st, sp);
-    }
+    const size_t lds = 2 * SCAN_KEYS * (size_t)D * sizeof(T) + (size_t)RING * 2 * SCAN_THREADS * 8;
+    HIP_TRY(set_lds((const void *)k_scan<T, D>, lds));
+    hipLaunchKernelGGL((k_scan<T, D>), dim3(sp.Hc * sp.n_tiles), dim3(SCAN_THREADS), lds, st, sp);
     HIP_TRY(hipGetLastError());
     return PIVOT_OK;
 }
@@ -1448,7 +1475,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
         int *cnt = (int *)take(pl.b_cnt);
         int *scnt = (int *)take(pl.b_scnt);
         uint32_t *surv = (uint32_t *)take(pl.b_surv);
-        uint32_t *samp = (uint32_t *)take(pl.b_samp);
+        uint2 *samp = (uint2 *)take(pl.b_samp);
         uint32_t *cand = (uint32_t *)take(pl.b_cand);
         uint32_t *fbl = (uint32_t *)take(pl.b_fbl);
 
@@ -1485,8 +1512,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             ss.kstride = pl.kstride;
             ss.koff = pl.kstride - 1;
             ss.tau = nullptr;
-            ss.out = samp;
-            ss.scores_only = 1;
+            ss.out = (uint32_t *)samp;
             ss.cap_half = pl.samp_half;
             ss.stride = pl.samp_half + 32;
             ss.cnt = scnt;
@@ -1509,7 +1535,6 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             sm.koff = 0;
             sm.tau = tau;
             sm.out = surv;
-            sm.scores_only = 0;
             sm.cap_half = pl.cap_half;
             sm.stride = pl.cap_half + 32;
             sm.cnt = cnt;
