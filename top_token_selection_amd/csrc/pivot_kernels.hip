@@ -320,10 +320,10 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
                     bool keep = s >= tau[gb];
                     if constexpr (decltype(causal)::value)
                         keep = keep && (kt * SCAN_KEYS + vo + 4 * half < vcount[gb]);
-                    if (keep) {
-                        rs[(cnt[gb] % RING) * NSTREAM] = make_uint2(__float_as_uint(s), tkey + kstr * (uint32_t)vo);
-                        cnt[gb] += 1u;
-                    }
+                    // written whether kept or not (slot cnt % RING is free:
+                    // fewer than RING entries wait), counted only if kept
+                    rs[(cnt[gb] % RING) * NSTREAM] = make_uint2(__float_as_uint(s), tkey + kstr * (uint32_t)vo);
+                    cnt[gb] += keep ? 1u : 0u;
                     if ((v & 7) == 7) flush(gb);
                 }
             }
