@@ -60,30 +60,44 @@ __device__ __forceinline__ int bit_width(uint32_t x) { return x ? 32 - __clz((in
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
-__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+// Cross-lane steps use DPP (data-parallel primitives of the VALU): row_shr:n
+// shifts within each row of 16 lanes, row_bcast:15 / row_bcast:31 carry lane
+// 15 of a row into the next row / lane 31 into rows 2 and 3. A lane with no
+// source (or in a row left out by the row mask) gets `old`.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
+constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+
+// op over lanes 0..l for every lane l (inclusive scan); lane 63 ends with
+// the op over the whole wavefront. `id` is op's identity.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan_op(uint32_t v, uint32_t id, Op op) {
+    v = op(v, dpp_u32<DPP_ROW_SHR1>(id, v));
+    v = op(v, dpp_u32<DPP_ROW_SHR2>(id, v));
+    v = op(v, dpp_u32<DPP_ROW_SHR4>(id, v));
+    v = op(v, dpp_u32<DPP_ROW_SHR8>(id, v));
+    v = op(v, dpp_u32<DPP_ROW_BCAST15, 0xA>(id, v));
+    v = op(v, dpp_u32<DPP_ROW_BCAST31, 0xC>(id, v));
     return v;
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+    v = wave_scan_op(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return min(a, b); });
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-    return v;
+    v = wave_scan_op(v, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
-    return v;
+    v = wave_scan_op(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 // Inclusive prefix sum over the 64 lanes.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-    const int l = lane_id();
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t t = (uint32_t)__shfl_up((int)v, o, 64);
-        if (l >= o) v += t;
-    }
-    return v;
+    return wave_scan_op(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
 // LDS ordering point for a single wavefront working in its private area.
