@@ -42,6 +42,9 @@ using namespace pivot;
 
 namespace {
 
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+
 constexpr int SCAN_THREADS = 256;  // 4 wavefronts
 constexpr int SCAN_ROWS = 256;     // groups per scan block (64 per wave)
 constexpr int SCAN_KEYS = 32;      // keys per k-tile
@@ -718,52 +721,103 @@ struct DecScanParams {
     uint32_t *dense;  // row (b, h) at offs[b]*H + h*ctx_b
 };
 
-// Streams the key cache once: thread task = (token, head) full dot product
-// of the head's proxy with that key row. Block = (sequence, 512-token chunk).
+// Streams the key cache once. Block = (sequence, group of 4 heads,
+// DEC_TOKENS-token chunk), 4 wavefronts. A load instruction of a wavefront
+// reads the 4 heads' key rows of one token (contiguous in the cache): 16
+// lanes per row, lane j reading the j-th sixteenth of the row (its slice of
+// its head's proxy stays in registers); the 16 partial dot products of a row
+// are summed with DPP row shifts, lane 15 of the row ending with the score.
 template <typename T, int D>
 __global__ void __launch_bounds__(DEC_THREADS) k_decode_scan(DecScanParams p) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    float *pr = (float *)smem;  // H x D proxies of this sequence
-    const int b = (int)(blockIdx.x / p.max_chunks);
+    constexpr int RB = D * (int)sizeof(T);  // bytes per key row
+    constexpr int CH = RB / 16;             // bytes per lane per row (8, 16 or 32)
+    constexpr int NE = CH / (int)sizeof(T); // elements per lane per row
+    constexpr int U = 32;                   // tokens per wavefront in flight
+    typedef typename std::conditional<CH == 8, uint2, uint4>::type chunk_t;
+    constexpr int NCH = CH >= 16 ? CH / 16 : 1;  // chunk_t loads per row
+    const int ngrp = (p.H + 3) / 4;
+    const int64_t per_seq = (int64_t)ngrp * p.max_chunks;
+    const int b = (int)(blockIdx.x / per_seq);
+    const int hg = (int)((blockIdx.x % per_seq) / p.max_chunks);
     const int64_t chunk = blockIdx.x % p.max_chunks;
     const int64_t off = p.offs[b];
     const int64_t ctx = p.offs[b + 1] - off;
     const int64_t t0 = chunk * DEC_TOKENS;
     if (t0 >= ctx) return;
-    const T *P = (const T *)p.P;
-    for (int e = threadIdx.x; e < p.H * D; e += DEC_THREADS) {
-        const int h = e / D, d = e % D;
-        pr[e] = load_f32(P + ((int64_t)h * p.B + b) * D + d);
-    }
-    __syncthreads();
-    const int64_t ntok = min((int64_t)DEC_TOKENS, ctx - t0);
-    const int64_t ntask = ntok * p.H;
-    const T *kc = (const T *)p.kc;
-    for (int64_t task = threadIdx.x; task < ntask; task += DEC_THREADS) {
-        const int64_t tok = t0 + task / p.H;
-        const int h = (int)(task % p.H);
-        const T *kr = kc + ((off + tok) * p.H + h) * (int64_t)D;
-        const float *ph = pr + h * D;
-        float acc = 0.f;
-        constexpr int PER = 16 / (int)sizeof(T);
-#pragma unroll 4
-        for (int d0 = 0; d0 < D; d0 += PER) {
-            const uint4 raw = *(const uint4 *)(kr + d0);
-            if constexpr (std::is_same<T, float>::value) {
-                acc = fmaf(ph[d0 + 0], __uint_as_float(raw.x), acc);
-                acc = fmaf(ph[d0 + 1], __uint_as_float(raw.y), acc);
-                acc = fmaf(ph[d0 + 2], __uint_as_float(raw.z), acc);
-                acc = fmaf(ph[d0 + 3], __uint_as_float(raw.w), acc);
-            } else {
-                const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+    const int64_t t1 = min(t0 + (int64_t)DEC_TOKENS, ctx);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, j = l & 15, rr = l >> 4;
+    const int h = min(4 * hg + rr, p.H - 1);  // lanes past the last head repeat it
+    const bool live = 4 * hg + rr < p.H;
+
+    float pv[NE];
+    {
+        const T *P = (const T *)p.P + ((int64_t)h * p.B + b) * D + NE * j;
 #pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2) {
-                    acc = fmaf(ph[d0 + 2 * q2], __uint_as_float(wds[q2] << 16), acc);
-                    acc = fmaf(ph[d0 + 2 * q2 + 1], __uint_as_float(wds[q2] & 0xFFFF0000u), acc);
+        for (int e = 0; e < NE; ++e) pv[e] = load_f32(P + e);
+    }
+    const unsigned char *base = (const unsigned char *)((const T *)p.kc + (off * p.H + h) * (int64_t)D) + CH * j;
+    const int64_t tstride = (int64_t)p.H * RB;  // bytes between consecutive tokens
+    uint32_t *out = p.dense + off * p.H + (int64_t)h * ctx;
+
+    // wavefront w takes tokens tb + w + 4u (u < U) of each block step
+    for (int64_t tb = t0; tb < t1; tb += 4 * U) {
+        chunk_t raw[U][NCH];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = min(tb + w + 4 * u, t1 - 1);
+            const chunk_t *src = (const chunk_t *)(base + t * tstride);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                // streamed once: nontemporal, so the cache keeps the scores
+                // the selection reads next
+                if constexpr (sizeof(chunk_t) == 16) {
+                    const u32x4_t x = __builtin_nontemporal_load((const u32x4_t *)(src + c));
+                    raw[u][c] = make_uint4(x[0], x[1], x[2], x[3]);
+                } else {
+                    const u32x2_t x = __builtin_nontemporal_load((const u32x2_t *)(src + c));
+                    raw[u][c] = make_uint2(x[0], x[1]);
                 }
             }
         }
-        p.dense[off * p.H + (int64_t)h * ctx + tok] = score_key(acc);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float acc = 0.f;
+            if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    acc = fmaf(pv[4 * c + 0], __uint_as_float(raw[u][c].x), acc);
+                    acc = fmaf(pv[4 * c + 1], __uint_as_float(raw[u][c].y), acc);
+                    acc = fmaf(pv[4 * c + 2], __uint_as_float(raw[u][c].z), acc);
+                    acc = fmaf(pv[4 * c + 3], __uint_as_float(raw[u][c].w), acc);
+                }
+            } else if constexpr (CH == 8) {
+                const uint32_t wds[2] = {raw[u][0].x, raw[u][0].y};
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) {
+                    acc = fmaf(pv[2 * q2], __uint_as_float(wds[q2] << 16), acc);
+                    acc = fmaf(pv[2 * q2 + 1], __uint_as_float(wds[q2] & 0xFFFF0000u), acc);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    const uint32_t wds[4] = {raw[u][c].x, raw[u][c].y, raw[u][c].z, raw[u][c].w};
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; ++q2) {
+                        acc = fmaf(pv[8 * c + 2 * q2], __uint_as_float(wds[q2] << 16), acc);
+                        acc = fmaf(pv[8 * c + 2 * q2 + 1], __uint_as_float(wds[q2] & 0xFFFF0000u), acc);
+                    }
+                }
+            }
+            // sum over the 16 lanes of the row: lane 15 of the row gets it
+            uint32_t x = __float_as_uint(acc);
+            auto fadd = [](uint32_t a2, uint32_t b2) { return __float_as_uint(__uint_as_float(a2) + __uint_as_float(b2)); };
+            x = fadd(x, dpp_u32<DPP_ROW_SHR1>(0u, x));
+            x = fadd(x, dpp_u32<DPP_ROW_SHR2>(0u, x));
+            x = fadd(x, dpp_u32<DPP_ROW_SHR4>(0u, x));
+            x = fadd(x, dpp_u32<DPP_ROW_SHR8>(0u, x));
+            const int64_t t = tb + w + 4 * u;
+            if (j == 15 && live && t < t1) out[t] = score_key(__uint_as_float(x));
+        }
     }
 }
 
@@ -1669,9 +1723,8 @@ int make_dec_plan(DecPlan &dp, int B, const int64_t *ctx, int g, int H, int D, i
 
 template <typename T, int D>
 int launch_dec_scan(const DecScanParams &ds, int nblocks, int H, hipStream_t st) {
-    const size_t lds = (size_t)H * D * 4;
-    HIP_TRY(set_lds((const void *)k_decode_scan<T, D>, lds));
-    hipLaunchKernelGGL((k_decode_scan<T, D>), dim3(nblocks), dim3(DEC_THREADS), lds, st, ds);
+    (void)H;
+    hipLaunchKernelGGL((k_decode_scan<T, D>), dim3(nblocks), dim3(DEC_THREADS), 0, st, ds);
     HIP_TRY(hipGetLastError());
     return PIVOT_OK;
 }
@@ -1710,7 +1763,7 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
     }
     {
         DecScanParams ds{P, kc, offs, dp.B, dp.H, (dp.max_ctx + DEC_TOKENS - 1) / DEC_TOKENS, dense};
-        const int nblocks = (int)(dp.B * ds.max_chunks);
+        const int nblocks = (int)((int64_t)dp.B * ((dp.H + 3) / 4) * ds.max_chunks);
         StageTimer tm(ST_DSCAN, st);
         int rc = dp.D == 64 ? launch_dec_scan<T, 64>(ds, nblocks, dp.H, st)
                             : launch_dec_scan<T, 128>(ds, nblocks, dp.H, st);
