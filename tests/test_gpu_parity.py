@@ -94,6 +94,26 @@ def test_refine_index_only_bit_exact(pv, S, H, D, top_k, g, ratio, dtype):
     np.testing.assert_array_equal(parity.to_host(idx), oi)
 
 
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+def test_heavy_ties_at_the_boundary(pv, mode):
+    """0/1 queries and keys: scores take ~25 values over 4096 candidates, so
+    hundreds of keys tie at the selection boundary (the per-query bucket of
+    the boundary overflows its staging and the exact general path takes
+    over, index-only and with scores)."""
+    print(f"\n[heavy ties] {mode}", flush=True)
+    S, H, D, top_k, g = 4104, 1, 64, 2048, 8
+    rng = np.random.default_rng(77)
+    q = syn.to_bf16_bits(rng.integers(0, 2, (S, H, D)).astype(np.float32))
+    k = syn.to_bf16_bits(rng.integers(0, 2, (S, H, D)).astype(np.float32))
+    oi, os_ = oracle.prefill(q, k, top_k, g, 2.0, mode)
+    gi, gs = run_prefill(pv, q, k, top_k, g, 2.0, mode)
+    np.testing.assert_array_equal(gi, oi)
+    np.testing.assert_array_equal(gs, os_)
+    only = pv.index_prefill(dev_tensor(q), dev_tensor(k), top_k=top_k, g=g, mode=mode)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(parity.to_host(only), oi)
+
+
 @pytest.mark.parametrize("S,H,D,top_k,dtype", [(1024, 8, 64, 64, "f32"), (700, 3, 128, 32, "bf16")])
 def test_dense_bit_exact_integer_inputs(pv, S, H, D, top_k, dtype):
     print(f"\n[dense exact] S={S} H={H} D={D} k={top_k} {dtype}", flush=True)

@@ -1047,7 +1047,8 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
         //    0.9 * count * 2048 / nt (rounded down instead when that
         //    overshoots 2048 in all), at least 2^(sh1 - 20) so that a key's
         //    bits inside its fine bucket fit 20 bits, at most 2^sh1. Table
-        //    word = fine base | log2(n) << 12.
+        //    word = fine base | log2(n) << 12 (an empty bin at or above b1:
+        //    the running base | 1 << 17).
         const uint32_t lgmin = sh1 > 20 ? (uint32_t)(sh1 - 20) : 0u;
         const float scl = (float)(REF_NB * 9 / 10) / (float)nt;
         for (int round_down = 0; round_down < 2; ++round_down) {
@@ -1075,7 +1076,10 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
 #pragma unroll
             for (int i = CPL - 1; i >= 0; --i) {
                 const uint32_t lg = lgs[i];
-                mine[i] = lg == 0xFFu ? 0xFFFFFFFFu : (run | (lg << 12));
+                const uint32_t bin = NC - CPL * (l + 1) + i;
+                // empty bins at or above b1 take no bucket but keep the base
+                // running, so bases never increase with the bin
+                mine[i] = lg != 0xFFu ? (run | (lg << 12)) : (bin >= b1 ? (run | (1u << 17)) : 0xFFFFFFFFu);
                 if (lg != 0xFFu) run += 1u << lg;
             }
             if (l == 63) vars[2] = run;  // fine buckets in use
@@ -1099,18 +1103,26 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
                 return (k == 0u || bin < b1) ? 0xFFFFFFFFu : w;
             };
             const uint32_t trashf = (uint32_t)(REF_NB + 2 * l);
-            // -- 3. fine histogram, crossing, offsets
+            // -- 3. fine histogram, crossing, offsets. From here on each key
+            //    register holds its packed word (every slot, so empty ones
+            //    read as "not wanted" in all passes); unpack() gives the key
+            //    back to the general path.
 #pragma unroll
-            for (int e = 0; e < REF_E / 4; ++e)
+            for (int e = 0; e < REF_E / 4; ++e) {
                 if (e < e4) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const uint32_t w = packed(key[4 * e + v]);
+                        key[4 * e + v] = w;
                         const uint32_t f = w == 0xFFFFFFFFu ? trashf : (w >> 20);
                         atomicAdd(&h2[f >> 1], 1u << ((f & 1u) << 4));
                     }
-                    __builtin_amdgcn_sched_barrier(0);  // bound the loads in flight
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) key[4 * e + v] = 0xFFFFFFFFu;
                 }
+                __builtin_amdgcn_sched_barrier(0);  // bound the loads in flight
+            }
             wave_lds_sync();
             {
                 uint32_t *fw = h2 + (REF_NB / 128) * l;  // lane l: fine buckets 32 l .. 32 l + 31
@@ -1151,14 +1163,6 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
             constexpr uint32_t TAGS = 2u * (uint32_t)(NC + 64) - 64u;  // + 64 trash tags
             constexpr int NSL = (int)(TAGS / 64u);                      // staged slots per lane
             if (nsc <= cap && nsc <= TAGS && msel <= STG) {
-                // from here on each key register holds its packed word (every
-                // slot, so empty ones read as "not wanted" in all passes)
-#pragma unroll
-                for (int e = 0; e < REF_E / 4; ++e) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) key[4 * e + v] = e < e4 ? packed(key[4 * e + v]) : 0xFFFFFFFFu;
-                    __builtin_amdgcn_sched_barrier(0);
-                }
                 wave_lds_sync();
                 uint16_t *tag = (uint16_t *)h1;
                 // -- 4. scatter fine buckets 0 .. fstar as (key bits in the
@@ -1249,6 +1253,28 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
                 for (int c = l; c < p.top_k; c += 64) dst[c] = c < (int)msel ? (int32_t)row[c] : -1;
                 return;
             }
+            // the boundary bucket does not fit: the general path needs the
+            // keys back. A packed word's coarse bin is the lowest bin at or
+            // above b1 whose table base is <= its fine bucket (bases fall as
+            // bins rise); keys below b1 rank under the msel-th and become 0.
+            auto unpack = [&](uint32_t w) -> uint32_t {
+                if (w == 0xFFFFFFFFu) return 0u;
+                const uint32_t fb = w >> 20;
+                uint32_t lo = b1, hi = NC - 1;
+                while (lo < hi) {
+                    const uint32_t mid = (lo + hi) >> 1;
+                    if ((h1[mid] & 0xFFFu) <= fb) hi = mid;
+                    else lo = mid + 1;
+                }
+                const uint32_t t = h1[lo];
+                const uint32_t lg = (t >> 12) & 31u;
+                const uint32_t sub = ((uint32_t)sh1 - lg) & 31u;
+                const uint32_t top = (1u << lg) - 1u - (fb - (t & 0xFFFu));
+                const uint32_t low = (top << sub) | (w & ((1u << sub) - 1u));
+                return mn + (lo << sh1) + low;
+            };
+#pragma unroll
+            for (int i = 0; i < REF_E; ++i) key[i] = unpack(key[i]);
         }
         wave_lds_sync();
     }
