@@ -106,6 +106,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-reuse", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip timing the dense indexer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     ap.add_argument("--recall-rows", type=int, default=256)
@@ -175,6 +176,15 @@ def main():
         log("timing Reuse")
         reuse_ms, _, reuse_stages, _ = time_calls(reuse, args.steps, args.warmup, pv)
         log(f"Reuse {reuse_ms:.2f} ms/step")
+
+    # ---------------------------------------- dense indexer (comparison)
+    dense_ms = dense_stages = None
+    if not args.no_dense:
+        def dense():
+            pv.dense_index(q, k, top_k, workspace=ws, out=out)
+        log("timing the dense indexer")
+        dense_ms, _, dense_stages, _ = time_calls(dense, max(1, args.steps // 2), 1, pv)
+        log(f"dense {dense_ms:.2f} ms/step")
 
     # ------------------------------------------------------------ roofline
     sum_n, sum_nk = prefix_sums(S, g, K)
@@ -304,6 +314,11 @@ def main():
             "reuse_ms_per_step": reuse_ms,
             "reuse_queries_per_s": S * H / (reuse_ms / 1e3) if reuse_ms else None,
             "reuse_stage_ms": reuse_stages,
+            "dense_ms_per_step": dense_ms,
+            "dense_queries_per_s": S * H / (dense_ms / 1e3) if dense_ms else None,
+            "dense_stage_ms": dense_stages,
+            "indexer_speedup_vs_dense": ({"refine": dense_ms / ms, "reuse": dense_ms / reuse_ms if reuse_ms else None}
+                                         if dense_ms else None),
             "decode": decode,
             "recall": recall,
             "host": {"cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count(),
