@@ -958,19 +958,30 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     for (int e = 0; e < REF_E / 4; ++e) {
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (e < e4) v = *(const uint4 *)(my + (e * 64 + l) * 16);
-        const int b = (e * 64 + l) * 4;
-        key[4 * e + 0] = b + 0 < nc ? v.x : 0u;
-        key[4 * e + 1] = b + 1 < nc ? v.y : 0u;
-        key[4 * e + 2] = b + 2 < nc ? v.z : 0u;
-        key[4 * e + 3] = b + 3 < nc ? v.w : 0u;
+        // position 256 e + 4 l + v; the bound is taken against a uniform
+        // value so that no per-position register outlives the load
+        const int rem = nc - 256 * e;
+        key[4 * e + 0] = 4 * l + 0 < rem ? v.x : 0u;
+        key[4 * e + 1] = 4 * l + 1 < rem ? v.y : 0u;
+        key[4 * e + 2] = 4 * l + 2 < rem ? v.z : 0u;
+        key[4 * e + 3] = 4 * l + 3 < rem ? v.w : 0u;
     }
+    // one key of every 64th part of the list, for the coarse range below
+    const uint32_t smp = nc >= 64 ? ((const uint32_t *)my)[((uint32_t)l * (uint32_t)nc) >> 6] : 0u;
     wave_lds_sync();
     const uint32_t msel = (uint32_t)min(p.top_k, nc);
     const int64_t obase = ((qrow0 + q0 + w) * p.H + h) * (int64_t)p.top_k;
 
     // ---- fused bucket select + sort ------------------------------------
-    // 1. A coarse histogram (1024 bins over [min, max] of this query's keys)
-    //    finds the bin holding the msel-th best key.
+    // 1. The lower end of the coarse range is a sampled key that lies below
+    //    the msel-th best with high probability (the r-th largest of 64 keys
+    //    taken evenly from the list, r four standard deviations past the
+    //    rank the msel-th key is expected to have among them); when fewer
+    //    than msel keys reach it, the list minimum. Bins over [lower end,
+    //    max] then spread the keys that matter (score tails and keys below
+    //    zero would otherwise crowd them into a few bins, and the atomics of
+    //    a histogram pass would serialise on those addresses). A coarse
+    //    histogram (1024 bins) finds the bin holding the msel-th best key.
     // 2. Equi-depth refinement: every coarse bin at or above it gets a
     //    power-of-two number of fine buckets roughly proportional to its
     //    count (2048 fine buckets in all, numbered from the best down), so a
@@ -980,16 +991,18 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     //    the fine bucket holding the msel-th key and gives every fine bucket
     //    its output offset.
     // 4. Fine buckets up to that one are scattered as packed words (key bits
-    //    inside the bucket, position); each element then counts the entries
-    //    of its bucket ranking above it (score desc, index asc).
+    //    inside the bucket, position), tagged with their bucket.
+    // 5. Each lane takes a run of consecutive staged slots and ranks every
+    //    entry against its bucket companions (score desc, index asc).
     // Out-of-range keys use per-lane trash bins / slots: no branches, no
     // single hot address.
     {
         constexpr int NC = 1 << REF_LOG2C;            // coarse bins
+        constexpr int CPL = NC / 64;                  // coarse bins per lane
         uint32_t *h1 = (uint32_t *)my;                // coarse counts, then the table
         uint32_t *h2 = h1 + NC + 64;                  // fine counters, two per word
         uint32_t *vars = h2 + REF_NB / 2 + 64;
-        uint32_t *buf = (uint32_t *)(my + REF_HDR);   // ref_cap entries + 64 trash slots
+        uint32_t *buf = (uint32_t *)(my + REF_HDR);   // ref_cap staged entries
         const uint32_t cap = (uint32_t)p.ref_cap;
         uint32_t mx = 0u, mnm1 = 0xFFFFFFFFu;
 #pragma unroll
@@ -1004,45 +1017,68 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
             }
         mx = wave_max(mx);
         const uint32_t mn = wave_min(mnm1) + 1u;
-        const int bw1 = bit_width(mx - mn);
-        const int sh1 = bw1 > REF_LOG2C ? bw1 - REF_LOG2C : 0;
-        constexpr int CPL = NC / 64;  // coarse bins per lane
-        // -- 1. coarse histogram
-        for (int i = l; i < NC + 64 + REF_NB / 2 + 64; i += 64) h1[i] = 0u;
-        wave_lds_sync();
+        uint32_t klo = mn;
+        {
+            const float pf = (float)msel / (float)nc;
+            const int rs = (int)ceilf(64.f * pf + 4.f * sqrtf(64.f * pf * (1.f - pf))) + 2;
+            if (nc >= 64 && rs <= 64) {
+                uint32_t rk = 0;
 #pragma unroll
-        for (int e = 0; e < REF_E / 4; ++e)
-            if (e < e4) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const uint32_t k = key[4 * e + v];
-                    atomicAdd(&h1[k != 0u ? (k - mn) >> sh1 : (uint32_t)(NC + l)], 1u);
+                for (int m = 0; m < 64; ++m) {
+                    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)smp, m);
+                    rk += (o > smp || (o == smp && m < l)) ? 1u : 0u;
                 }
+                const unsigned long long bal = __ballot(rk == (uint32_t)(rs - 1));
+                klo = (uint32_t)__builtin_amdgcn_readlane((int)smp, (int)__builtin_ctzll(bal));
             }
-        wave_lds_sync();
+        }
         // lane l owns coarse bins [NC - CPL (l + 1), NC - CPL l), the top first
         uint32_t *mine = h1 + NC - CPL * (l + 1);
-        {
+        uint32_t cc[CPL];
+        int sh1 = 0;
+        uint32_t b1 = 0, nt = 0;
+        for (int att = 0; att < 2; ++att) {
+            const int bw1 = bit_width(mx - klo);
+            sh1 = bw1 > REF_LOG2C ? bw1 - REF_LOG2C : 0;
+            for (int i = l; i < (NC + 64 + REF_NB / 2 + 64) / 4; i += 64)
+                ((uint4 *)h1)[i] = make_uint4(0u, 0u, 0u, 0u);
+            if (l == 0) vars[0] = 0xFFFFFFFFu;
+            wave_lds_sync();
+#pragma unroll
+            for (int e = 0; e < REF_E / 4; ++e)
+                if (e < e4) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const uint32_t k = key[4 * e + v];
+                        atomicAdd(&h1[k >= klo ? (k - klo) >> sh1 : (uint32_t)(NC + l)], 1u);
+                    }
+                }
+            wave_lds_sync();
             uint32_t loc = 0;
 #pragma unroll
             for (int i = 0; i < CPL / 4; ++i) {
                 const uint4 c4 = *(const uint4 *)(mine + 4 * i);
+                cc[4 * i + 0] = c4.x;
+                cc[4 * i + 1] = c4.y;
+                cc[4 * i + 2] = c4.z;
+                cc[4 * i + 3] = c4.w;
                 loc += c4.x + c4.y + c4.z + c4.w;
             }
             uint32_t run = wave_incl_scan(loc) - loc;
 #pragma unroll
             for (int i = CPL - 1; i >= 0; --i) {
-                const uint32_t c = mine[i];
-                if (run < msel && msel <= run + c) {
+                if (run < msel && msel <= run + cc[i]) {
                     vars[0] = (uint32_t)(NC - CPL * (l + 1) + i);
-                    vars[1] = run + c;
+                    vars[1] = run + cc[i];
                 }
-                run += c;
+                run += cc[i];
             }
+            wave_lds_sync();
+            b1 = vars[0];
+            nt = vars[1];
+            if (b1 != 0xFFFFFFFFu) break;
+            klo = mn;  // the sample was not below the msel-th key
         }
-        wave_lds_sync();
-        const uint32_t b1 = vars[0];
-        const uint32_t nt = vars[1];  // keys in coarse bins >= b1
         // -- 2. fine buckets per coarse bin: n = the power of two nearest to
         //    0.9 * count * 2048 / nt (rounded down instead when that
         //    overshoots 2048 in all), at least 2^(sh1 - 20) so that a key's
@@ -1056,7 +1092,7 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const uint32_t bin = NC - CPL * (l + 1) + i;
-                const uint32_t c = h1[bin];
+                const uint32_t c = cc[i];
                 uint32_t lg = 0xFFu;  // no fine buckets
                 if (bin >= b1 && c != 0u) {
                     const uint32_t want = max(1u, (uint32_t)((float)c * scl));
@@ -1086,13 +1122,30 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
             break;
         }
         wave_lds_sync();
+        // a packed word's coarse bin is the lowest bin at or above b1 whose
+        // table base is <= its fine bucket (bases fall as bins rise)
+        auto unpack = [&](uint32_t w) -> uint32_t {
+            if (w == 0xFFFFFFFFu) return 0u;
+            const uint32_t fb = w >> 20;
+            uint32_t lo = b1, hi = NC - 1;
+            while (lo < hi) {
+                const uint32_t mid = (lo + hi) >> 1;
+                if ((h1[mid] & 0xFFFu) <= fb) hi = mid;
+                else lo = mid + 1;
+            }
+            const uint32_t t = h1[lo];
+            const uint32_t lg = (t >> 12) & 31u;
+            const uint32_t sub = ((uint32_t)sh1 - lg) & 31u;
+            const uint32_t top = (1u << lg) - 1u - (fb - (t & 0xFFFu));
+            const uint32_t low = (top << sub) | (w & ((1u << sub) - 1u));
+            return klo + (lo << sh1) + low;
+        };
         if (vars[2] <= (uint32_t)REF_NB && !p.out_score) {
             // packed word of a key: fine bucket << 20 | its bits inside the
             // fine bucket (0 = best bucket); 0xFFFFFFFF when not wanted
-            // (branch-free: the table is read for every key, so the reads of
-            // many keys overlap instead of waiting one by one)
+            // (below the range, below b1, or an empty slot)
             auto packed = [&](uint32_t k) -> uint32_t {
-                const uint32_t rel = k - mn;
+                const uint32_t rel = k - klo;
                 const uint32_t bin = rel >> sh1;
                 const uint32_t t = h1[min(bin, (uint32_t)(NC - 1))];
                 const uint32_t lg = (t >> 12) & 31u;
@@ -1100,9 +1153,8 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
                 const uint32_t low = rel & ((1u << sh1) - 1u);
                 const uint32_t w =
                     (((t & 0xFFFu) + ((1u << lg) - 1u - (low >> sub))) << 20) | (low & ((1u << sub) - 1u));
-                return (k == 0u || bin < b1) ? 0xFFFFFFFFu : w;
+                return (k < klo || bin < b1) ? 0xFFFFFFFFu : w;
             };
-            const uint32_t trashf = (uint32_t)(REF_NB + 2 * l);
             // -- 3. fine histogram, crossing, offsets. From here on each key
             //    register holds its packed word (every slot, so empty ones
             //    read as "not wanted" in all passes); unpack() gives the key
@@ -1114,7 +1166,7 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
                     for (int v = 0; v < 4; ++v) {
                         const uint32_t w = packed(key[4 * e + v]);
                         key[4 * e + v] = w;
-                        const uint32_t f = w == 0xFFFFFFFFu ? trashf : (w >> 20);
+                        const uint32_t f = w == 0xFFFFFFFFu ? (uint32_t)(REF_NB + 2 * l) : (w >> 20);
                         atomicAdd(&h2[f >> 1], 1u << ((f & 1u) << 4));
                     }
                 } else {
@@ -1161,14 +1213,16 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
             // known) then hold the finished row.
             constexpr uint32_t STG = (uint32_t)(NC + 64 + REF_NB / 2 + 64);
             constexpr uint32_t TAGS = 2u * (uint32_t)(NC + 64) - 64u;  // + 64 trash tags
-            constexpr int NSL = (int)(TAGS / 64u);                      // staged slots per lane
+            constexpr int NSL = 36;                                     // staged slots per lane
+            static_assert(NSL % 4 == 0 && 64 * NSL >= (int)TAGS, "every staged slot has a lane");
             if (nsc <= cap && nsc <= TAGS && msel <= STG) {
                 wave_lds_sync();
                 uint16_t *tag = (uint16_t *)h1;
+                const uint32_t trashf = (uint32_t)(REF_NB + 2 * l);
                 // -- 4. scatter fine buckets 0 .. fstar as (key bits in the
                 //    bucket << 12 | position) with the bucket as a tag (slots
                 //    of 8 keys claimed before any is stored, so the atomics
-                //    overlap)
+                //    overlap; keys not taken go to per-lane trash slots)
 #pragma clang loop unroll(full)
                 for (int e0 = 0; e0 < REF_E / 4; e0 += 2)
                     if (e0 < e4) {
@@ -1185,94 +1239,122 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
                             const bool take = fb[i] < (uint32_t)REF_NB && e < e4;
                             const uint32_t slot = (got[i] >> ((fb[i] & 1u) << 4)) & 0xFFFFu;
                             buf[take ? slot : cap + l] =
-                                ((key[4 * e0 + i] & 0xFFFFFu) << 12) | (uint32_t)((e * 64 + l) * 4 + v);
+                                ((key[4 * e0 + i] & 0xFFFFFu) << 12) | (256u * (uint32_t)e + (uint32_t)(4 * l + v));
                             tag[take ? slot : TAGS + l] = (uint16_t)fb[i];
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 wave_lds_sync();
-                // -- 5. rank inside the bucket, one staged entry per lane and
-                //    step: counter f now ends fine bucket f, which starts where
-                //    f-1 ends; the entry counts the entries of its bucket that
-                //    rank above it (the first eight in one go; longer buckets
-                //    and equal keys, by key index, in a counted loop). The
-                //    final (slot, position) pairs wait in the key registers.
-                auto fend = [&](uint32_t f) { return (h2[f >> 1] >> ((f & 1u) << 4)) & 0xFFFFu; };
-#pragma clang loop unroll(full)
-                for (int i = 0; i < NSL; ++i) {
-                    const uint32_t u = (uint32_t)(i * 64 + l);
-                    key[i] = 0xFFFFFFFFu;
-                    if ((uint32_t)(i * 64) < nsc) {
-                        const bool act = u < nsc;
-                        const uint32_t uc = act ? u : 0u;
-                        const uint32_t w = buf[uc];
-                        const uint32_t f = tag[uc];
-                        const uint32_t pos = w & 4095u;
-                        const uint32_t lo = w & ~4095u;
-                        const uint32_t hi = lo | 4095u;
-                        const uint32_t end = fend(f);
-                        const uint32_t beg = f == 0u ? 0u : fend(min(f - 1u, (uint32_t)REF_NB - 1u));
-                        const uint32_t cnt = end - beg;
-                        // slots past the bucket are read (64 trash slots follow
-                        // the buffer) and masked to 0
-                        const uint32_t *bp = buf + beg;
-                        uint32_t above = 0, same = 0;
+                // -- 5. rank inside the bucket. Slots run in bucket order, so
+                //    ordering every bucket puts the row in place. Lane l
+                //    holds the staged slots [NSL l, NSL (l + 1)) and X more
+                //    on either side as 64-bit words (bucket + 1) << 52 |
+                //    (inverted key bits in the bucket) << 32 | key index and
+                //    runs odd-even transposition rounds until none swaps:
+                //    the words of a bucket then stand in final order (score
+                //    desc, index asc), and every bucket that touches the
+                //    lane's own slots is whole in its window unless it
+                //    reaches past an edge of the window. In that rare case
+                //    every entry is ranked by a counted loop over its bucket
+                //    instead and stored straight to the output row.
+                constexpr int X = 8;
+                constexpr int NW = NSL + 2 * X;
+                const uint32_t s0 = (uint32_t)(NSL * l);
+                const bool own = s0 < nsc;
+                // window entries below lim hold slots before nsc
+                const int lim = own ? (int)(nsc - s0) + X : 0;
+                uint64_t A[NW];
+                {
+                    const uint4 *bp = (const uint4 *)(buf + s0);
+                    const uint2 *tp = (const uint2 *)(tag + s0);
 #pragma unroll
-                        for (int t = 0; t < 8; ++t) {
-                            const uint32_t raw = bp[t];
-                            const uint32_t en = (uint32_t)t < cnt ? raw : 0u;
-                            above += en > hi;
-                            same += en >= lo;
+                    for (int i = -X / 4; i < NSL / 4 + X / 4; ++i) {
+                        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+                        uint2 y = make_uint2(0u, 0u);
+                        if (own && (i >= 0 || l > 0)) {
+                            x = bp[i];
+                            y = tp[i];
                         }
-                        same -= above;
-                        // masked slots (0) count as "same" when lo == 0
-                        if (lo == 0u) same -= 8u - min(cnt, 8u);
-                        uint32_t rank = above;
-                        if (act && (cnt > 8u || same > 1u)) {
-                            rank = 0;
-                            const uint32_t myidx = cl[pos];
-                            for (uint32_t x = beg; x < end; ++x) {
-                                const uint32_t en = buf[x];
-                                if (en > hi) ++rank;
-                                else if (en >= lo && (en & 4095u) != pos) rank += cl[en & 4095u] < myidx;
+                        const int j = 4 * i + X;
+                        const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+                        const uint32_t tg[4] = {y.x & 0xFFFFu, y.x >> 16, y.y & 0xFFFFu, y.y >> 16};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            // window entry j + q is slot s0 - X + j + q; the list
+                            // read stays inside LDS whatever the word holds
+                            const bool ok = j + q < X ? l > 0 : j + q < lim;
+                            const uint32_t idx = cl[wd[q] & 4095u];
+                            const uint32_t kv = ((tg[q] + 1u) << 20) | (0xFFFFFu - (wd[q] >> 12));
+                            A[j + q] = ok ? (((uint64_t)kv << 32) | idx) : (j + q < X ? 0ull : ~0ull);
+                        }
+                    }
+                }
+                // a bucket reaching from an own slot past the window
+                const uint32_t tl = (uint32_t)(A[0] >> 52), tf = (uint32_t)(A[X] >> 52);
+                const uint32_t tb = (uint32_t)(A[X + NSL - 1] >> 52), tr = (uint32_t)(A[NW - 1] >> 52);
+                const bool edge = own && ((tl != 0u && tl == tf) || (tb <= (uint32_t)REF_NB && tb == tr));
+                if (__ballot(edge) == 0ull) {
+                    for (int it = 0; it <= NW / 2; ++it) {
+                        bool sw = false;
+#pragma unroll
+                        for (int par = 0; par < 2; ++par) {
+#pragma unroll
+                            for (int i = par; i + 1 < NW; i += 2) {
+                                const bool c = A[i] > A[i + 1];
+                                const uint64_t a = A[i];
+                                A[i] = c ? A[i + 1] : a;
+                                A[i + 1] = c ? a : A[i + 1];
+                                sw |= c;
                             }
                         }
-                        const uint32_t fin = beg + rank;
-                        if (act && fin < msel) key[i] = (fin << 12) | pos;
+                        if (__ballot(sw) == 0ull) break;
                     }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                wave_lds_sync();
-                // -- 6. finished row into LDS, then out with whole-line stores
-                uint32_t *row = h1;
+                    wave_lds_sync();
+                    // -- 6. finished row into LDS, then out with whole-line stores
+                    const int nown = own ? (int)min(msel - min(msel, s0), (uint32_t)NSL) : 0;
 #pragma unroll
-                for (int i = 0; i < NSL; ++i)
-                    if (key[i] != 0xFFFFFFFFu) row[key[i] >> 12] = cl[key[i] & 4095u];
-                wave_lds_sync();
+                    for (int t = 0; t < NSL; t += 4) {
+                        const uint4 o = make_uint4((uint32_t)A[X + t], (uint32_t)A[X + t + 1], (uint32_t)A[X + t + 2],
+                                                   (uint32_t)A[X + t + 3]);
+                        if (t + 4 <= nown) {
+                            *(uint4 *)(buf + s0 + t) = o;
+                        } else if (t < nown) {
+                            buf[s0 + t] = o.x;
+                            if (t + 1 < nown) buf[s0 + t + 1] = o.y;
+                            if (t + 2 < nown) buf[s0 + t + 2] = o.z;
+                        }
+                    }
+                    wave_lds_sync();
+                    int32_t *dst = p.out_idx + obase;
+                    for (int c = l; c < p.top_k; c += 64) dst[c] = c < (int)msel ? (int32_t)buf[c] : -1;
+                    return;
+                }
+                auto fend = [&](uint32_t f) { return (h2[f >> 1] >> ((f & 1u) << 4)) & 0xFFFFu; };
                 int32_t *dst = p.out_idx + obase;
-                for (int c = l; c < p.top_k; c += 64) dst[c] = c < (int)msel ? (int32_t)row[c] : -1;
+                for (uint32_t t = 0; t < (uint32_t)NSL; ++t) {
+                    const uint32_t u = s0 + t;
+                    if (u < nsc) {
+                        const uint32_t w = buf[u];
+                        const uint32_t f = tag[u];
+                        const uint32_t end = fend(f);
+                        const uint32_t beg = f == 0u ? 0u : fend(f - 1u);
+                        const uint32_t lw = w >> 12;
+                        const uint32_t myidx = cl[w & 4095u];
+                        uint32_t rank = 0;
+                        for (uint32_t x = beg; x < end; ++x) {
+                            const uint32_t en = buf[x];
+                            const uint32_t le = en >> 12;
+                            if (le > lw) ++rank;
+                            else if (le == lw && x != u) rank += cl[en & 4095u] < myidx ? 1u : 0u;
+                        }
+                        if (beg + rank < msel) dst[beg + rank] = (int32_t)myidx;
+                    }
+                }
+                for (int c = (int)msel + l; c < p.top_k; c += 64) dst[c] = -1;
                 return;
             }
             // the boundary bucket does not fit: the general path needs the
-            // keys back. A packed word's coarse bin is the lowest bin at or
-            // above b1 whose table base is <= its fine bucket (bases fall as
-            // bins rise); keys below b1 rank under the msel-th and become 0.
-            auto unpack = [&](uint32_t w) -> uint32_t {
-                if (w == 0xFFFFFFFFu) return 0u;
-                const uint32_t fb = w >> 20;
-                uint32_t lo = b1, hi = NC - 1;
-                while (lo < hi) {
-                    const uint32_t mid = (lo + hi) >> 1;
-                    if ((h1[mid] & 0xFFFu) <= fb) hi = mid;
-                    else lo = mid + 1;
-                }
-                const uint32_t t = h1[lo];
-                const uint32_t lg = (t >> 12) & 31u;
-                const uint32_t sub = ((uint32_t)sh1 - lg) & 31u;
-                const uint32_t top = (1u << lg) - 1u - (fb - (t & 0xFFFu));
-                const uint32_t low = (top << sub) | (w & ((1u << sub) - 1u));
-                return mn + (lo << sh1) + low;
-            };
+            // keys back; keys below b1 rank under the msel-th and become 0.
 #pragma unroll
             for (int i = 0; i < REF_E; ++i) key[i] = unpack(key[i]);
         }
@@ -1293,7 +1375,7 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
         for (int e = 0; e < REF_E / 4; ++e)
             if (e < e4) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) f(key[4 * e + v], (uint32_t)((e * 64 + l) * 4 + v));
+                for (int v = 0; v < 4; ++v) f(key[4 * e + v], 256u * (uint32_t)e + (uint32_t)(4 * l + v));
             }
     };
     auto idx_of = [&](uint32_t pos) { return cl[pos]; };
@@ -1305,7 +1387,7 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const uint32_t k = key[4 * e + v];
-                    const uint32_t pos = (e * 64 + l) * 4 + v;
+                    const uint32_t pos = 256u * (uint32_t)e + (uint32_t)(4 * l + v);
                     bool take = k > rule.T;
                     if (k == rule.T) take = (~cl[pos]) >= rule.I;
                     if (k != 0u && take) f(k, pos);
