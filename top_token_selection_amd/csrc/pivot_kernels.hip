@@ -905,16 +905,16 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
         frag_t a[4][NKS];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+            // a list entry is always a key of the prefix; past the list the
+            // slot holds stale LDS words: the clamp keeps every gather inside
+            // the tensor, and scores past nc are never read
             const int pidx = (b0 + u) * 16 + qcol;
-            const bool pv = pidx < nc;
-            // a candidate list entry is always a key of the prefix; the clamp
-            // keeps the gather inside the tensor whatever the list holds
-            const uint32_t c = pv ? min(cl[pidx], (uint32_t)(n - 1)) : 0u;
+            const uint32_t c = min(cl[pidx], (uint32_t)(n - 1));
             const T *kr = Kx + ((kbase + c) * p.H + h) * (int64_t)D;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const int dofs = F32 ? 16 * ks + 4 * lq : 32 * ks + 8 * lq;
-                a[u][ks] = pv ? *(const frag_t *)(kr + dofs) : frag_t{};
+                a[u][ks] = *(const frag_t *)(kr + dofs);
             }
         }
 #pragma unroll
@@ -931,17 +931,12 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
                 }
             }
             // lane holds query column qcol, candidates (b0+u)*16 + 4*lq + v
+            // (a region has room for 64 scores past the last block)
             const int pp = (b0 + u) * 16 + 4 * lq;
-            if (qcol < nq && pp < nc) {
+            if (qcol < nq) {
                 uint32_t *dst = (uint32_t *)(regs + qcol * p.reg_bytes) + pp;
-                if (pp + 3 < nc) {
-                    *(uint4 *)dst = make_uint4(score_key(acc[0]), score_key(acc[1]), score_key(acc[2]),
-                                               score_key(acc[3]));
-                } else {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        if (pp + v < nc) dst[v] = score_key(acc[v]);
-                }
+                *(uint4 *)dst = make_uint4(score_key(acc[0]), score_key(acc[1]), score_key(acc[2]),
+                                           score_key(acc[3]));
             }
         }
     }
@@ -1566,7 +1561,8 @@ constexpr size_t LDS_MAX = 163840;
 RefLayout refine_layout(int64_t K, int top_k, int g) {
     RefLayout L{};
     const size_t clb = ((size_t)K * 4 + 15) & ~(size_t)15;
-    const size_t r_scores = (size_t)((K + 255) / 256) * 1024;
+    // scores of the whole list and 64 past its last 16-candidate block
+    const size_t r_scores = (size_t)((K + 255) / 256) * 1024 + 256;
     const size_t r_general = ((size_t)(1 << REF_LOG2NB) + 8 + 16) * 4 + (size_t)top_k * 6;
     const size_t r_fused = (size_t)REF_HDR + 4 * ((size_t)top_k + 64 + 64);
     const size_t r_full = (size_t)REF_HDR + 4 * ((size_t)REF_FIX * 64 + 64);
@@ -1578,6 +1574,11 @@ RefLayout refine_layout(int64_t K, int top_k, int g) {
     size_t r = std::min(spare, r_full);
     r = std::max(r, need);
     r = (r + 15) & ~(size_t)15;
+    // regions 64 bytes past a multiple of 256 apart: the 16-byte score
+    // stores of the query columns then fall in distinct LDS banks
+    size_t r2 = (r & ~(size_t)255) + 64;
+    if (r2 > r) r2 -= 256;
+    if (r2 >= std::max(need, r_fused)) r = r2;
     L.reg_bytes = (int)r;
     // entries of the staging buffer, less the 64 trash slots at its end
     L.cap = r > (size_t)REF_HDR + 256 ? (int)std::min<size_t>((r - REF_HDR) / 4 - 64, (size_t)REF_FIX * 64) : 0;
