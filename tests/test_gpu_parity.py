@@ -79,19 +79,40 @@ def test_prefill_bit_exact_integer_inputs(pv, mode, S, H, D, top_k, g, ratio, dt
         np.testing.assert_allclose(gs, os_, rtol=4 * 2.0 ** -23, atol=0)
 
 
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
 @pytest.mark.parametrize("S,H,D,top_k,g,ratio,dtype", EXACT_CASES)
-def test_refine_index_only_bit_exact(pv, S, H, D, top_k, g, ratio, dtype):
-    """Indices without scores take the per-query bucket sort; they must equal
-    the oracle's rows exactly as well."""
-    print(f"\n[refine index-only] S={S} H={H} D={D} k={top_k} g={g} r={ratio} {dtype}", flush=True)
+def test_index_only_bit_exact(pv, mode, S, H, D, top_k, g, ratio, dtype):
+    """Indices without scores take the wavefront bucket sorts (Refine: per
+    query; Reuse: per group, one wavefront per row of survivors); they must
+    equal the oracle's rows exactly as well."""
+    print(f"\n[{mode} index-only] S={S} H={H} D={D} k={top_k} g={g} r={ratio} {dtype}", flush=True)
     a = 8 if dtype == "f32" else 4
     q = syn.integers((S, H, D), 7000 + S + g, a, dtype)
     k = syn.integers((S, H, D), 8000 + S + g, a, dtype)
     idx = pv.index_prefill(dev_tensor(q), dev_tensor(k), top_k=top_k, g=g, candidate_ratio=ratio,
-                           mode="refine")
+                           mode=mode)
     torch.cuda.synchronize()
-    oi, _ = oracle.prefill(q, k, top_k, g, ratio, "refine")
+    oi, _ = oracle.prefill(q, k, top_k, g, ratio, mode)
     np.testing.assert_array_equal(parity.to_host(idx), oi)
+
+
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+def test_index_only_gaussian_large_top_k(pv, mode):
+    """Gaussian inputs with top_k = 2048 (the largest top_k the wavefront
+    sorts take) and with top_k = 2500 (past it: the general selectors; K =
+    4000 for Refine); index-only rows equal the rows of the scored launch
+    (general selectors) exactly."""
+    S, H, D, g = 9000, 2, 128, 8
+    q = syn.gaussian((S, H, D), 7301, "bf16")
+    k = syn.gaussian((S, H, D), 7302, "bf16")
+    for top_k, ratio in ((2048, 2.0), (2500, 1.6)):
+        print(f"\n[{mode} index-only gaussian] S={S} H={H} k={top_k} r={ratio}", flush=True)
+        qd, kd = dev_tensor(q), dev_tensor(k)
+        a = pv.index_prefill(qd, kd, top_k=top_k, g=g, candidate_ratio=ratio, mode=mode)
+        b, _ = pv.index_prefill(qd, kd, top_k=top_k, g=g, candidate_ratio=ratio, mode=mode,
+                                return_scores=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(parity.to_host(a), parity.to_host(b))
 
 
 @pytest.mark.parametrize("mode", ["refine", "reuse"])
@@ -121,10 +142,12 @@ def test_dense_bit_exact_integer_inputs(pv, S, H, D, top_k, dtype):
     q = syn.integers((S, H, D), 7100 + S, a, dtype)
     k = syn.integers((S, H, D), 8100 + S, a, dtype)
     idx, sc = pv.dense_index(dev_tensor(q), dev_tensor(k), top_k=top_k, return_scores=True)
+    only = pv.dense_index(dev_tensor(q), dev_tensor(k), top_k=top_k)
     torch.cuda.synchronize()
     oi, os_ = oracle.dense(q, k, top_k)
     np.testing.assert_array_equal(parity.to_host(idx), oi)
     np.testing.assert_array_equal(parity.to_host(sc), os_)
+    np.testing.assert_array_equal(parity.to_host(only), oi)
 
 
 @pytest.mark.parametrize("mode", ["refine", "reuse"])

@@ -56,32 +56,35 @@ def test_int_workload_sampled_rows_bit_exact(pv, mode):
     np.testing.assert_array_equal(gs[ri, rh], os_)
 
 
-def test_int_workload_refine_index_only_bit_exact(pv):
-    """Index-only rows (per-query bucket sort) on the integer workload."""
-    print("\n[int workload] S=16384 H=16 refine index-only", flush=True)
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+def test_int_workload_index_only_bit_exact(pv, mode):
+    """Index-only rows (wavefront bucket sorts) on the integer workload."""
+    print(f"\n[int workload] S=16384 H=16 {mode} index-only", flush=True)
     cfg = syn.int_prefill()
     q, k, top_k, g = cfg["q"], cfg["k"], cfg["top_k"], cfg["g"]
     S, H, D = q.shape
-    idx = pv.index_prefill(to_dev(q), to_dev(k), top_k=top_k, g=g, mode="refine")
+    idx = pv.index_prefill(to_dev(q), to_dev(k), top_k=top_k, g=g, mode=mode)
     torch.cuda.synchronize()
     gi = parity.to_host(idx)
     rng = np.random.default_rng(4)
     ri = np.concatenate([rng.integers(0, S, 120), [0, 1, 7, 8, 9, 1023, 1024, 1025, S - 1]])
     rh = rng.integers(0, H, len(ri)).astype(np.int32)
-    oi, _ = oracle.prefill_rows(q, k, ri, rh, top_k, g, 2.0, "refine")
+    oi, _ = oracle.prefill_rows(q, k, ri, rh, top_k, g, 2.0, mode)
     np.testing.assert_array_equal(gi[ri, rh], oi)
 
 
 @pytest.mark.parametrize("long", [False, True])
-def test_long_workload_refine_index_only_equals_scored(pv, long):
-    """At full size, the index-only launch (the bench's) returns exactly the
-    indices of the launch that also returns scores, in every row."""
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+def test_long_workload_index_only_equals_scored(pv, mode, long):
+    """At full size, the index-only launch (the bench's: wavefront bucket
+    sorts) returns exactly the indices of the launch that also returns scores
+    (general selectors), in every row."""
     S, H, g, seed = (131072, 32, 16, 1004) if long else (65536, 64, 8, 1003)
-    print(f"\n[long workload] S={S} H={H} g={g} refine index-only vs scored", flush=True)
+    print(f"\n[long workload] S={S} H={H} g={g} {mode} index-only vs scored", flush=True)
     cfg = syn.long_prefill_device(DEV, S=S, H=H, g=g, seed=seed)
     q, k, top_k = cfg["q"], cfg["k"], cfg["top_k"]
-    a = pv.index_prefill(q, k, top_k=top_k, g=g, mode="refine")
-    b, sc = pv.index_prefill(q, k, top_k=top_k, g=g, mode="refine", return_scores=True)
+    a = pv.index_prefill(q, k, top_k=top_k, g=g, mode=mode)
+    b, sc = pv.index_prefill(q, k, top_k=top_k, g=g, mode=mode, return_scores=True)
     del sc
     torch.cuda.synchronize()
     same = torch.eq(a, b).all(dim=2)
@@ -127,6 +130,21 @@ def test_long_workloads_sampled_rows_tolerant(pv, mode, long):
         if e:
             errs.append((i, h, e))
     assert not errs, errs[:5]
+
+
+def test_dense_index_only_equals_scored(pv):
+    """The dense indexer at S=32768, H=4 on the long-workload distribution:
+    index-only rows (one wavefront per query row) equal the scored launch's
+    (block selector) in every row."""
+    print("\n[dense] S=32768 H=4 index-only vs scored", flush=True)
+    cfg = syn.long_prefill_device(DEV, S=32768, H=4, g=8, seed=1006)
+    q, k, top_k = cfg["q"], cfg["k"], cfg["top_k"]
+    a = pv.dense_index(q, k, top_k=top_k)
+    b, sc = pv.dense_index(q, k, top_k=top_k, return_scores=True)
+    del sc
+    torch.cuda.synchronize()
+    bad = torch.nonzero(~torch.eq(a, b).all(dim=2))[:5].tolist()
+    assert not bad, bad
 
 
 @pytest.mark.parametrize("g", [2, 4])

@@ -66,6 +66,10 @@ constexpr int MAX_TOPK = 4096;
 constexpr int FB_BLOCKS = 256;
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_TOKENS = 512;    // tokens per decode-scan block
+constexpr int SW_E = 96;           // select (wave): positions per lane (6144 per row)
+constexpr int SW_WAVES = 4;        // select (wave): rows per block
+constexpr int SW_CAP = 2240;       // select (wave): staged entries per row
+constexpr int SW_REG = REF_HDR + 4 * (SW_CAP + 64);  // select (wave): LDS bytes per row
 
 // Hardware places block b on XCD b % 8; hand each XCD a contiguous range of
 // logical work so neighbouring work shares that XCD's L2.
@@ -481,6 +485,12 @@ struct SelParams {
     RowOut o;
     uint32_t *fb_list;
     uint32_t *fb_count;
+    // sorted rows: k_select_wave lists here the rows it leaves to k_select,
+    // which then walks the list (list != 0) instead of one row per block
+    uint32_t *big_list;
+    uint32_t *big_count;
+    int64_t rows;
+    int list;
 };
 
 // Copies a staged row (LDS, msel valid entries) into every member row of
@@ -503,8 +513,7 @@ __device__ __forceinline__ void write_member_rows(const RowOut &o, int hl, int64
 // row's best Ksel keys when the row is not queued) are held in registers and
 // the exact best min(Ksel, n) of them selected. Slots past the survivors
 // hold key 0 (below every score) and never rank.
-__global__ void __launch_bounds__(SEL_THREADS) k_select(SelParams p) {
-    extern __shared__ __align__(16) unsigned char smem[];
+__device__ __forceinline__ void select_row(const SelParams &p, const int64_t r, unsigned char *smem) {
     uint32_t *hist = (uint32_t *)smem;
     uint32_t *vars = hist + (1 << SEL_LOG2NB);
     uint32_t *red = vars + 8;
@@ -512,7 +521,6 @@ __global__ void __launch_bounds__(SEL_THREADS) k_select(SelParams p) {
     uint32_t *bufk = ctr + 4;
     uint32_t *bufp = bufk + MAX_TOPK;
 
-    const int64_t r = blockIdx.x;
     const int64_t j = r % p.G;
     const int hl = (int)(r / p.G);
     const int64_t n = prefix_len(j, p.g);
@@ -582,6 +590,19 @@ __global__ void __launch_bounds__(SEL_THREADS) k_select(SelParams p) {
             __syncthreads();
             write_member_rows(p.o, hl, j, bufk, msel, true);
         }
+    }
+}
+
+__global__ void __launch_bounds__(SEL_THREADS) k_select(SelParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    if (!p.list) {
+        select_row(p, blockIdx.x, smem);
+        return;
+    }
+    const uint32_t nl = *p.big_count;
+    for (uint32_t it = blockIdx.x; it < nl; it += gridDim.x) {
+        select_row(p, (int64_t)p.big_list[it], smem);
+        __syncthreads();
     }
 }
 
@@ -848,6 +869,505 @@ struct RefParams {
 // the group's candidate list, scores them against the member queries on MFMA
 // (16x16: 16 candidates x 16 query columns, members in the first columns)
 // into LDS, then every wavefront selects and orders its own query's top_k.
+// ---- fused bucket select + sort of one wavefront's keys ----------------
+// Exact selection and ordering (score desc, key index asc) of the msel best
+// of nc keys held by a wavefront, position 256 e + 4 l + v in key[4 e + v]
+// of lane l (key 0 = empty slot, below every score). idx_of(pos) gives the
+// key index of a position (any pos < 2^POSB must be safe to pass); smp is
+// one key of the list per lane, taken evenly over it.
+// 1. The lower end of the coarse range is a sampled key that lies below
+//    the msel-th best with high probability (the r-th largest of 64 keys
+//    taken evenly from the list, r four standard deviations past the
+//    rank the msel-th key is expected to have among them); when fewer
+//    than msel keys reach it, the list minimum. Bins over [lower end,
+//    max] then spread the keys that matter (score tails and keys below
+//    zero would otherwise crowd them into a few bins, and the atomics of
+//    a histogram pass would serialise on those addresses). A coarse
+//    histogram (1024 bins) finds the bin holding the msel-th best key.
+// 2. Equi-depth refinement: every coarse bin at or above it gets a
+//    power-of-two number of fine buckets roughly proportional to its
+//    count (2048 fine buckets in all, numbered from the best down), so a
+//    fine bucket holds one or two keys on average whatever the shape of
+//    the score distribution.
+// 3. A fine histogram (16-bit counters, two per word); its scan finds
+//    the fine bucket holding the msel-th key and gives every fine bucket
+//    its output offset.
+// 4. Fine buckets up to that one are scattered as packed words (key bits
+//    inside the bucket, position), tagged with their bucket.
+// 5. Each lane takes a run of consecutive staged slots and ranks every
+//    entry against its bucket companions (score desc, index asc).
+// Out-of-range keys use per-lane trash bins / slots: no branches, no
+// single hot address.
+// `my` is the wavefront's LDS region (REF_HDR bytes of header, then cap + 64
+// staged words); positions take POSB bits of a staged word, key bits inside
+// a fine bucket the other LOWB.
+// Returns 1: the row (key indices in final order) is in row[0, msel) (LDS);
+// 2: every entry went out through put(rank, index) (ranks >= msel are not
+// passed); 0: the general path must run, key[] hold the keys again.
+template <int E, int POSB, class IDX, class PUT>
+__device__ __forceinline__ int fused_select(uint32_t (&key)[E], const int e4, const int nc, const uint32_t msel,
+                                            const uint32_t smp, unsigned char *my, const uint32_t cap, IDX idx_of,
+                                            PUT put, const uint32_t *&row) {
+    constexpr int LOWB = 32 - POSB;
+    constexpr uint32_t LM = (1u << LOWB) - 1u;
+    constexpr uint32_t PM = (1u << POSB) - 1u;
+    static_assert(64 * E <= (1 << POSB), "positions fit their bits");
+    const int l = lane_id();
+    constexpr int NC = 1 << REF_LOG2C;            // coarse bins
+    constexpr int CPL = NC / 64;                  // coarse bins per lane
+    uint32_t *h1 = (uint32_t *)my;                // coarse counts, then the table
+    uint32_t *h2 = h1 + NC + 64;                  // fine counters, two per word
+    uint32_t *vars = h2 + REF_NB / 2 + 64;
+    uint32_t *buf = (uint32_t *)(my + REF_HDR);   // ref_cap staged entries
+    uint32_t mx = 0u, mnm1 = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = 0; e < E / 4; ++e)
+        if (e < e4) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint32_t k = key[4 * e + v];
+                mx = max(mx, k);
+                mnm1 = min(mnm1, k - 1u);  // empty slots (0) wrap to the top
+            }
+        }
+    mx = wave_max(mx);
+    const uint32_t mn = wave_min(mnm1) + 1u;
+    uint32_t klo = mn;
+    {
+        const float pf = (float)msel / (float)nc;
+        const int rs = (int)ceilf(64.f * pf + 4.f * sqrtf(64.f * pf * (1.f - pf))) + 2;
+        if (nc >= 64 && rs <= 64) {
+            uint32_t rk = 0;
+#pragma unroll
+            for (int m = 0; m < 64; ++m) {
+                const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)smp, m);
+                rk += (o > smp || (o == smp && m < l)) ? 1u : 0u;
+            }
+            const unsigned long long bal = __ballot(rk == (uint32_t)(rs - 1));
+            klo = (uint32_t)__builtin_amdgcn_readlane((int)smp, (int)__builtin_ctzll(bal));
+        }
+    }
+    // lane l owns coarse bins [NC - CPL (l + 1), NC - CPL l), the top first
+    uint32_t *mine = h1 + NC - CPL * (l + 1);
+    uint32_t cc[CPL];
+    int sh1 = 0;
+    uint32_t b1 = 0, nt = 0;
+    for (int att = 0; att < 2; ++att) {
+        const int bw1 = bit_width(mx - klo);
+        sh1 = bw1 > REF_LOG2C ? bw1 - REF_LOG2C : 0;
+        for (int i = l; i < (NC + 64 + REF_NB / 2 + 64) / 4; i += 64)
+            ((uint4 *)h1)[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (l == 0) vars[0] = 0xFFFFFFFFu;
+        wave_lds_sync();
+#pragma unroll
+        for (int e = 0; e < E / 4; ++e)
+            if (e < e4) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint32_t k = key[4 * e + v];
+                    atomicAdd(&h1[k >= klo ? (k - klo) >> sh1 : (uint32_t)(NC + l)], 1u);
+                }
+            }
+        wave_lds_sync();
+        uint32_t loc = 0;
+#pragma unroll
+        for (int i = 0; i < CPL / 4; ++i) {
+            const uint4 c4 = *(const uint4 *)(mine + 4 * i);
+            cc[4 * i + 0] = c4.x;
+            cc[4 * i + 1] = c4.y;
+            cc[4 * i + 2] = c4.z;
+            cc[4 * i + 3] = c4.w;
+            loc += c4.x + c4.y + c4.z + c4.w;
+        }
+        uint32_t run = wave_incl_scan(loc) - loc;
+#pragma unroll
+        for (int i = CPL - 1; i >= 0; --i) {
+            if (run < msel && msel <= run + cc[i]) {
+                vars[0] = (uint32_t)(NC - CPL * (l + 1) + i);
+                vars[1] = run + cc[i];
+            }
+            run += cc[i];
+        }
+        wave_lds_sync();
+        b1 = vars[0];
+        nt = vars[1];
+        if (b1 != 0xFFFFFFFFu) break;
+        klo = mn;  // the sample was not below the msel-th key
+    }
+    // -- 2. fine buckets per coarse bin: n = the power of two nearest to
+    //    0.9 * count * 2048 / nt (rounded down instead when that
+    //    overshoots 2048 in all), at least 2^(sh1 - 20) so that a key's
+    //    bits inside its fine bucket fit LOWB bits, at most 2^sh1. Table
+    //    word = fine base | log2(n) << 12 (an empty bin at or above b1:
+    //    the running base | 1 << 17).
+    const uint32_t lgmin = sh1 > LOWB ? (uint32_t)(sh1 - LOWB) : 0u;
+    const float scl = (float)(REF_NB * 9 / 10) / (float)nt;
+    for (int round_down = 0; round_down < 2; ++round_down) {
+        uint32_t lgs[CPL], loc = 0;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const uint32_t bin = NC - CPL * (l + 1) + i;
+            const uint32_t c = cc[i];
+            uint32_t lg = 0xFFu;  // no fine buckets
+            if (bin >= b1 && c != 0u) {
+                const uint32_t want = max(1u, (uint32_t)((float)c * scl));
+                lg = (uint32_t)(31 - __clz((int)want));
+                // nearest: round up when want >= 1.5 * 2^lg
+                if (!round_down && 2u * want >= 3u << lg) ++lg;
+                lg = min(lg, (uint32_t)sh1);
+                lg = max(lg, lgmin);
+                loc += 1u << lg;
+            }
+            lgs[i] = lg;
+        }
+        const uint32_t total = wave_sum(loc);
+        if (total > (uint32_t)REF_NB && !round_down) continue;
+        uint32_t run = wave_incl_scan(loc) - loc;
+        wave_lds_sync();
+#pragma unroll
+        for (int i = CPL - 1; i >= 0; --i) {
+            const uint32_t lg = lgs[i];
+            const uint32_t bin = NC - CPL * (l + 1) + i;
+            // empty bins at or above b1 take no bucket but keep the base
+            // running, so bases never increase with the bin
+            mine[i] = lg != 0xFFu ? (run | (lg << 12)) : (bin >= b1 ? (run | (1u << 17)) : 0xFFFFFFFFu);
+            if (lg != 0xFFu) run += 1u << lg;
+        }
+        if (l == 63) vars[2] = run;  // fine buckets in use
+        break;
+    }
+    wave_lds_sync();
+    // a packed word's coarse bin is the lowest bin at or above b1 whose
+    // table base is <= its fine bucket (bases fall as bins rise)
+    auto unpack = [&](uint32_t w) -> uint32_t {
+        if (w == 0xFFFFFFFFu) return 0u;
+        const uint32_t fb = w >> 20;
+        uint32_t lo = b1, hi = NC - 1;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if ((h1[mid] & 0xFFFu) <= fb) hi = mid;
+            else lo = mid + 1;
+        }
+        const uint32_t t = h1[lo];
+        const uint32_t lg = (t >> 12) & 31u;
+        const uint32_t sub = ((uint32_t)sh1 - lg) & 31u;
+        const uint32_t top = (1u << lg) - 1u - (fb - (t & 0xFFFu));
+        const uint32_t low = (top << sub) | (w & ((1u << sub) - 1u));
+        return klo + (lo << sh1) + low;
+    };
+    if (vars[2] <= (uint32_t)REF_NB) {
+        // packed word of a key: fine bucket << 20 | its bits inside the
+        // fine bucket (0 = best bucket); 0xFFFFFFFF when not wanted
+        // (below the range, below b1, or an empty slot)
+        auto packed = [&](uint32_t k) -> uint32_t {
+            const uint32_t rel = k - klo;
+            const uint32_t bin = rel >> sh1;
+            const uint32_t t = h1[min(bin, (uint32_t)(NC - 1))];
+            const uint32_t lg = (t >> 12) & 31u;
+            const uint32_t sub = ((uint32_t)sh1 - lg) & 31u;
+            const uint32_t low = rel & ((1u << sh1) - 1u);
+            const uint32_t w =
+                (((t & 0xFFFu) + ((1u << lg) - 1u - (low >> sub))) << 20) | (low & ((1u << sub) - 1u));
+            return (k < klo || bin < b1) ? 0xFFFFFFFFu : w;
+        };
+        // -- 3. fine histogram, crossing, offsets. From here on each key
+        //    register holds its packed word (every slot, so empty ones
+        //    read as "not wanted" in all passes); unpack() gives the key
+        //    back to the general path.
+#pragma unroll
+        for (int e = 0; e < E / 4; ++e) {
+            if (e < e4) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint32_t w = packed(key[4 * e + v]);
+                    key[4 * e + v] = w;
+                    const uint32_t f = w == 0xFFFFFFFFu ? (uint32_t)(REF_NB + 2 * l) : (w >> 20);
+                    atomicAdd(&h2[f >> 1], 1u << ((f & 1u) << 4));
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) key[4 * e + v] = 0xFFFFFFFFu;
+            }
+            __builtin_amdgcn_sched_barrier(0);  // bound the loads in flight
+        }
+        wave_lds_sync();
+        {
+            uint32_t *fw = h2 + (REF_NB / 128) * l;  // lane l: fine buckets 32 l .. 32 l + 31
+            uint32_t loc = 0;
+#pragma unroll
+            for (int i = 0; i < REF_NB / 512; ++i) {
+                const uint4 c4 = *(const uint4 *)(fw + 4 * i);
+                loc += (c4.x & 0xFFFFu) + (c4.x >> 16) + (c4.y & 0xFFFFu) + (c4.y >> 16) +
+                       (c4.z & 0xFFFFu) + (c4.z >> 16) + (c4.w & 0xFFFFu) + (c4.w >> 16);
+            }
+            uint32_t run = wave_incl_scan(loc) - loc;
+#pragma unroll
+            for (int i = 0; i < REF_NB / 512; ++i) {
+                const uint4 c4 = *(const uint4 *)(fw + 4 * i);
+                const uint32_t w4[4] = {c4.x, c4.y, c4.z, c4.w};
+                uint32_t o4[4];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const uint32_t c = (w4[t >> 1] >> ((t & 1) << 4)) & 0xFFFFu;
+                    if (t & 1) o4[t >> 1] |= run << 16;
+                    else o4[t >> 1] = run;
+                    if (run < msel && msel <= run + c) {
+                        vars[3] = (uint32_t)(32 * l + 8 * i + t);
+                        vars[4] = run + c;
+                    }
+                    run += c;
+                }
+                *(uint4 *)(fw + 4 * i) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+            }
+        }
+        wave_lds_sync();
+        const uint32_t fstar = vars[3];
+        const uint32_t nsc = vars[4];
+        // h1 (the table, dead once every key is packed) then holds a 16-bit
+        // bucket tag per staged entry; h1..h2 (dead once every rank is
+        // known) then hold the finished row.
+        constexpr uint32_t STG = (uint32_t)(NC + 64 + REF_NB / 2 + 64);
+        constexpr uint32_t TAGS = 2u * (uint32_t)(NC + 64) - 64u;  // + 64 trash tags
+        constexpr int NSL = 36;                                     // staged slots per lane
+        static_assert(NSL % 4 == 0 && 64 * NSL >= (int)TAGS, "every staged slot has a lane");
+        if (nsc <= cap && nsc <= TAGS && msel <= STG) {
+            wave_lds_sync();
+            uint16_t *tag = (uint16_t *)h1;
+            const uint32_t trashf = (uint32_t)(REF_NB + 2 * l);
+            // -- 4. scatter fine buckets 0 .. fstar as (key bits in the
+            //    bucket << 12 | position) with the bucket as a tag (slots
+            //    of 8 keys claimed before any is stored, so the atomics
+            //    overlap; keys not taken go to per-lane trash slots)
+#pragma clang loop unroll(full)
+            for (int e0 = 0; e0 < E / 4; e0 += 2)
+                if (e0 < e4) {
+                    uint32_t got[8], fb[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t w = key[4 * e0 + i];
+                        fb[i] = (w == 0xFFFFFFFFu || (w >> 20) > fstar) ? trashf : (w >> 20);
+                        got[i] = atomicAdd(&h2[fb[i] >> 1], 1u << ((fb[i] & 1u) << 4));
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int e = e0 + i / 4, v = i % 4;
+                        const bool take = fb[i] < (uint32_t)REF_NB && e < e4;
+                        const uint32_t slot = (got[i] >> ((fb[i] & 1u) << 4)) & 0xFFFFu;
+                        buf[take ? slot : cap + l] =
+                            ((key[4 * e0 + i] & LM) << POSB) | (256u * (uint32_t)e + (uint32_t)(4 * l + v));
+                        tag[take ? slot : TAGS + l] = (uint16_t)fb[i];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            wave_lds_sync();
+            // -- 5. rank inside the bucket. Slots run in bucket order, so
+            //    ordering every bucket puts the row in place. Lane l
+            //    holds the staged slots [NSL l, NSL (l + 1)) and X more
+            //    on either side as 64-bit words (bucket + 1) << 52 |
+            //    (inverted key bits in the bucket) << 32 | key index and
+            //    runs odd-even transposition rounds until none swaps:
+            //    the words of a bucket then stand in final order (score
+            //    desc, index asc), and every bucket that touches the
+            //    lane's own slots is whole in its window unless it
+            //    reaches past an edge of the window. In that rare case
+            //    every entry is ranked by a counted loop over its bucket
+            //    instead and stored straight to the output row.
+            constexpr int X = 8;
+            constexpr int NW = NSL + 2 * X;
+            const uint32_t s0 = (uint32_t)(NSL * l);
+            const bool own = s0 < nsc;
+            // window entries below lim hold slots before nsc
+            const int lim = own ? (int)(nsc - s0) + X : 0;
+            uint64_t A[NW];
+            {
+                const uint4 *bp = (const uint4 *)(buf + s0);
+                const uint2 *tp = (const uint2 *)(tag + s0);
+#pragma unroll
+                for (int i = -X / 4; i < NSL / 4 + X / 4; ++i) {
+                    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+                    uint2 y = make_uint2(0u, 0u);
+                    if (own && (i >= 0 || l > 0)) {
+                        x = bp[i];
+                        y = tp[i];
+                    }
+                    const int j = 4 * i + X;
+                    const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+                    const uint32_t tg[4] = {y.x & 0xFFFFu, y.x >> 16, y.y & 0xFFFFu, y.y >> 16};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        // window entry j + q is slot s0 - X + j + q; the list
+                        // read stays inside LDS whatever the word holds
+                        const bool ok = j + q < X ? l > 0 : j + q < lim;
+                        const uint32_t idx = idx_of(wd[q] & PM);
+                        const uint32_t kv = ((tg[q] + 1u) << LOWB) | (LM - (wd[q] >> POSB));
+                        A[j + q] = ok ? (((uint64_t)kv << 32) | idx) : (j + q < X ? 0ull : ~0ull);
+                    }
+                }
+            }
+            // a bucket reaching from an own slot past the window
+            const uint32_t tl = (uint32_t)(A[0] >> (32 + LOWB)), tf = (uint32_t)(A[X] >> (32 + LOWB));
+            const uint32_t tb = (uint32_t)(A[X + NSL - 1] >> (32 + LOWB));
+            const uint32_t tr = (uint32_t)(A[NW - 1] >> (32 + LOWB));
+            const bool edge = own && ((tl != 0u && tl == tf) || (tb <= (uint32_t)REF_NB && tb == tr));
+            if (__ballot(edge) == 0ull) {
+                for (int it = 0; it <= NW / 2; ++it) {
+                    bool sw = false;
+#pragma unroll
+                    for (int par = 0; par < 2; ++par) {
+#pragma unroll
+                        for (int i = par; i + 1 < NW; i += 2) {
+                            const bool c = A[i] > A[i + 1];
+                            const uint64_t a = A[i];
+                            A[i] = c ? A[i + 1] : a;
+                            A[i + 1] = c ? a : A[i + 1];
+                            sw |= c;
+                        }
+                    }
+                    if (__ballot(sw) == 0ull) break;
+                }
+                wave_lds_sync();
+                // -- 6. finished row into LDS, then out with whole-line stores
+                const int nown = own ? (int)min(msel - min(msel, s0), (uint32_t)NSL) : 0;
+#pragma unroll
+                for (int t = 0; t < NSL; t += 4) {
+                    const uint4 o = make_uint4((uint32_t)A[X + t], (uint32_t)A[X + t + 1], (uint32_t)A[X + t + 2],
+                                               (uint32_t)A[X + t + 3]);
+                    if (t + 4 <= nown) {
+                        *(uint4 *)(buf + s0 + t) = o;
+                    } else if (t < nown) {
+                        buf[s0 + t] = o.x;
+                        if (t + 1 < nown) buf[s0 + t + 1] = o.y;
+                        if (t + 2 < nown) buf[s0 + t + 2] = o.z;
+                    }
+                }
+                wave_lds_sync();
+                row = buf;
+                return 1;
+            }
+            auto fend = [&](uint32_t f) { return (h2[f >> 1] >> ((f & 1u) << 4)) & 0xFFFFu; };
+            for (uint32_t t = 0; t < (uint32_t)NSL; ++t) {
+                const uint32_t u = s0 + t;
+                if (u < nsc) {
+                    const uint32_t w = buf[u];
+                    const uint32_t f = tag[u];
+                    const uint32_t end = fend(f);
+                    const uint32_t beg = f == 0u ? 0u : fend(f - 1u);
+                    const uint32_t lw = w >> POSB;
+                    const uint32_t myidx = idx_of(w & PM);
+                    uint32_t rank = 0;
+                    for (uint32_t x = beg; x < end; ++x) {
+                        const uint32_t en = buf[x];
+                        const uint32_t le = en >> POSB;
+                        if (le > lw) ++rank;
+                        else if (le == lw && x != u) rank += idx_of(en & PM) < myidx ? 1u : 0u;
+                    }
+                    if (beg + rank < msel) put(beg + rank, myidx);
+                }
+            }
+            return 2;
+        }
+        // the boundary bucket does not fit: the general path needs the
+        // keys back; keys below b1 rank under the msel-th and become 0.
+#pragma unroll
+        for (int i = 0; i < E; ++i) key[i] = unpack(key[i]);
+    }
+    wave_lds_sync();
+    return 0;
+}
+
+// ------------------------------------------------------- select (wave)
+
+// One wavefront per row of sorted output (Reuse, dense): the row's survivors
+// are loaded into registers as positions -- those of the first half, padded
+// to a multiple of four, then those of the second -- and go through the
+// fused bucket select; the best min(Ksel, n) in order go to every member row.
+// Rows with more than 64 * SW_E positions, rows the fused path declines and
+// calls that want scores are listed for k_select; overflowing rows are
+// queued for k_fallback, as there.
+__global__ void __launch_bounds__(64 * SW_WAVES) k_select_wave(SelParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int w = (int)(threadIdx.x >> 6), l = (int)(threadIdx.x & 63);
+    const int64_t r = (int64_t)blockIdx.x * SW_WAVES + w;
+    if (r >= p.rows) return;
+    const int64_t j = r % p.G;
+    const int hl = (int)(r / p.G);
+    const int64_t n = prefix_len(j, p.g);
+    const int c0 = p.cnt[2 * r], c1 = p.cnt[2 * r + 1];
+    const uint32_t msel = (uint32_t)min(p.Ksel, n);
+    if (c0 > p.cap_half || c1 > p.cap_half || (uint32_t)(c0 + c1) < msel) {
+        if (l == 0) {
+            const uint32_t slot = atomicAdd(p.fb_count, 1u);
+            p.fb_list[slot] = (uint32_t)r;
+        }
+        return;
+    }
+    auto to_list = [&]() {
+        if (l == 0) {
+            const uint32_t slot = atomicAdd(p.big_count, 1u);
+            p.big_list[slot] = (uint32_t)r;
+        }
+    };
+    const int ns = c0 + c1;
+    const int c0p = (c0 + 3) & ~3;
+    const int nv = c0p + c1;
+    if (nv > 64 * SW_E || p.o.out_score) {
+        to_list();
+        return;
+    }
+    const uint2 *b0 = p.surv + (2 * r) * (int64_t)p.stride;
+    const uint2 *b1 = b0 + p.stride;
+    const int e4 = (nv + 255) / 256;
+    uint32_t key[SW_E];
+#pragma unroll
+    for (int e = 0; e < SW_E / 4; ++e) {
+        // positions pos .. pos + 3 lie in one half: lim of them are survivors
+        const int pos = 256 * e + 4 * l;
+        const int lim = pos < c0p ? c0 - pos : nv - pos;
+        uint4 x0 = make_uint4(0u, 0u, 0u, 0u), x1 = x0;
+        if (e < e4 && lim > 0) {
+            const uint4 *src = (const uint4 *)(pos < c0p ? b0 + pos : b1 + (pos - c0p));
+            x0 = src[0];
+            x1 = src[1];
+        }
+        key[4 * e + 0] = 0 < lim ? score_key(__uint_as_float(x0.x)) : 0u;
+        key[4 * e + 1] = 1 < lim ? score_key(__uint_as_float(x0.z)) : 0u;
+        key[4 * e + 2] = 2 < lim ? score_key(__uint_as_float(x1.x)) : 0u;
+        key[4 * e + 3] = 3 < lim ? score_key(__uint_as_float(x1.z)) : 0u;
+    }
+    uint32_t smp = 0u;
+    if (ns >= 64) {
+        const int s = (int)(((uint32_t)l * (uint32_t)ns) >> 6);
+        smp = score_key(__uint_as_float(s < c0 ? b0[s].x : b1[s - c0].x));
+    }
+    // any position maps into this row's buffers (pads read stale words)
+    auto idx_of = [&](uint32_t pos) -> uint32_t {
+        const int q = min((int)pos, nv - 1);
+        return q < c0p ? b0[q].y : b1[q - c0p].y;
+    };
+    const int64_t i0 = j * p.g;
+    const int m = (int)min((int64_t)p.g, p.o.S - i0);
+    const int64_t rstride = (int64_t)p.o.H * p.o.top_k;
+    int32_t *dst0 = p.o.out_idx + (i0 * p.o.H + p.o.h0 + hl) * (int64_t)p.o.top_k;
+    const uint32_t *row = nullptr;
+    const int st = fused_select<SW_E, 13>(
+        key, e4, ns, msel, smp, smem + w * SW_REG, (uint32_t)SW_CAP, idx_of,
+        [&](uint32_t fin, uint32_t idx) {
+            for (int t = 0; t < m; ++t) dst0[t * rstride + fin] = (int32_t)idx;
+        },
+        row);
+    if (st == 0) {
+        to_list();
+        return;
+    }
+    for (int t = 0; t < m; ++t) {
+        int32_t *dst = dst0 + t * rstride;
+        if (st == 1)
+            for (int c = l; c < p.o.top_k; c += 64) dst[c] = c < (int)msel ? (int32_t)row[c] : -1;
+        else
+            for (int c = (int)msel + l; c < p.o.top_k; c += 64) dst[c] = -1;
+    }
+}
+
 template <typename T, int D>
 __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -967,393 +1487,17 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     const uint32_t msel = (uint32_t)min(p.top_k, nc);
     const int64_t obase = ((qrow0 + q0 + w) * p.H + h) * (int64_t)p.top_k;
 
-    // ---- fused bucket select + sort ------------------------------------
-    // 1. The lower end of the coarse range is a sampled key that lies below
-    //    the msel-th best with high probability (the r-th largest of 64 keys
-    //    taken evenly from the list, r four standard deviations past the
-    //    rank the msel-th key is expected to have among them); when fewer
-    //    than msel keys reach it, the list minimum. Bins over [lower end,
-    //    max] then spread the keys that matter (score tails and keys below
-    //    zero would otherwise crowd them into a few bins, and the atomics of
-    //    a histogram pass would serialise on those addresses). A coarse
-    //    histogram (1024 bins) finds the bin holding the msel-th best key.
-    // 2. Equi-depth refinement: every coarse bin at or above it gets a
-    //    power-of-two number of fine buckets roughly proportional to its
-    //    count (2048 fine buckets in all, numbered from the best down), so a
-    //    fine bucket holds one or two keys on average whatever the shape of
-    //    the score distribution.
-    // 3. A fine histogram (16-bit counters, two per word); its scan finds
-    //    the fine bucket holding the msel-th key and gives every fine bucket
-    //    its output offset.
-    // 4. Fine buckets up to that one are scattered as packed words (key bits
-    //    inside the bucket, position), tagged with their bucket.
-    // 5. Each lane takes a run of consecutive staged slots and ranks every
-    //    entry against its bucket companions (score desc, index asc).
-    // Out-of-range keys use per-lane trash bins / slots: no branches, no
-    // single hot address.
-    {
-        constexpr int NC = 1 << REF_LOG2C;            // coarse bins
-        constexpr int CPL = NC / 64;                  // coarse bins per lane
-        uint32_t *h1 = (uint32_t *)my;                // coarse counts, then the table
-        uint32_t *h2 = h1 + NC + 64;                  // fine counters, two per word
-        uint32_t *vars = h2 + REF_NB / 2 + 64;
-        uint32_t *buf = (uint32_t *)(my + REF_HDR);   // ref_cap staged entries
-        const uint32_t cap = (uint32_t)p.ref_cap;
-        uint32_t mx = 0u, mnm1 = 0xFFFFFFFFu;
-#pragma unroll
-        for (int e = 0; e < REF_E / 4; ++e)
-            if (e < e4) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const uint32_t k = key[4 * e + v];
-                    mx = max(mx, k);
-                    mnm1 = min(mnm1, k - 1u);  // empty slots (0) wrap to the top
-                }
-            }
-        mx = wave_max(mx);
-        const uint32_t mn = wave_min(mnm1) + 1u;
-        uint32_t klo = mn;
-        {
-            const float pf = (float)msel / (float)nc;
-            const int rs = (int)ceilf(64.f * pf + 4.f * sqrtf(64.f * pf * (1.f - pf))) + 2;
-            if (nc >= 64 && rs <= 64) {
-                uint32_t rk = 0;
-#pragma unroll
-                for (int m = 0; m < 64; ++m) {
-                    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)smp, m);
-                    rk += (o > smp || (o == smp && m < l)) ? 1u : 0u;
-                }
-                const unsigned long long bal = __ballot(rk == (uint32_t)(rs - 1));
-                klo = (uint32_t)__builtin_amdgcn_readlane((int)smp, (int)__builtin_ctzll(bal));
-            }
-        }
-        // lane l owns coarse bins [NC - CPL (l + 1), NC - CPL l), the top first
-        uint32_t *mine = h1 + NC - CPL * (l + 1);
-        uint32_t cc[CPL];
-        int sh1 = 0;
-        uint32_t b1 = 0, nt = 0;
-        for (int att = 0; att < 2; ++att) {
-            const int bw1 = bit_width(mx - klo);
-            sh1 = bw1 > REF_LOG2C ? bw1 - REF_LOG2C : 0;
-            for (int i = l; i < (NC + 64 + REF_NB / 2 + 64) / 4; i += 64)
-                ((uint4 *)h1)[i] = make_uint4(0u, 0u, 0u, 0u);
-            if (l == 0) vars[0] = 0xFFFFFFFFu;
-            wave_lds_sync();
-#pragma unroll
-            for (int e = 0; e < REF_E / 4; ++e)
-                if (e < e4) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const uint32_t k = key[4 * e + v];
-                        atomicAdd(&h1[k >= klo ? (k - klo) >> sh1 : (uint32_t)(NC + l)], 1u);
-                    }
-                }
-            wave_lds_sync();
-            uint32_t loc = 0;
-#pragma unroll
-            for (int i = 0; i < CPL / 4; ++i) {
-                const uint4 c4 = *(const uint4 *)(mine + 4 * i);
-                cc[4 * i + 0] = c4.x;
-                cc[4 * i + 1] = c4.y;
-                cc[4 * i + 2] = c4.z;
-                cc[4 * i + 3] = c4.w;
-                loc += c4.x + c4.y + c4.z + c4.w;
-            }
-            uint32_t run = wave_incl_scan(loc) - loc;
-#pragma unroll
-            for (int i = CPL - 1; i >= 0; --i) {
-                if (run < msel && msel <= run + cc[i]) {
-                    vars[0] = (uint32_t)(NC - CPL * (l + 1) + i);
-                    vars[1] = run + cc[i];
-                }
-                run += cc[i];
-            }
-            wave_lds_sync();
-            b1 = vars[0];
-            nt = vars[1];
-            if (b1 != 0xFFFFFFFFu) break;
-            klo = mn;  // the sample was not below the msel-th key
-        }
-        // -- 2. fine buckets per coarse bin: n = the power of two nearest to
-        //    0.9 * count * 2048 / nt (rounded down instead when that
-        //    overshoots 2048 in all), at least 2^(sh1 - 20) so that a key's
-        //    bits inside its fine bucket fit 20 bits, at most 2^sh1. Table
-        //    word = fine base | log2(n) << 12 (an empty bin at or above b1:
-        //    the running base | 1 << 17).
-        const uint32_t lgmin = sh1 > 20 ? (uint32_t)(sh1 - 20) : 0u;
-        const float scl = (float)(REF_NB * 9 / 10) / (float)nt;
-        for (int round_down = 0; round_down < 2; ++round_down) {
-            uint32_t lgs[CPL], loc = 0;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const uint32_t bin = NC - CPL * (l + 1) + i;
-                const uint32_t c = cc[i];
-                uint32_t lg = 0xFFu;  // no fine buckets
-                if (bin >= b1 && c != 0u) {
-                    const uint32_t want = max(1u, (uint32_t)((float)c * scl));
-                    lg = (uint32_t)(31 - __clz((int)want));
-                    // nearest: round up when want >= 1.5 * 2^lg
-                    if (!round_down && 2u * want >= 3u << lg) ++lg;
-                    lg = min(lg, (uint32_t)sh1);
-                    lg = max(lg, lgmin);
-                    loc += 1u << lg;
-                }
-                lgs[i] = lg;
-            }
-            const uint32_t total = wave_sum(loc);
-            if (total > (uint32_t)REF_NB && !round_down) continue;
-            uint32_t run = wave_incl_scan(loc) - loc;
-            wave_lds_sync();
-#pragma unroll
-            for (int i = CPL - 1; i >= 0; --i) {
-                const uint32_t lg = lgs[i];
-                const uint32_t bin = NC - CPL * (l + 1) + i;
-                // empty bins at or above b1 take no bucket but keep the base
-                // running, so bases never increase with the bin
-                mine[i] = lg != 0xFFu ? (run | (lg << 12)) : (bin >= b1 ? (run | (1u << 17)) : 0xFFFFFFFFu);
-                if (lg != 0xFFu) run += 1u << lg;
-            }
-            if (l == 63) vars[2] = run;  // fine buckets in use
-            break;
-        }
-        wave_lds_sync();
-        // a packed word's coarse bin is the lowest bin at or above b1 whose
-        // table base is <= its fine bucket (bases fall as bins rise)
-        auto unpack = [&](uint32_t w) -> uint32_t {
-            if (w == 0xFFFFFFFFu) return 0u;
-            const uint32_t fb = w >> 20;
-            uint32_t lo = b1, hi = NC - 1;
-            while (lo < hi) {
-                const uint32_t mid = (lo + hi) >> 1;
-                if ((h1[mid] & 0xFFFu) <= fb) hi = mid;
-                else lo = mid + 1;
-            }
-            const uint32_t t = h1[lo];
-            const uint32_t lg = (t >> 12) & 31u;
-            const uint32_t sub = ((uint32_t)sh1 - lg) & 31u;
-            const uint32_t top = (1u << lg) - 1u - (fb - (t & 0xFFFu));
-            const uint32_t low = (top << sub) | (w & ((1u << sub) - 1u));
-            return klo + (lo << sh1) + low;
-        };
-        if (vars[2] <= (uint32_t)REF_NB && !p.out_score) {
-            // packed word of a key: fine bucket << 20 | its bits inside the
-            // fine bucket (0 = best bucket); 0xFFFFFFFF when not wanted
-            // (below the range, below b1, or an empty slot)
-            auto packed = [&](uint32_t k) -> uint32_t {
-                const uint32_t rel = k - klo;
-                const uint32_t bin = rel >> sh1;
-                const uint32_t t = h1[min(bin, (uint32_t)(NC - 1))];
-                const uint32_t lg = (t >> 12) & 31u;
-                const uint32_t sub = ((uint32_t)sh1 - lg) & 31u;
-                const uint32_t low = rel & ((1u << sh1) - 1u);
-                const uint32_t w =
-                    (((t & 0xFFFu) + ((1u << lg) - 1u - (low >> sub))) << 20) | (low & ((1u << sub) - 1u));
-                return (k < klo || bin < b1) ? 0xFFFFFFFFu : w;
-            };
-            // -- 3. fine histogram, crossing, offsets. From here on each key
-            //    register holds its packed word (every slot, so empty ones
-            //    read as "not wanted" in all passes); unpack() gives the key
-            //    back to the general path.
-#pragma unroll
-            for (int e = 0; e < REF_E / 4; ++e) {
-                if (e < e4) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const uint32_t w = packed(key[4 * e + v]);
-                        key[4 * e + v] = w;
-                        const uint32_t f = w == 0xFFFFFFFFu ? (uint32_t)(REF_NB + 2 * l) : (w >> 20);
-                        atomicAdd(&h2[f >> 1], 1u << ((f & 1u) << 4));
-                    }
-                } else {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) key[4 * e + v] = 0xFFFFFFFFu;
-                }
-                __builtin_amdgcn_sched_barrier(0);  // bound the loads in flight
-            }
-            wave_lds_sync();
-            {
-                uint32_t *fw = h2 + (REF_NB / 128) * l;  // lane l: fine buckets 32 l .. 32 l + 31
-                uint32_t loc = 0;
-#pragma unroll
-                for (int i = 0; i < REF_NB / 512; ++i) {
-                    const uint4 c4 = *(const uint4 *)(fw + 4 * i);
-                    loc += (c4.x & 0xFFFFu) + (c4.x >> 16) + (c4.y & 0xFFFFu) + (c4.y >> 16) +
-                           (c4.z & 0xFFFFu) + (c4.z >> 16) + (c4.w & 0xFFFFu) + (c4.w >> 16);
-                }
-                uint32_t run = wave_incl_scan(loc) - loc;
-#pragma unroll
-                for (int i = 0; i < REF_NB / 512; ++i) {
-                    const uint4 c4 = *(const uint4 *)(fw + 4 * i);
-                    const uint32_t w4[4] = {c4.x, c4.y, c4.z, c4.w};
-                    uint32_t o4[4];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const uint32_t c = (w4[t >> 1] >> ((t & 1) << 4)) & 0xFFFFu;
-                        if (t & 1) o4[t >> 1] |= run << 16;
-                        else o4[t >> 1] = run;
-                        if (run < msel && msel <= run + c) {
-                            vars[3] = (uint32_t)(32 * l + 8 * i + t);
-                            vars[4] = run + c;
-                        }
-                        run += c;
-                    }
-                    *(uint4 *)(fw + 4 * i) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
-                }
-            }
-            wave_lds_sync();
-            const uint32_t fstar = vars[3];
-            const uint32_t nsc = vars[4];
-            // h1 (the table, dead once every key is packed) then holds a 16-bit
-            // bucket tag per staged entry; h1..h2 (dead once every rank is
-            // known) then hold the finished row.
-            constexpr uint32_t STG = (uint32_t)(NC + 64 + REF_NB / 2 + 64);
-            constexpr uint32_t TAGS = 2u * (uint32_t)(NC + 64) - 64u;  // + 64 trash tags
-            constexpr int NSL = 36;                                     // staged slots per lane
-            static_assert(NSL % 4 == 0 && 64 * NSL >= (int)TAGS, "every staged slot has a lane");
-            if (nsc <= cap && nsc <= TAGS && msel <= STG) {
-                wave_lds_sync();
-                uint16_t *tag = (uint16_t *)h1;
-                const uint32_t trashf = (uint32_t)(REF_NB + 2 * l);
-                // -- 4. scatter fine buckets 0 .. fstar as (key bits in the
-                //    bucket << 12 | position) with the bucket as a tag (slots
-                //    of 8 keys claimed before any is stored, so the atomics
-                //    overlap; keys not taken go to per-lane trash slots)
-#pragma clang loop unroll(full)
-                for (int e0 = 0; e0 < REF_E / 4; e0 += 2)
-                    if (e0 < e4) {
-                        uint32_t got[8], fb[8];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            const uint32_t w = key[4 * e0 + i];
-                            fb[i] = (w == 0xFFFFFFFFu || (w >> 20) > fstar) ? trashf : (w >> 20);
-                            got[i] = atomicAdd(&h2[fb[i] >> 1], 1u << ((fb[i] & 1u) << 4));
-                        }
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            const int e = e0 + i / 4, v = i % 4;
-                            const bool take = fb[i] < (uint32_t)REF_NB && e < e4;
-                            const uint32_t slot = (got[i] >> ((fb[i] & 1u) << 4)) & 0xFFFFu;
-                            buf[take ? slot : cap + l] =
-                                ((key[4 * e0 + i] & 0xFFFFFu) << 12) | (256u * (uint32_t)e + (uint32_t)(4 * l + v));
-                            tag[take ? slot : TAGS + l] = (uint16_t)fb[i];
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                wave_lds_sync();
-                // -- 5. rank inside the bucket. Slots run in bucket order, so
-                //    ordering every bucket puts the row in place. Lane l
-                //    holds the staged slots [NSL l, NSL (l + 1)) and X more
-                //    on either side as 64-bit words (bucket + 1) << 52 |
-                //    (inverted key bits in the bucket) << 32 | key index and
-                //    runs odd-even transposition rounds until none swaps:
-                //    the words of a bucket then stand in final order (score
-                //    desc, index asc), and every bucket that touches the
-                //    lane's own slots is whole in its window unless it
-                //    reaches past an edge of the window. In that rare case
-                //    every entry is ranked by a counted loop over its bucket
-                //    instead and stored straight to the output row.
-                constexpr int X = 8;
-                constexpr int NW = NSL + 2 * X;
-                const uint32_t s0 = (uint32_t)(NSL * l);
-                const bool own = s0 < nsc;
-                // window entries below lim hold slots before nsc
-                const int lim = own ? (int)(nsc - s0) + X : 0;
-                uint64_t A[NW];
-                {
-                    const uint4 *bp = (const uint4 *)(buf + s0);
-                    const uint2 *tp = (const uint2 *)(tag + s0);
-#pragma unroll
-                    for (int i = -X / 4; i < NSL / 4 + X / 4; ++i) {
-                        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-                        uint2 y = make_uint2(0u, 0u);
-                        if (own && (i >= 0 || l > 0)) {
-                            x = bp[i];
-                            y = tp[i];
-                        }
-                        const int j = 4 * i + X;
-                        const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
-                        const uint32_t tg[4] = {y.x & 0xFFFFu, y.x >> 16, y.y & 0xFFFFu, y.y >> 16};
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            // window entry j + q is slot s0 - X + j + q; the list
-                            // read stays inside LDS whatever the word holds
-                            const bool ok = j + q < X ? l > 0 : j + q < lim;
-                            const uint32_t idx = cl[wd[q] & 4095u];
-                            const uint32_t kv = ((tg[q] + 1u) << 20) | (0xFFFFFu - (wd[q] >> 12));
-                            A[j + q] = ok ? (((uint64_t)kv << 32) | idx) : (j + q < X ? 0ull : ~0ull);
-                        }
-                    }
-                }
-                // a bucket reaching from an own slot past the window
-                const uint32_t tl = (uint32_t)(A[0] >> 52), tf = (uint32_t)(A[X] >> 52);
-                const uint32_t tb = (uint32_t)(A[X + NSL - 1] >> 52), tr = (uint32_t)(A[NW - 1] >> 52);
-                const bool edge = own && ((tl != 0u && tl == tf) || (tb <= (uint32_t)REF_NB && tb == tr));
-                if (__ballot(edge) == 0ull) {
-                    for (int it = 0; it <= NW / 2; ++it) {
-                        bool sw = false;
-#pragma unroll
-                        for (int par = 0; par < 2; ++par) {
-#pragma unroll
-                            for (int i = par; i + 1 < NW; i += 2) {
-                                const bool c = A[i] > A[i + 1];
-                                const uint64_t a = A[i];
-                                A[i] = c ? A[i + 1] : a;
-                                A[i + 1] = c ? a : A[i + 1];
-                                sw |= c;
-                            }
-                        }
-                        if (__ballot(sw) == 0ull) break;
-                    }
-                    wave_lds_sync();
-                    // -- 6. finished row into LDS, then out with whole-line stores
-                    const int nown = own ? (int)min(msel - min(msel, s0), (uint32_t)NSL) : 0;
-#pragma unroll
-                    for (int t = 0; t < NSL; t += 4) {
-                        const uint4 o = make_uint4((uint32_t)A[X + t], (uint32_t)A[X + t + 1], (uint32_t)A[X + t + 2],
-                                                   (uint32_t)A[X + t + 3]);
-                        if (t + 4 <= nown) {
-                            *(uint4 *)(buf + s0 + t) = o;
-                        } else if (t < nown) {
-                            buf[s0 + t] = o.x;
-                            if (t + 1 < nown) buf[s0 + t + 1] = o.y;
-                            if (t + 2 < nown) buf[s0 + t + 2] = o.z;
-                        }
-                    }
-                    wave_lds_sync();
-                    int32_t *dst = p.out_idx + obase;
-                    for (int c = l; c < p.top_k; c += 64) dst[c] = c < (int)msel ? (int32_t)buf[c] : -1;
-                    return;
-                }
-                auto fend = [&](uint32_t f) { return (h2[f >> 1] >> ((f & 1u) << 4)) & 0xFFFFu; };
-                int32_t *dst = p.out_idx + obase;
-                for (uint32_t t = 0; t < (uint32_t)NSL; ++t) {
-                    const uint32_t u = s0 + t;
-                    if (u < nsc) {
-                        const uint32_t w = buf[u];
-                        const uint32_t f = tag[u];
-                        const uint32_t end = fend(f);
-                        const uint32_t beg = f == 0u ? 0u : fend(f - 1u);
-                        const uint32_t lw = w >> 12;
-                        const uint32_t myidx = cl[w & 4095u];
-                        uint32_t rank = 0;
-                        for (uint32_t x = beg; x < end; ++x) {
-                            const uint32_t en = buf[x];
-                            const uint32_t le = en >> 12;
-                            if (le > lw) ++rank;
-                            else if (le == lw && x != u) rank += cl[en & 4095u] < myidx ? 1u : 0u;
-                        }
-                        if (beg + rank < msel) dst[beg + rank] = (int32_t)myidx;
-                    }
-                }
-                for (int c = (int)msel + l; c < p.top_k; c += 64) dst[c] = -1;
-                return;
-            }
-            // the boundary bucket does not fit: the general path needs the
-            // keys back; keys below b1 rank under the msel-th and become 0.
-#pragma unroll
-            for (int i = 0; i < REF_E; ++i) key[i] = unpack(key[i]);
-        }
-        wave_lds_sync();
+    const uint32_t *row = nullptr;
+    if (!p.out_score) {
+        int32_t *dst = p.out_idx + obase;
+        const int st = fused_select<REF_E, 12>(
+            key, e4, nc, msel, smp, my, (uint32_t)p.ref_cap, [&](uint32_t pos) { return cl[pos]; },
+            [&](uint32_t fin, uint32_t idx) { dst[fin] = (int32_t)idx; }, row);
+        if (st == 1)
+            for (int c = l; c < p.top_k; c += 64) dst[c] = c < (int)msel ? (int32_t)row[c] : -1;
+        if (st == 2)
+            for (int c = (int)msel + l; c < p.top_k; c += 64) dst[c] = -1;
+        if (st != 0) return;
     }
 
     // ---- general path: the boundary bucket is too large to stage (heavy
@@ -1452,7 +1596,7 @@ struct Plan {
     int n_tiles;
     size_t esz;
     // per-head bytes of each workspace array
-    size_t b_P, b_tau, b_cnt, b_scnt, b_surv, b_samp, b_cand, b_fbl;
+    size_t b_P, b_tau, b_cnt, b_scnt, b_surv, b_samp, b_cand, b_fbl, b_big;
     size_t fixed;  // fb_count + fallback scratch
 };
 
@@ -1526,12 +1670,13 @@ int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio,
     pl.b_samp = pl.n_max > pl.keep_all_n ? align256(rows * 2 * (size_t)(pl.samp_half + 32) * 8) : 0;
     pl.b_cand = pl.mode == PIVOT_REFINE ? align256(rows * (size_t)K * 4) : 0;
     pl.b_fbl = align256(rows * 4);
+    pl.b_big = pl.mode == PIVOT_REUSE ? align256(rows * 4) : 0;
     pl.fixed = 256 + align256((size_t)FB_BLOCKS * (size_t)pl.n_max * 4);
     return PIVOT_OK;
 }
 
 size_t per_head_bytes(const Plan &pl) {
-    return pl.b_P + pl.b_tau + pl.b_cnt + pl.b_scnt + pl.b_surv + pl.b_samp + pl.b_cand + pl.b_fbl;
+    return pl.b_P + pl.b_tau + pl.b_cnt + pl.b_scnt + pl.b_surv + pl.b_samp + pl.b_cand + pl.b_fbl + pl.b_big;
 }
 
 hipError_t set_lds(const void *fn, size_t bytes) {
@@ -1641,6 +1786,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
         uint2 *samp = (uint2 *)take(pl.b_samp);
         uint32_t *cand = (uint32_t *)take(pl.b_cand);
         uint32_t *fbl = (uint32_t *)take(pl.b_fbl);
+        uint32_t *bigl = (uint32_t *)take(pl.b_big);
 
         ScanParams sp{};
         if (pl.dense) {
@@ -1666,7 +1812,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
         sp.g = pl.g;
         sp.n_tiles = pl.n_tiles;
         sp.Hc = Hc;
-        hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, st, fb_count, (int64_t)1);
+        hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, st, fb_count, (int64_t)2);
         HIP_TRY(hipGetLastError());
 
         // sample pass + thresholds
@@ -1719,9 +1865,25 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
         const int sorted_out = pl.mode == PIVOT_REUSE ? 1 : 0;
         {
             SelParams se{(const uint2 *)surv, cnt, pl.cap_half, pl.cap_half + 32, pl.G, pl.g, pl.Ksel, sorted_out, ro, fbl, fb_count};
+            se.big_list = bigl;
+            se.big_count = fb_count + 1;
+            se.rows = rows;
             const size_t lds = sel_lds_bytes(0);
             StageTimer tm(ST_SELECT, st);
-            hipLaunchKernelGGL(k_select, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, se);
+            // the wavefront sort stages at most 2112 entries: top_k up to
+            // 2048 leaves the boundary bucket its slack
+            if (sorted_out && pl.Ksel <= 2048) {
+                const size_t wlds = (size_t)SW_WAVES * SW_REG;
+                HIP_TRY(set_lds((const void *)k_select_wave, wlds));
+                hipLaunchKernelGGL(k_select_wave, dim3((unsigned)((rows + SW_WAVES - 1) / SW_WAVES)),
+                                   dim3(64 * SW_WAVES), wlds, st, se);
+                HIP_TRY(hipGetLastError());
+                se.list = 1;
+                hipLaunchKernelGGL(k_select, dim3((unsigned)std::min<int64_t>(rows, 2048)), dim3(SEL_THREADS), lds,
+                                   st, se);
+            } else {
+                hipLaunchKernelGGL(k_select, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, se);
+            }
             HIP_TRY(hipGetLastError());
         }
         {
