@@ -901,13 +901,15 @@ struct RefParams {
 // `my` is the wavefront's LDS region (REF_HDR bytes of header, then cap + 64
 // staged words); positions take POSB bits of a staged word, key bits inside
 // a fine bucket the other LOWB.
-// Returns 1: the row (key indices in final order) is in row[0, msel) (LDS);
-// 2: every entry went out through put(rank, index) (ranks >= msel are not
-// passed); 0: the general path must run, key[] hold the keys again.
-template <int E, int POSB, class IDX, class PUT>
-__device__ __forceinline__ int fused_select(uint32_t (&key)[E], const int e4, const int nc, const uint32_t msel,
-                                            const uint32_t smp, unsigned char *my, const uint32_t cap, IDX idx_of,
-                                            PUT put, const uint32_t *&row) {
+// Returns true when the row is out: either emit(row) was called with the
+// row (key indices in final order) in row[0, msel) of LDS, or every entry
+// went through put(rank, index) (ranks >= msel are not passed) and then
+// emit(nullptr). Returns false when the general path must run; key[] then
+// hold the keys again.
+template <int E, int POSB, class IDX, class PUT, class EMIT>
+__device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, const int nc, const uint32_t msel,
+                                             const uint32_t smp, unsigned char *my, const uint32_t cap, IDX idx_of,
+                                             PUT put, EMIT emit) {
     constexpr int LOWB = 32 - POSB;
     constexpr uint32_t LM = (1u << LOWB) - 1u;
     constexpr uint32_t PM = (1u << POSB) - 1u;
@@ -1130,7 +1132,7 @@ __device__ __forceinline__ int fused_select(uint32_t (&key)[E], const int e4, co
         constexpr uint32_t TAGS = 2u * (uint32_t)(NC + 64) - 64u;  // + 64 trash tags
         constexpr int NSL = 36;                                     // staged slots per lane
         static_assert(NSL % 4 == 0 && 64 * NSL >= (int)TAGS, "every staged slot has a lane");
-        if (nsc <= cap && nsc <= TAGS && msel <= STG) {
+        if (nsc <= cap && nsc <= TAGS && msel <= STG && cap + 64u >= 64u * (uint32_t)NSL) {
             wave_lds_sync();
             uint16_t *tag = (uint16_t *)h1;
             const uint32_t trashf = (uint32_t)(REF_NB + 2 * l);
@@ -1226,23 +1228,16 @@ __device__ __forceinline__ int fused_select(uint32_t (&key)[E], const int e4, co
                     if (__ballot(sw) == 0ull) break;
                 }
                 wave_lds_sync();
-                // -- 6. finished row into LDS, then out with whole-line stores
-                const int nown = own ? (int)min(msel - min(msel, s0), (uint32_t)NSL) : 0;
+                // -- 6. finished row into LDS (every lane stores its whole
+                //    run: slots past nsc are never read), then out with
+                //    whole-line stores
 #pragma unroll
-                for (int t = 0; t < NSL; t += 4) {
-                    const uint4 o = make_uint4((uint32_t)A[X + t], (uint32_t)A[X + t + 1], (uint32_t)A[X + t + 2],
-                                               (uint32_t)A[X + t + 3]);
-                    if (t + 4 <= nown) {
-                        *(uint4 *)(buf + s0 + t) = o;
-                    } else if (t < nown) {
-                        buf[s0 + t] = o.x;
-                        if (t + 1 < nown) buf[s0 + t + 1] = o.y;
-                        if (t + 2 < nown) buf[s0 + t + 2] = o.z;
-                    }
-                }
+                for (int t = 0; t < NSL; t += 4)
+                    *(uint4 *)(buf + s0 + t) = make_uint4((uint32_t)A[X + t], (uint32_t)A[X + t + 1],
+                                                          (uint32_t)A[X + t + 2], (uint32_t)A[X + t + 3]);
                 wave_lds_sync();
-                row = buf;
-                return 1;
+                emit((const uint32_t *)buf);
+                return true;
             }
             auto fend = [&](uint32_t f) { return (h2[f >> 1] >> ((f & 1u) << 4)) & 0xFFFFu; };
             for (uint32_t t = 0; t < (uint32_t)NSL; ++t) {
@@ -1264,7 +1259,8 @@ __device__ __forceinline__ int fused_select(uint32_t (&key)[E], const int e4, co
                     if (beg + rank < msel) put(beg + rank, myidx);
                 }
             }
-            return 2;
+            emit((const uint32_t *)nullptr);
+            return true;
         }
         // the boundary bucket does not fit: the general path needs the
         // keys back; keys below b1 rank under the msel-th and become 0.
@@ -1272,7 +1268,7 @@ __device__ __forceinline__ int fused_select(uint32_t (&key)[E], const int e4, co
         for (int i = 0; i < E; ++i) key[i] = unpack(key[i]);
     }
     wave_lds_sync();
-    return 0;
+    return false;
 }
 
 // ------------------------------------------------------- select (wave)
@@ -1348,24 +1344,17 @@ __global__ void __launch_bounds__(64 * SW_WAVES) k_select_wave(SelParams p) {
     const int m = (int)min((int64_t)p.g, p.o.S - i0);
     const int64_t rstride = (int64_t)p.o.H * p.o.top_k;
     int32_t *dst0 = p.o.out_idx + (i0 * p.o.H + p.o.h0 + hl) * (int64_t)p.o.top_k;
-    const uint32_t *row = nullptr;
-    const int st = fused_select<SW_E, 13>(
+    const bool done = fused_select<SW_E, 13>(
         key, e4, ns, msel, smp, smem + w * SW_REG, (uint32_t)SW_CAP, idx_of,
         [&](uint32_t fin, uint32_t idx) {
             for (int t = 0; t < m; ++t) dst0[t * rstride + fin] = (int32_t)idx;
         },
-        row);
-    if (st == 0) {
-        to_list();
-        return;
-    }
-    for (int t = 0; t < m; ++t) {
-        int32_t *dst = dst0 + t * rstride;
-        if (st == 1)
-            for (int c = l; c < p.o.top_k; c += 64) dst[c] = c < (int)msel ? (int32_t)row[c] : -1;
-        else
-            for (int c = (int)msel + l; c < p.o.top_k; c += 64) dst[c] = -1;
-    }
+        [&](const uint32_t *row) {
+            for (int t = 0; t < m; ++t)
+                for (int c = row ? l : (int)msel + l; c < p.o.top_k; c += 64)
+                    dst0[t * rstride + c] = c < (int)msel ? (int32_t)row[c] : -1;
+        });
+    if (!done) to_list();
 }
 
 template <typename T, int D>
@@ -1393,7 +1382,9 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     const int nc = (int)min(p.Kc, n);
     const int q0 = qb * p.nqw;
     const int nq = (int)min((int64_t)p.nqw, m - q0);
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    // the wavefront index is uniform: held in scalar registers, so are the
+    // addresses and counts derived from it
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int nthreads = p.nqw * 64;
 
     uint32_t *cl = (uint32_t *)smem;                    // candidate list (Kc)
@@ -1487,18 +1478,15 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     const uint32_t msel = (uint32_t)min(p.top_k, nc);
     const int64_t obase = ((qrow0 + q0 + w) * p.H + h) * (int64_t)p.top_k;
 
-    const uint32_t *row = nullptr;
-    if (!p.out_score) {
-        int32_t *dst = p.out_idx + obase;
-        const int st = fused_select<REF_E, 12>(
+    if (!p.out_score &&
+        fused_select<REF_E, 12>(
             key, e4, nc, msel, smp, my, (uint32_t)p.ref_cap, [&](uint32_t pos) { return cl[pos]; },
-            [&](uint32_t fin, uint32_t idx) { dst[fin] = (int32_t)idx; }, row);
-        if (st == 1)
-            for (int c = l; c < p.top_k; c += 64) dst[c] = c < (int)msel ? (int32_t)row[c] : -1;
-        if (st == 2)
-            for (int c = (int)msel + l; c < p.top_k; c += 64) dst[c] = -1;
-        if (st != 0) return;
-    }
+            [&](uint32_t fin, uint32_t idx) { p.out_idx[obase + fin] = (int32_t)idx; },
+            [&](const uint32_t *row) {
+                for (int c = row ? l : (int)msel + l; c < p.top_k; c += 64)
+                    p.out_idx[obase + c] = c < (int)msel ? (int32_t)row[c] : -1;
+            }))
+        return;
 
     // ---- general path: the boundary bucket is too large to stage (heavy
     // ties); exact narrowing selection, then a bucket sort of the selection
