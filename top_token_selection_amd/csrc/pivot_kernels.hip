@@ -177,7 +177,11 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     constexpr int NLD = SCAN_KEYS * NCK / SCAN_THREADS;  // loads per thread per tile
     constexpr int NSTREAM = 2 * SCAN_THREADS;  // (row, half) streams per block
     extern __shared__ __align__(16) unsigned char smem[];
-    uint2 *ring = (uint2 *)(smem + 2 * TILE);  // [RING][NSTREAM]
+    // survivor rings: score bits [RING][NSTREAM], then key indices likewise
+    uint32_t *ringS = (uint32_t *)(smem + 2 * TILE);
+    constexpr uint32_t RROW = NSTREAM * 4;         // bytes per ring row
+    constexpr uint32_t RKEYS = RING * NSTREAM;     // words from scores to keys
+    static_assert((RING & (RING - 1)) == 0 && (RROW & (RROW - 1)) == 0, "ring sizes are powers of two");
 
     const int nb = p.Hc * p.n_tiles;
     const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)nb);
@@ -201,11 +205,12 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     }
     const float never = __builtin_nanf("");  // s >= NaN is false for every s
 
-    // this lane's two streams: survivors cnt[gb] kept so far, fl[gb] of
-    // them already written to the stream's buffer at byte offset soff0[gb]
-    // from the block's part of the survivor array
+    // this lane's two streams: survivors kept so far (cs[gb], counted in
+    // units of RROW so that it is the ring row's byte offset once masked),
+    // fl[gb] of them already written to the stream's buffer at byte offset
+    // soff0[gb] from the block's part of the survivor array
     unsigned char *sb = (unsigned char *)p.out + ((int64_t)hl * p.G + j0) * 2 * (int64_t)p.stride * 8;
-    uint32_t soff0[2], cnt[2] = {0u, 0u}, fl[2] = {0u, 0u};
+    uint32_t soff0[2], cs[2] = {0u, 0u}, fl[2] = {0u, 0u};
     int vcount[2];
     float tau[2];
     for (int gb = 0; gb < 2; ++gb) {
@@ -293,17 +298,20 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     };
 
     // the FLUSH oldest staged survivors of stream gb leave as one chunk
-    // (entries fl .. fl+7 sit in ring slots fl % RING .. +7); at most
+    // (entries fl .. fl+7 sit in ring rows fl % RING .. +7); at most
     // cap_half + 16 are ever kept, inside the stream's stride
     auto flush = [&](int gb) {
-        if (cnt[gb] - fl[gb] >= (uint32_t)FLUSH) {
-            const uint2 *src = ring + (fl[gb] % RING) * NSTREAM + gb * SCAN_THREADS + stream0;
-            uint2 e[FLUSH];
+        if (cs[gb] / RROW - fl[gb] >= (uint32_t)FLUSH) {
+            const uint32_t *src = ringS + (fl[gb] % RING) * NSTREAM + gb * SCAN_THREADS + stream0;
+            uint32_t sv[FLUSH], kv[FLUSH];
 #pragma unroll
-            for (int i = 0; i < FLUSH; ++i) e[i] = src[i * NSTREAM];
+            for (int i = 0; i < FLUSH; ++i) {
+                sv[i] = src[i * NSTREAM];
+                kv[i] = src[i * NSTREAM + RKEYS];
+            }
             uint4 *dst = (uint4 *)(sb + soff0[gb] + fl[gb] * 8u);
 #pragma unroll
-            for (int i = 0; i < FLUSH / 2; ++i) dst[i] = make_uint4(e[2 * i].x, e[2 * i].y, e[2 * i + 1].x, e[2 * i + 1].y);
+            for (int i = 0; i < FLUSH / 2; ++i) dst[i] = make_uint4(sv[2 * i], kv[2 * i], sv[2 * i + 1], kv[2 * i + 1]);
             fl[gb] += FLUSH;
         }
     };
@@ -311,26 +319,37 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     // keep the scores of tile kt that reach the row's threshold; at most 16
     // per stream and tile. Tiles below every row's prefix end skip the causal
     // test. A flush check after every 8 scores keeps the ring from filling.
+    // Per score: one compare (two on causal tiles), the count update, the
+    // ring row address from the count (one and-or), and two 32-bit LDS
+    // stores (score bits, key index); the 16 key indices of the tile are
+    // shared by both column blocks. A slot is written whether kept or not
+    // (row cnt % RING is free: fewer than RING entries wait); only kept ones
+    // are counted.
     auto filter = [&](int kt, const acc_t &acc) {
 #pragma unroll
         for (int gb = 0; gb < 2; ++gb)
-            if (cnt[gb] > (uint32_t)p.cap_half) tau[gb] = never;
+            if (cs[gb] > (uint32_t)p.cap_half * RROW) tau[gb] = never;
         const uint32_t tkey = kstr * (uint32_t)(kt * SCAN_KEYS) + lane_key;
+        uint32_t kv[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) kv[v] = tkey + kstr * (uint32_t)(8 * (v >> 2) + (v & 3));
         auto run = [&](auto causal) {
 #pragma unroll
             for (int gb = 0; gb < 2; ++gb) {
-                uint2 *rs = ring + gb * SCAN_THREADS + stream0;
+                // byte offset of this stream's column in a ring row
+                const uint32_t col = (uint32_t)(gb * SCAN_THREADS + stream0) * 4u;
+                // rows' key bound relative to this lane's first key of the tile
+                const int lim = vcount[gb] - (kt * SCAN_KEYS + 4 * half);
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int vo = 8 * (v >> 2) + (v & 3);  // + 4 * half
-                    const float s = acc[gb][v];
-                    bool keep = s >= tau[gb];
-                    if constexpr (decltype(causal)::value)
-                        keep = keep && (kt * SCAN_KEYS + vo + 4 * half < vcount[gb]);
-                    // written whether kept or not (slot cnt % RING is free:
-                    // fewer than RING entries wait), counted only if kept
-                    rs[(cnt[gb] % RING) * NSTREAM] = make_uint2(__float_as_uint(s), tkey + kstr * (uint32_t)vo);
-                    cnt[gb] += keep ? 1u : 0u;
+                    const int vo = 8 * (v >> 2) + (v & 3);
+                    const float sc = acc[gb][v];
+                    bool keep = sc >= tau[gb];
+                    if constexpr (decltype(causal)::value) keep = keep && (vo < lim);
+                    uint32_t *slot = (uint32_t *)((unsigned char *)ringS + ((cs[gb] & ((RING - 1) * RROW)) | col));
+                    slot[0] = __float_as_uint(sc);
+                    slot[RKEYS] = kv[v];
+                    cs[gb] += keep ? RROW : 0u;
                     if ((v & 7) == 7) flush(gb);
                 }
             }
@@ -366,11 +385,12 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
 
     // the rest of each ring (fewer than FLUSH entries) one by one
     for (int gb = 0; gb < 2; ++gb) {
-        const uint2 *rs = ring + gb * SCAN_THREADS + stream0;
-        for (uint32_t e = fl[gb]; e < cnt[gb]; ++e)
-            *(uint2 *)(sb + soff0[gb] + e * 8u) = rs[(e % RING) * NSTREAM];
+        const uint32_t *rs = ringS + gb * SCAN_THREADS + stream0;
+        const uint32_t cnt = cs[gb] / RROW;
+        for (uint32_t e = fl[gb]; e < cnt; ++e)
+            *(uint2 *)(sb + soff0[gb] + e * 8u) = make_uint2(rs[(e % RING) * NSTREAM], rs[(e % RING) * NSTREAM + RKEYS]);
         const int64_t j = j0 + 64 * w + 32 * gb + (l & 31);
-        if (j < p.G) p.cnt[((int64_t)hl * p.G + j) * 2 + half] = (int)cnt[gb];
+        if (j < p.G) p.cnt[((int64_t)hl * p.G + j) * 2 + half] = (int)cnt;
     }
 }
 
