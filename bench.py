@@ -99,6 +99,48 @@ def time_calls(fn, steps: int, warmup: int, pv):
     return ms, wall / steps * 1e3, per_stage, launches
 
 
+def sweep(args, dev, torch, np, syn, pv):
+    """Recall-speed grid over group size and candidate ratio (the pages fix g
+    by hand and give no adaptive rule); one JSON line."""
+    S, H, D = 65536, 64, 128
+    log(f"drawing prefill S={S} H={H} D={D} on the device")
+    cfg = syn.long_prefill_device(dev, S=S, H=H, g=8, seed=1003)
+    q, k = cfg["q"], cfg["k"]
+    rng = np.random.default_rng(17)
+    nrows = 1024
+    ri = torch.from_numpy(rng.integers(32, S, nrows)).to(dev)
+    rh = torch.from_numpy(rng.integers(0, H, nrows)).to(dev)
+    grid = []
+    for top_k, ratios in ((2048, (1.0, 1.5, 2.0)), (1024, (1.0, 1.5, 2.0, 4.0))):
+        out = torch.empty((S, H, top_k), dtype=torch.int32, device=dev)
+        dense_ms, _, _, _ = time_calls(lambda: pv.dense_index(q, k, top_k, out=out, max_workspace_bytes=48 << 30),
+                                       1, 1, pv)
+        ref = out[ri, rh].cpu().numpy()
+        ref_sets = [set(r[r >= 0].tolist()) for r in ref]
+        for g in (1, 2, 4, 8, 16, 32):
+            for ratio in ratios:
+                for mode in ("refine", "reuse"):
+                    # small groups need large workspaces: heads then run in chunks
+                    def call():
+                        pv.index_prefill(q, k, top_k, g, ratio, mode, out=out, max_workspace_bytes=200 << 30)
+                    ms, _, _, _ = time_calls(call, max(1, args.steps // 2), 1, pv)
+                    rows = out[ri, rh].cpu().numpy()
+                    rec = float(np.mean([len(set(a[a >= 0].tolist()) & b) / len(b) for a, b in zip(rows, ref_sets)]))
+                    e = {"top_k": top_k, "g": g, "candidate_ratio": ratio, "K": pv.candidate_count(top_k, ratio),
+                         "mode": mode, "ms_per_call": ms, "queries_per_s": S * H / (ms / 1e3),
+                         "speedup_vs_dense": dense_ms / ms, "recall": rec}
+                    grid.append(e)
+                    log(f"top_k={top_k} g={g:2d} ratio={ratio} {mode}: {ms:7.2f} ms, recall {rec:.4f}, "
+                        f"x{dense_ms / ms:.2f} vs dense")
+        grid.append({"top_k": top_k, "mode": "dense", "ms_per_call": dense_ms,
+                     "queries_per_s": S * H / (dense_ms / 1e3)})
+        del out
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "g x candidate_ratio", "workload": f"S={S} H={H} D={D} bf16 AR(1)/Pareto seed 1003",
+                      "recall_rows": nrows, "recall_against": "dense indexer (GPU), seed 17 sample",
+                      "grid": grid}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,9 +150,15 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip timing the dense indexer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other workloads (tiny, S=16384 integer, S=131072 long)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     ap.add_argument("--recall-rows", type=int, default=256)
     ap.add_argument("--long", action="store_true", help="S=131072, H=32, g=16 instead")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line: recall@top_k against the dense indexer and time per call "
+                         "over g in {1,2,4,8,16,32} and candidate_ratio in {1,1.5,2,4} on the S=65536 workload "
+                         "(top_k 2048 for K <= 4096, and top_k 1024 for every ratio)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain float32 copy kernel (1 GiB read, 1 GiB written) so that "
                          "a counter run can scale FETCH_SIZE / WRITE_SIZE")
@@ -139,6 +187,9 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy: {n * 4} bytes read, {n * 4} bytes written")
         del src, dst
+    if args.sweep:
+        sweep(args, dev, torch, np, syn, pv)
+        return
     S, H, g = (131072, 32, 16) if args.long else (65536, 64, 8)
     D, top_k, ratio = 128, 2048, 2.0
     K = pv.candidate_count(top_k, ratio)
@@ -286,6 +337,85 @@ def main():
             del dc, dws, dout
             torch.cuda.empty_cache()
 
+    # ----------------------------------------------------- other workloads
+    configs = None
+    if not args.no_configs:
+        configs = {}
+
+        def host(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        def prefill_config(name, qd, kd, tk, gg, modes, dense_too, ksteps):
+            Sx, Hx, Dx = qd.shape
+            Kx = pv.candidate_count(tk, 2.0)
+            wsx = torch.empty(max(pv.prefill_workspace_bytes(Sx, Hx, Dx, tk, gg, 2.0, m, qd.dtype)
+                                  for m in ("refine", "reuse")), dtype=torch.uint8, device=dev)
+            outx = torch.empty((Sx, Hx, tk), dtype=torch.int32, device=dev)
+            sn, _ = prefix_sums(Sx, gg, Kx)
+            res = {"S": Sx, "H": Hx, "D": Dx, "top_k": tk, "g": gg, "K": Kx, "dtype": str(qd.dtype)}
+            for mode in modes:
+                def call():
+                    pv.index_prefill(qd, kd, tk, gg, 2.0, mode, workspace=wsx, out=outx)
+                cms, _, cst, _ = time_calls(call, ksteps, args.warmup, pv)
+                st = cst.get("scan", 0.0) / 1e3
+                res[mode] = {"ms_per_step": cms, "queries_per_s": Sx * Hx / (cms / 1e3), "stage_ms": cst,
+                             "scan_mfma_frac": 2.0 * Dx * Hx * sn / st / BF16_PEAK if st else None}
+                log(f"{name} {mode}: {cms:.3f} ms/step ({Sx * Hx / (cms / 1e3):.3e} queries/s)")
+            if dense_too:
+                def dcall():
+                    pv.dense_index(qd, kd, tk, workspace=wsx, out=outx)
+                cms, _, cst, _ = time_calls(dcall, ksteps, args.warmup, pv)
+                res["dense"] = {"ms_per_step": cms, "queries_per_s": Sx * Hx / (cms / 1e3), "stage_ms": cst}
+                log(f"{name} dense: {cms:.3f} ms/step")
+            del wsx, outx
+            return res
+
+        tc = syn.tiny_prefill()
+        configs["tiny"] = prefill_config("tiny S=1024 H=8 D=64 fp32", host(tc["q"]), host(tc["k"]), 64, 8,
+                                         ("refine", "reuse"), True, args.steps * 4)
+        ic = syn.int_prefill()
+        configs["int16k"] = prefill_config("S=16384 H=16 integer bf16", host(ic["q"]), host(ic["k"]), 512, 8,
+                                           ("refine", "reuse"), False, args.steps * 2)
+        del tc, ic
+        log("drawing the long prefill S=131072 H=32 g=16 on the device")
+        lc = syn.long_prefill_device(dev, S=131072, H=32, g=16, seed=1004)
+        lres = prefill_config("long S=131072 H=32 g=16", lc["q"], lc["k"], 2048, 16, ("refine", "reuse"),
+                              False, max(2, args.steps // 2))
+        # recall@2048 on a 4096-row sample against the dense indexer (GPU;
+        # bit-exact to the oracle on integer inputs, tie-tolerant on these)
+        if args.recall_rows > 0:
+            Sl, Hl = 131072, 32
+            rng = np.random.default_rng(13)
+            li = torch.from_numpy(rng.integers(16, Sl, 4096)).to(dev)
+            lh = torch.from_numpy(rng.integers(0, Hl, 4096)).to(dev)
+            lws = torch.empty(pv.prefill_workspace_bytes(Sl, Hl, 128, 2048, 16, 2.0, "refine", torch.bfloat16),
+                              dtype=torch.uint8, device=dev)
+            lout = torch.empty((Sl, Hl, 2048), dtype=torch.int32, device=dev)
+            rows = {}
+            for mode in ("refine", "reuse"):
+                pv.index_prefill(lc["q"], lc["k"], 2048, 16, 2.0, mode, workspace=lws, out=lout)
+                rows[mode] = lout[li, lh].cpu().numpy()
+            del lws
+            pv.dense_index(lc["q"], lc["k"], 2048, out=lout, max_workspace_bytes=48 << 30)
+            drows = lout[li, lh].cpu().numpy()
+            del lout
+
+            def rec2(a_rows):
+                vals = []
+                for a, b in zip(a_rows, drows):
+                    bs = set(b[b >= 0].tolist())
+                    vals.append(len(set(a[a >= 0].tolist()) & bs) / len(bs))
+                return float(np.mean(vals))
+            lres["recall"] = {"refine": rec2(rows["refine"]), "reuse": rec2(rows["reuse"]), "rows": 4096,
+                              "against": "dense indexer (GPU)",
+                              "sample": "positions uniform in [16, S), heads uniform, seed 13"}
+            log(f"long recall@2048: {lres['recall']}")
+        configs["long131k"] = lres
+        del lc
+        torch.cuda.empty_cache()
+
     line = {
         "metric": "indexed queries/s (Refine, S=64K prefill) + decode us/step; % MFMA/HBM roofline",
         "value": qps,
@@ -321,6 +451,7 @@ def main():
                                          if dense_ms else None),
             "decode": decode,
             "recall": recall,
+            "configs": configs,
             "host": {"cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count(),
                      "gpu": torch.cuda.get_device_name(dev)},
         },
