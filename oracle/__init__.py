@@ -22,8 +22,10 @@ _SRC = os.path.join(_HERE, "pivot_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
-REFINE, REUSE = 0, 1
-MODES = {"refine": REFINE, "reuse": REUSE}
+REFINE, REUSE, REFINE_LITERAL = 0, 1, 2
+# "refine_literal": the per-position-rescan Refine of the pages' pivot_refine
+# code (prefill only; prefill() and prefill_rows())
+MODES = {"refine": REFINE, "reuse": REUSE, "refine_literal": REFINE_LITERAL}
 
 _lib = None
 

@@ -38,7 +38,12 @@
  *   - dense indexer: query i ranks keys [0, max(i, 1)) by its own score;
  *   - decode: the g queries of one multi-token-prediction step of sequence b
  *     form one group whose prefix is the whole cached context [0, ctx_b),
- *     ctx_b >= 1.
+ *     ctx_b >= 1;
+ *   - the literal per-position Refine (mode 2, kept for comparison): the
+ *     pivot_refine code of "Show Me The Code" as written -- position i >= 1
+ *     scans keys [0, i) with its group's proxy, takes its own candidate set
+ *     and re-scores it with q_i; position 0, which that code skips, gets a
+ *     row of padding.
  */
 #include <math.h>
 #include <stdint.h>
@@ -49,6 +54,7 @@
 #define OR_BF16 1
 #define OR_REFINE 0
 #define OR_REUSE 1
+#define OR_REFINE_LITERAL 2
 
 #define OR_OK 0
 #define OR_EINVAL (-1)
@@ -260,6 +266,56 @@ static int one_group(const void *q, const void *k, int dt, int H, int D,
     return OR_OK;
 }
 
+/* The literal per-position Refine row of position i, head h (the pivot_refine
+ * code of "Show Me The Code"): the proxy of i's group scans keys [0, i), the
+ * first min(K, i) under the total order are i's candidates, q_i re-scores
+ * them and keeps its own first min(top_k, |C|). Position 0 is skipped by that
+ * code: its row is all padding. */
+static int literal_row(const void *q, const void *k, int dt, int64_t S, int H, int D,
+                       int top_k, int64_t K, int g, int h, int64_t i,
+                       int32_t *out_idx, float *out_score, size_t row_off)
+{
+    if (i == 0) {
+        write_row(out_idx, out_score, row_off, top_k, NULL, 0);
+        return OR_OK;
+    }
+    int64_t i0 = (i / g) * (int64_t)g;
+    int64_t m = min64(g, S - i0);
+    int64_t n = i;
+    int64_t nc = min64(K, n);
+    float *p = (float *)malloc(sizeof(float) * (size_t)D);
+    float *a = (float *)malloc(sizeof(float) * (size_t)D);
+    scored_t *all = (scored_t *)malloc(sizeof(scored_t) * (size_t)n);
+    scored_t *mine = (scored_t *)malloc(sizeof(scored_t) * (size_t)nc);
+    if (!p || !a || !all || !mine) {
+        free(p);
+        free(a);
+        free(all);
+        free(mine);
+        return OR_ENOMEM;
+    }
+    group_proxy(q, dt, H, D, h, i0, m, p);
+    for (int64_t c = 0; c < n; ++c) {
+        all[c].score = score_of(p, k, dt, ((size_t)c * H + h) * D, D);
+        all[c].idx = (int32_t)c;
+    }
+    qsort(all, (size_t)n, sizeof(scored_t), better_first);
+    for (int d = 0; d < D; ++d)
+        a[d] = load_elem(q, dt, ((size_t)i * H + h) * D + d);
+    for (int64_t c = 0; c < nc; ++c) {
+        int32_t key = all[c].idx;
+        mine[c].score = score_of(a, k, dt, ((size_t)key * H + h) * D, D);
+        mine[c].idx = key;
+    }
+    qsort(mine, (size_t)nc, sizeof(scored_t), better_first);
+    write_row(out_idx, out_score, row_off, top_k, mine, min64(top_k, nc));
+    free(p);
+    free(a);
+    free(all);
+    free(mine);
+    return OR_OK;
+}
+
 /* The dense indexer row of query i, head h: rank every key of [0, max(i,1))
  * by q_i's own score (the DSA indexer the pages compare against). */
 static int dense_row(const void *q, const void *k, int dt, int H, int D,
@@ -314,10 +370,21 @@ int oracle_prefill(const void *q, const void *k, int dt, int64_t S, int32_t H,
     if (rc)
         return rc;
     int64_t K = oracle_candidate_count(top_k, candidate_ratio);
-    if (K < 0 || g < 1 || !out_idx || (mode != OR_REFINE && mode != OR_REUSE))
+    if (K < 0 || g < 1 || !out_idx ||
+        (mode != OR_REFINE && mode != OR_REUSE && mode != OR_REFINE_LITERAL))
         return OR_EINVAL;
     if (h_begin < 0 || h_end > H || h_begin > h_end)
         return OR_EINVAL;
+    if (mode == OR_REFINE_LITERAL) {
+        for (int32_t h = h_begin; h < h_end; ++h)
+            for (int64_t i = 0; i < S; ++i) {
+                rc = literal_row(q, k, dt, S, H, D, top_k, K, g, h, i, out_idx, out_score,
+                                 ((size_t)i * H + h) * (size_t)top_k);
+                if (rc)
+                    return rc;
+            }
+        return OR_OK;
+    }
     for (int32_t h = h_begin; h < h_end; ++h) {
         for (int64_t i0 = 0; i0 < S; i0 += g) {
             int64_t m = min64(g, S - i0);
@@ -345,8 +412,19 @@ int oracle_prefill_rows(const void *q, const void *k, int dt, int64_t S,
         return rc;
     int64_t K = oracle_candidate_count(top_k, candidate_ratio);
     if (K < 0 || g < 1 || !out_idx || !rows_i || !rows_h || n_rows < 0 ||
-        (mode != OR_REFINE && mode != OR_REUSE))
+        (mode != OR_REFINE && mode != OR_REUSE && mode != OR_REFINE_LITERAL))
         return OR_EINVAL;
+    if (mode == OR_REFINE_LITERAL) {
+        for (int64_t r = 0; r < n_rows; ++r) {
+            if (rows_i[r] < 0 || rows_i[r] >= S || rows_h[r] < 0 || rows_h[r] >= H)
+                return OR_EINVAL;
+            rc = literal_row(q, k, dt, S, H, D, top_k, K, g, rows_h[r], rows_i[r], out_idx, out_score,
+                             (size_t)r * top_k);
+            if (rc)
+                return rc;
+        }
+        return OR_OK;
+    }
     int32_t *tmp_idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)g * H * top_k);
     float *tmp_sc = (float *)malloc(sizeof(float) * (size_t)g * H * top_k);
     if (!tmp_idx || !tmp_sc) {

@@ -110,3 +110,25 @@ def dense_exact(q: np.ndarray, k: np.ndarray, top_k: int):
                 idx[i, h, t] = c
                 sc[i, h, t] = s
     return idx, sc
+
+
+def literal_exact(q: np.ndarray, k: np.ndarray, top_k: int, g: int, K: int):
+    """The literal per-position Refine by exact arithmetic: position i >= 1
+    scans keys [0, i) with its group's proxy, keeps its own first min(K, i)
+    and re-scores them with q_i; position 0 is all padding."""
+    bf16 = q.dtype == np.uint16
+    qv, kv = values(q), values(k)
+    S, H, D = q.shape
+    idx = np.full((S, H, top_k), -1, np.int64)
+    sc = np.full((S, H, top_k), -np.inf, np.float64)
+    for h in range(H):
+        for i in range(1, S):
+            i0 = (i // g) * g
+            p = proxy_exact(qv, i0, min(g, S - i0), h, bf16)
+            cand = topk_exact([(dot_f32(p, kv, c, h), c) for c in range(i)], K)
+            qi = [Fraction(float(x)) for x in qv[i, h]]
+            row = topk_exact([(dot_f32(qi, kv, c, h), c) for _, c in cand], top_k)
+            for t, (s, c) in enumerate(row):
+                idx[i, h, t] = c
+                sc[i, h, t] = s
+    return idx, sc

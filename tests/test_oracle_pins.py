@@ -370,6 +370,97 @@ def test_reuse_matches_pages_loop_float64():
     np.testing.assert_array_equal(np.where(idx < 0, 0, idx), want)
 
 
+# ------------------------------- literal per-position Refine (comparison)
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("S,H,D,top_k,g,ratio", [
+    (24, 2, 4, 3, 4, 2.0),
+    (19, 1, 8, 4, 4, 1.5),   # ragged last group
+    (12, 1, 4, 8, 8, 3.0),   # top_k larger than early prefixes
+])
+def test_literal_refine_matches_exact_bruteforce(dtype, S, H, D, top_k, g, ratio):
+    q = syn.integers((S, H, D), 41 + S, 3, dtype)
+    k = syn.integers((S, H, D), 43 + S, 3, dtype)
+    K = oracle.candidate_count(top_k, ratio)
+    want_idx, want_sc = exact_ref.literal_exact(q, k, top_k, g, K)
+    got_idx, got_sc = oracle.prefill(q, k, top_k, g, ratio, "refine_literal")
+    np.testing.assert_array_equal(got_idx, want_idx)
+    np.testing.assert_array_equal(got_sc.astype(np.float64), want_sc)
+
+
+def test_literal_refine_identities():
+    """Position i of the literal loop scans [0, i): at a group's first
+    member (i = j*g, j >= 1) that is the one-scan prefix, so the rows agree;
+    with g = 1 the proxy is q_i itself and every row i >= 1 is the dense row;
+    row 0 is padding."""
+    S, H, D, top_k, g = 96, 2, 16, 5, 8
+    q = syn.gaussian((S, H, D), 51, "f32")
+    k = syn.gaussian((S, H, D), 52, "f32")
+    lit, lsc = oracle.prefill(q, k, top_k, g, 2.0, "refine_literal")
+    one, osc = oracle.prefill(q, k, top_k, g, 2.0, "refine")
+    firsts = np.arange(g, S, g)
+    np.testing.assert_array_equal(lit[firsts], one[firsts])
+    np.testing.assert_array_equal(lsc[firsts], osc[firsts])
+    assert (lit[0] == -1).all() and np.isneginf(lsc[0]).all()
+    lit1, _ = oracle.prefill(q, k, top_k, 1, 2.0, "refine_literal")
+    dense, _ = oracle.dense(q, k, top_k)
+    np.testing.assert_array_equal(lit1[1:], dense[1:])
+    # K covering every prefix: the candidate set is the whole prefix
+    litK, _ = oracle.prefill(q, k, 2, g, float(S), "refine_literal")
+    denseK, _ = oracle.dense(q, k, 2)
+    np.testing.assert_array_equal(litK[1:], denseK[1:])
+
+
+def pages_refine_torch(q, k, top_k, group_size, candidate_ratio):
+    """The pivot_refine loop of "Show Me The Code", re-expressed in torch
+    float64: per head, per group: proxy = mean of the group; per position pos
+    > 0: scan k[:pos], top-K, re-score with q[pos], top-k. Zero-initialised
+    output as on the pages."""
+    import torch
+    qv = torch.from_numpy(exact_ref.values(q))
+    kv = torch.from_numpy(exact_ref.values(k))
+    S, H, D = q.shape
+    K = int(top_k * candidate_ratio)
+    out = torch.zeros(S, H, top_k, dtype=torch.long)
+    for h in range(H):
+        for g_start in range(0, S, group_size):
+            g_end = min(g_start + group_size, S)
+            proxy = qv[g_start:g_end, h].mean(dim=0)
+            for pos in range(g_start, g_end):
+                if pos == 0:
+                    continue
+                n_take = min(K, pos)
+                cand = torch.topk(kv[:pos, h] @ proxy, n_take).indices
+                kk = min(top_k, n_take)
+                best = torch.topk(kv[cand, h] @ qv[pos, h], kk).indices
+                out[pos, h, :kk] = cand[best]
+    return out.numpy()
+
+
+def test_literal_refine_matches_pages_loop_float64():
+    """Tie-free fp32 inputs, power-of-two groups: the pages' float64 loop and
+    the oracle's literal mode agree on every row once -1 padding is mapped
+    to the pages' 0."""
+    S, H, D, top_k, g = 96, 2, 16, 6, 8
+    q = syn.integers((S, H, D), 121, 8, "f32")
+    k = syn.gaussian((S, H, D), 122, "f32")
+    idx, _ = oracle.prefill(q, k, top_k, g, 2.0, "refine_literal")
+    want = pages_refine_torch(q, k, top_k, g, 2.0)
+    np.testing.assert_array_equal(np.where(idx < 0, 0, idx), want)
+
+
+def test_literal_rows_api_matches_full():
+    S, H, D, top_k, g = 64, 3, 8, 4, 4
+    q = syn.gaussian((S, H, D), 61, "bf16")
+    k = syn.gaussian((S, H, D), 62, "bf16")
+    full, fsc = oracle.prefill(q, k, top_k, g, 2.0, "refine_literal")
+    ri = np.array([0, 1, 5, 17, 63], np.int64)
+    rh = np.array([0, 2, 1, 0, 2], np.int32)
+    idx, sc = oracle.prefill_rows(q, k, ri, rh, top_k, g, 2.0, "refine_literal")
+    np.testing.assert_array_equal(idx, full[ri, rh])
+    np.testing.assert_array_equal(sc, fsc[ri, rh])
+
+
 # ----------------------------------------------------------- decode path
 
 @pytest.mark.parametrize("mode", ["refine", "reuse"])
