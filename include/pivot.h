@@ -72,7 +72,13 @@ typedef enum {
 } pivot_status;
 
 typedef enum { PIVOT_F32 = 0, PIVOT_BF16 = 1 } pivot_dtype;
-typedef enum { PIVOT_REFINE = 0, PIVOT_REUSE = 1 } pivot_mode;
+/* PIVOT_REFINE_LITERAL (prefill only, for comparison): the per-position
+ * rescan that the pivot_refine code of "PIVOT Explained", section "Show Me
+ * The Code", carries out as written -- position i >= 1 scans keys [0, i)
+ * with its group's proxy, takes its own min(K, i) candidates and re-scores
+ * them with q_i; position 0 (skipped by that code) is all padding. It does g
+ * scans per group where PIVOT_REFINE does one. */
+typedef enum { PIVOT_REFINE = 0, PIVOT_REUSE = 1, PIVOT_REFINE_LITERAL = 2 } pivot_mode;
 
 /* Human-readable text of a status code (static storage). */
 const char *pivot_status_string(int status);
@@ -94,7 +100,7 @@ size_t pivot_prefill_workspace_bytes(int64_t S, int32_t H, int32_t D,
  *   q, k      device (S, H, D) of `dtype` (PIVOT_F32 or PIVOT_BF16)
  *   S >= 1, H >= 1, D in {64, 128}, 1 <= top_k <= 4096, g >= 1,
  *   K = floor(top_k * candidate_ratio) with top_k <= K <= 4096,
- *   mode      PIVOT_REFINE or PIVOT_REUSE
+ *   mode      PIVOT_REFINE, PIVOT_REUSE or PIVOT_REFINE_LITERAL
  *   out_idx   device (S, H, top_k) int32, written completely
  *   out_score device (S, H, top_k) float32 or NULL
  *   workspace device scratch, workspace_bytes as described above

@@ -70,7 +70,10 @@ def test_workspace_sizes(pv):
     assert full - one == 63 * (two - one)
     assert f(0, 1, 128, 64, 8, 2.0, 0, 1) == 0        # S < 1
     assert f(64, 1, 96, 8, 8, 2.0, 0, 1) == 0         # D unsupported
-    assert f(64, 1, 64, 8, 8, 2.0, 2, 1) == 0         # bad mode
+    assert f(64, 1, 64, 8, 8, 2.0, 3, 1) == 0         # bad mode
+    # the literal per-position Refine scans one row per position: its
+    # workspace grows like g = 1 Refine's, not like one row per group
+    assert f(4096, 1, 128, 64, 8, 2.0, 2, 1) > f(4096, 1, 128, 64, 8, 2.0, 0, 1)
     assert f(64, 1, 64, 4097, 8, 1.0, 0, 1) == 0      # top_k above 4096
     assert f(64, 1, 64, 2048, 8, 2.5, 0, 1) == 0      # K above 4096
     assert pv.lib.dense_index_workspace_bytes(1024, 8, 64, 64, 0) > 0

@@ -272,3 +272,31 @@ def test_tiny_workload_gaussian_tolerant(pv, mode):
                 if e:
                     errs.append((i, h, e))
     assert not errs, errs[:5]
+
+
+# ------------------------------- literal per-position Refine (comparison)
+
+@pytest.mark.parametrize("S,H,D,top_k,g,ratio,dtype", [
+    (1024, 8, 64, 64, 8, 2.0, "f32"),
+    (700, 3, 128, 16, 8, 2.0, "bf16"),
+    (600, 2, 64, 24, 3, 1.5, "bf16"),
+    (2100, 1, 128, 100, 8, 2.0, "bf16"),
+])
+def test_literal_refine_bit_exact_integer_inputs(pv, S, H, D, top_k, g, ratio, dtype):
+    """The per-position rescan (one scan row per position, the group's proxy)
+    against the oracle's literal mode, with scores and index-only."""
+    print(f"\n[literal exact] S={S} H={H} D={D} k={top_k} g={g} r={ratio} {dtype}", flush=True)
+    a = 8 if dtype == "f32" else 4
+    q = syn.integers((S, H, D), 7400 + S + g, a, dtype)
+    k = syn.integers((S, H, D), 8400 + S + g, a, dtype)
+    gi, gs = run_prefill(pv, q, k, top_k, g, ratio, "refine_literal")
+    oi, os_ = oracle.prefill(q, k, top_k, g, ratio, "refine_literal")
+    np.testing.assert_array_equal(gi, oi)
+    if dtype == "bf16" or (S % g == 0 and (g & (g - 1)) == 0):
+        np.testing.assert_array_equal(gs, os_)
+    else:
+        np.testing.assert_allclose(gs, os_, rtol=4 * 2.0 ** -23, atol=0)
+    only = pv.index_prefill(dev_tensor(q), dev_tensor(k), top_k=top_k, g=g, candidate_ratio=ratio,
+                            mode="refine_literal")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(parity.to_host(only), oi)

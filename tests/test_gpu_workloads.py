@@ -190,3 +190,49 @@ def test_decode_workload_tolerant(pv, mode, g):
                 errs.append((b, t, e))
         off += n
     assert not errs, errs[:5]
+
+
+def test_literal_refine_long_distribution_tolerant(pv):
+    """The per-position rescan at S=16384, H=8 on the long-workload
+    distribution (AR(1) queries, Pareto-norm keys, top_k=2048, K=4096):
+    sampled rows against the oracle, tie-tolerant; the index-only launch
+    equals the scored one in every row."""
+    S, H, g = 16384, 8, 8
+    print(f"\n[literal] S={S} H={H} g={g}", flush=True)
+    cfg = syn.long_prefill_device(DEV, S=S, H=H, g=g, seed=1007)
+    q, k, top_k = cfg["q"], cfg["k"], cfg["top_k"]
+    D = q.shape[2]
+    idx, sc = pv.index_prefill(q, k, top_k=top_k, g=g, mode="refine_literal", return_scores=True)
+    only = pv.index_prefill(q, k, top_k=top_k, g=g, mode="refine_literal")
+    torch.cuda.synchronize()
+    bad = torch.nonzero(~torch.eq(idx, only).all(dim=2))[:5].tolist()
+    assert not bad, bad
+    rng = np.random.default_rng(8)
+    ri = np.concatenate([rng.integers(0, S, 12), [0, 1, 9, 4097, S - 1]])
+    rh = rng.integers(0, H, len(ri)).astype(np.int32)
+    ri_d = torch.from_numpy(ri).to(DEV)
+    rh_d = torch.from_numpy(rh.astype(np.int64)).to(DEV)
+    gi = idx[ri_d, rh_d].cpu().numpy()
+    gs = sc[ri_d, rh_d].cpu().numpy()
+    del idx, sc, only
+    qh = syn.bf16_tensor_to_bits(q)
+    kh = syn.bf16_tensor_to_bits(k)
+    oi, os_ = oracle.prefill_rows(qh, kh, ri, rh, top_k, g, 2.0, "refine_literal")
+    errs = []
+    for r in range(len(ri)):
+        i, h = int(ri[r]), int(rh[r])
+        if i == 0:
+            assert (gi[r] == -1).all(), gi[r][:4]
+            continue
+        j = i // g
+        proxy = oracle.proxy(qh, g, h, j).astype(np.float64)
+        kv = syn.bf16_bits_to_f32(kh[:i, h]).astype(np.float64)
+        ps = kv @ proxy
+        order = np.lexsort((np.arange(i), -ps))
+        cand = order[:min(4096, i)]
+        avec = syn.bf16_bits_to_f32(qh[i, h]).astype(np.float64)
+        e = parity.tolerant_row_match(gi[r], gs[r], oi[r], os_[r], avec, kh, h, D,
+                                      cand_idx=cand, cand_sc=ps[cand], proxy=proxy)
+        if e:
+            errs.append((i, h, e))
+    assert not errs, errs[:5]

@@ -25,8 +25,10 @@ LIB_PATH = os.path.join(_HERE, "libpivot.so")
 
 PIVOT_OK, PIVOT_EINVAL, PIVOT_EUNSUPPORTED, PIVOT_EWORKSPACE, PIVOT_EHIP = 0, -1, -2, -3, -4
 PIVOT_F32, PIVOT_BF16 = 0, 1
-PIVOT_REFINE, PIVOT_REUSE = 0, 1
-_MODES = {"refine": PIVOT_REFINE, "reuse": PIVOT_REUSE}
+PIVOT_REFINE, PIVOT_REUSE, PIVOT_REFINE_LITERAL = 0, 1, 2
+# "refine_literal": the per-position-rescan Refine of the pages' pivot_refine
+# code, prefill only (comparison)
+_MODES = {"refine": PIVOT_REFINE, "reuse": PIVOT_REUSE, "refine_literal": PIVOT_REFINE_LITERAL}
 
 #: every symbol include/pivot.h declares
 EXPORTED = (

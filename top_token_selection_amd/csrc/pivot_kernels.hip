@@ -94,12 +94,12 @@ __device__ __forceinline__ int64_t virt_count(int64_t n, int kstride, int koff) 
 
 template <typename T>
 __global__ void k_proxy(const T *__restrict__ q, int64_t S, int H, int D, int g,
-                        int h0, int Hc, int64_t G, T *__restrict__ P) {
+                        int h0, int Hc, int64_t G, int rep, T *__restrict__ P) {
     const int64_t total = (int64_t)Hc * G * D;
     for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
          t += (int64_t)gridDim.x * blockDim.x) {
         const int d = (int)(t % D);
-        const int64_t j = (t / D) % G;
+        const int64_t j = (t / D) % G / rep;  // rep proxy rows per group
         const int hl = (int)(t / ((int64_t)D * G));
         const int64_t i0 = j * g;
         const int64_t m = min((int64_t)g, S - i0);
@@ -881,6 +881,7 @@ struct RefParams {
     int top_k;
     int reg_bytes;         // per-wave LDS region
     int ref_cap;           // staged entries of the fused select (top_k + slack)
+    int pad_first;         // literal per-position Refine: position 0 is padding
     int32_t *out_idx;
     float *out_score;
 };
@@ -1406,6 +1407,15 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     // addresses and counts derived from it
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int nthreads = p.nqw * 64;
+    if (p.pad_first && qrow0 == 0) {
+        // literal per-position Refine: no key precedes position 0
+        const int64_t base = (int64_t)h * p.top_k;
+        for (int c = tid; c < p.top_k; c += nthreads) {
+            p.out_idx[base + c] = -1;
+            if (p.out_score) p.out_score[base + c] = -INFINITY;
+        }
+        return;
+    }
 
     uint32_t *cl = (uint32_t *)smem;                    // candidate list (Kc)
     unsigned char *regs = smem + ((p.Kc * 4 + 15) & ~15);
@@ -1596,6 +1606,10 @@ struct Plan {
     int64_t S;
     int H, D, top_k, g, mode, dtype;
     bool dense;
+    // literal per-position Refine: one scan row per position (g above is 1,
+    // G is S), each row's proxy the mean of its group of gp positions
+    bool literal;
+    int gp;
     int64_t K, Ksel, G, n_max;
     int kstride;
     int64_t rsel;
@@ -1630,7 +1644,8 @@ int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio,
               int dtype, bool dense) {
     if (S < 1 || S > (int64_t)INT32_MAX - 1 || H < 1 || g < 1) return PIVOT_EINVAL;
     if (dtype != PIVOT_F32 && dtype != PIVOT_BF16) return PIVOT_EINVAL;
-    if (mode != PIVOT_REFINE && mode != PIVOT_REUSE) return PIVOT_EINVAL;
+    if (mode != PIVOT_REFINE && mode != PIVOT_REUSE && !(mode == PIVOT_REFINE_LITERAL && !dense))
+        return PIVOT_EINVAL;
     if (top_k < 1) return PIVOT_EINVAL;
     int64_t K = top_k;
     if (!dense) {
@@ -1643,8 +1658,10 @@ int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio,
     pl.H = H;
     pl.D = D;
     pl.top_k = top_k;
-    pl.g = dense ? 1 : g;
-    pl.mode = dense ? PIVOT_REUSE : mode;
+    pl.literal = mode == PIVOT_REFINE_LITERAL;
+    pl.gp = g;
+    pl.g = dense || pl.literal ? 1 : g;
+    pl.mode = dense ? PIVOT_REUSE : (pl.literal ? PIVOT_REFINE : mode);
     pl.dtype = dtype;
     pl.dense = dense;
     pl.K = K;
@@ -1805,8 +1822,8 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             const int64_t total = rows * D;
             const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
             StageTimer tm(ST_PROXY, st);
-            hipLaunchKernelGGL((k_proxy<T>), dim3(blocks), dim3(256), 0, st, q, pl.S, pl.H, pl.D, pl.g,
-                               h0, Hc, pl.G, P);
+            hipLaunchKernelGGL((k_proxy<T>), dim3(blocks), dim3(256), 0, st, q, pl.S, pl.H, pl.D, pl.gp,
+                               h0, Hc, pl.G, pl.literal ? pl.gp : 1, P);
             HIP_TRY(hipGetLastError());
             sp.P = P;
             sp.p_row = D;
@@ -1939,6 +1956,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             rp.top_k = pl.top_k;
             rp.reg_bytes = lay.reg_bytes;
             rp.ref_cap = lay.cap;
+            rp.pad_first = pl.literal ? 1 : 0;
             rp.out_idx = out_idx;
             rp.out_score = out_score;
             const size_t lds = lay.lds;
@@ -2037,7 +2055,7 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
         const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
         StageTimer tm(ST_PROXY, st);
         hipLaunchKernelGGL((k_proxy<T>), dim3(blocks), dim3(256), 0, st, q, (int64_t)dp.B * dp.g, dp.H,
-                           dp.D, dp.g, 0, dp.H, (int64_t)dp.B, P);
+                           dp.D, dp.g, 0, dp.H, (int64_t)dp.B, 1, P);
         HIP_TRY(hipGetLastError());
     }
     {
