@@ -150,6 +150,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip timing the dense indexer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-literal", action="store_true",
+                    help="skip the literal per-position Refine comparison (8 heads of the S=65536 workload)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip timing the other workloads (tiny, S=16384 integer, S=131072 long)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
@@ -286,6 +288,43 @@ def main():
         recall = {"refine": rec(ref_rows), "reuse": rec(reu_rows), "rows": int(args.recall_rows),
                   "sample": "positions uniform in [g, S), heads uniform, seed 7", "oracle_s": dense_s}
         log(f"recall@{top_k}: {recall}")
+
+    # ------------------------------- literal per-position Refine (comparison)
+    literal = None
+    if not args.no_literal:
+        Hl = 8
+        ql = q[:, :Hl].contiguous()
+        kl = k[:, :Hl].contiguous()
+        lout = torch.empty((S, Hl, top_k), dtype=torch.int32, device=dev)
+        lws = torch.empty(pv.prefill_workspace_bytes(S, Hl, D, top_k, g, ratio, "refine_literal", torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+
+        def lit():
+            pv.index_prefill(ql, kl, top_k, g, ratio, "refine_literal", workspace=lws, out=lout)
+        log(f"timing the literal per-position Refine on {Hl} heads")
+        lms, _, lst, _ = time_calls(lit, max(1, args.steps // 2), 1, pv)
+        literal = {"heads": Hl, "ms_per_step": lms, "queries_per_s": S * Hl / (lms / 1e3), "stage_ms": lst}
+        # recall@top_k on 512 rows of these heads against the dense indexer (GPU)
+        if args.recall_rows > 0:
+            lrng = np.random.default_rng(9)
+            li = torch.from_numpy(lrng.integers(g, S, 512)).to(dev)
+            lh = torch.from_numpy(lrng.integers(0, Hl, 512)).to(dev)
+            lit_rows = lout[li, lh].cpu().numpy()
+            pv.index_prefill(ql, kl, top_k, g, ratio, "refine", workspace=lws, out=lout)
+            one_rows = lout[li, lh].cpu().numpy()
+            del lws
+            pv.dense_index(ql, kl, top_k, out=lout, max_workspace_bytes=48 << 30)
+            den_rows = lout[li, lh].cpu().numpy()
+
+            def rec3(a_rows):
+                return float(np.mean([len(set(a[a >= 0].tolist()) & set(b[b >= 0].tolist()))
+                                      / max(1, int((b >= 0).sum())) for a, b in zip(a_rows, den_rows)]))
+            literal["recall"] = {"literal": rec3(lit_rows), "refine": rec3(one_rows), "rows": 512,
+                                 "against": "dense indexer (GPU)",
+                                 "sample": f"positions uniform in [g, S), heads uniform in [0, {Hl}), seed 9"}
+        log(f"literal per-position Refine: {lms:.2f} ms/step on {Hl} heads; {literal.get('recall')}")
+        del ql, kl, lout
+        torch.cuda.empty_cache()
 
     # ---------------------------------------------------------- CPU oracle
     cpu = None
@@ -451,6 +490,7 @@ def main():
                                          if dense_ms else None),
             "decode": decode,
             "recall": recall,
+            "literal_refine": literal,
             "configs": configs,
             "host": {"cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count(),
                      "gpu": torch.cuda.get_device_name(dev)},
