@@ -69,6 +69,8 @@ def _load():
     lib.oracle_dense_rows.restype = ci
     lib.oracle_decode.argtypes = [vp, vp, ci, vp, i32, i32, i32, i32, i32, f64, ci, i32, i32, vp, vp]
     lib.oracle_decode.restype = ci
+    lib.oracle_sparse_attention.argtypes = [vp, vp, vp, ci, i64, i32, i32, vp, i32, f64, vp]
+    lib.oracle_sparse_attention.restype = ci
     _lib = lib
     return lib
 
@@ -217,3 +219,21 @@ def decode(q, k_cache, ctx_lens, g, top_k=64, candidate_ratio=2.0, mode="refine"
                                  candidate_ratio, MODES[mode], hb, he, _ptr(idx), _ptr(sc)),
            "oracle_decode")
     return idx, sc
+
+
+def sparse_attention(q, k, v, idx, scale=None):
+    """Downstream sparse attention over the indices: (S, H, D) float32.
+    scale defaults to D**-0.5 (the pages' demo)."""
+    q, k, dt = _prep(q, k)
+    v = np.ascontiguousarray(v)
+    if v.dtype != q.dtype or v.shape != q.shape:
+        raise ValueError("v must match q and k")
+    idx = np.ascontiguousarray(idx, np.int32)
+    S, H, D = q.shape
+    if idx.ndim != 3 or idx.shape[:2] != (S, H):
+        raise ValueError("idx must be (S, H, top_k)")
+    out = np.empty((S, H, D), np.float32)
+    sc = float(D) ** -0.5 if scale is None else float(scale)
+    _check(_load().oracle_sparse_attention(_ptr(q), _ptr(k), _ptr(v), dt, S, H, D, _ptr(idx), idx.shape[2],
+                                           sc, _ptr(out)), "oracle_sparse_attention")
+    return out

@@ -620,3 +620,71 @@ int oracle_decode(const void *q, const void *k_cache, int dt,
     }
     return OR_OK;
 }
+
+/* ---------------------------------------------- downstream sparse attention */
+
+/* The attention the pages run on the indices ("Show Me The Code", the quick
+ * test): for query i, head h, over the valid entries c of idx[i, h, :]
+ * (0 <= c < S; -1 and anything else is padding),
+ *   w_c = exp(scale * q_i . k_c) / sum_c' exp(scale * q_i . k_c'),
+ *   out[i, h, :] = sum_c w_c * v_c,
+ * in double (the exponent is shifted by the row maximum, which leaves the
+ * quotient unchanged), rounded once to float. A row without a valid entry
+ * is zero. Repeated entries count once each, as in the pages' loop. */
+int oracle_sparse_attention(const void *q, const void *k, const void *v, int dt,
+                            int64_t S, int32_t H, int32_t D, const int32_t *idx,
+                            int32_t top_k, double scale, float *out)
+{
+    if (!q || !k || !v || !idx || !out || S < 1 || H < 1 || D < 1 || top_k < 1)
+        return OR_EINVAL;
+    if (dt != OR_F32 && dt != OR_BF16)
+        return OR_EINVAL;
+    double *s = (double *)malloc(sizeof(double) * (size_t)top_k);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!s || !acc) {
+        free(s);
+        free(acc);
+        return OR_ENOMEM;
+    }
+    for (int64_t i = 0; i < S; ++i) {
+        for (int32_t h = 0; h < H; ++h) {
+            const int32_t *row = idx + ((size_t)i * H + h) * (size_t)top_k;
+            double mx = -INFINITY;
+            int any = 0;
+            for (int t = 0; t < top_k; ++t) {
+                int32_t c = row[t];
+                s[t] = -INFINITY;
+                if (c < 0 || c >= S)
+                    continue;
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d)
+                    dot += (double)load_elem(q, dt, ((size_t)i * H + h) * D + d) *
+                           (double)load_elem(k, dt, ((size_t)c * H + h) * D + d);
+                s[t] = scale * dot;
+                if (s[t] > mx)
+                    mx = s[t];
+                any = 1;
+            }
+            for (int d = 0; d < D; ++d)
+                acc[d] = 0.0;
+            double den = 0.0;
+            if (any) {
+                for (int t = 0; t < top_k; ++t) {
+                    int32_t c = row[t];
+                    if (c < 0 || c >= S)
+                        continue;
+                    double e = exp(s[t] - mx);
+                    den += e;
+                    for (int d = 0; d < D; ++d)
+                        acc[d] += e * (double)load_elem(v, dt, ((size_t)c * H + h) * D + d);
+                }
+            }
+            float *o = out + ((size_t)i * H + h) * (size_t)D;
+            for (int d = 0; d < D; ++d)
+                o[d] = any ? (float)(acc[d] / den) : 0.0f;
+        }
+    }
+    free(s);
+    free(acc);
+    return OR_OK;
+}

@@ -517,3 +517,94 @@ def test_groups_api_matches_full():
             np.testing.assert_array_equal(gi[t, :m], full[i0:i0 + m, heads[t]])
             np.testing.assert_array_equal(gs[t, :m], fs[i0:i0 + m, heads[t]])
             assert (gi[t, m:] == -1).all()
+
+
+# ------------------------------------------- downstream sparse attention
+
+def _att_inputs(S=40, H=2, D=8, seed=71, dtype="f32"):
+    q = syn.gaussian((S, H, D), seed, dtype)
+    k = syn.gaussian((S, H, D), seed + 1, dtype)
+    v = syn.gaussian((S, H, D), seed + 2, dtype)
+    return q, k, v
+
+
+def test_attention_zero_query_is_the_mean_of_v():
+    """q = 0: every weight is equal, the output is the mean of V[idx]."""
+    q, k, v = _att_inputs()
+    q[:] = 0
+    rng = np.random.default_rng(3)
+    idx = np.stack([np.stack([rng.choice(40, 5, replace=False) for _ in range(2)]) for _ in range(40)]).astype(np.int32)
+    out = oracle.sparse_attention(q, k, v, idx)
+    want = np.stack([[v[idx[i, h], h].astype(np.float64).mean(axis=0) for h in range(2)] for i in range(40)])
+    np.testing.assert_allclose(out, want, rtol=1e-6, atol=1e-7)
+
+
+def test_attention_single_index_returns_that_value_row():
+    q, k, v = _att_inputs(dtype="bf16")
+    idx = np.full((40, 2, 4), -1, np.int32)
+    idx[:, :, 2] = (np.arange(40) * 7 % 40)[:, None]
+    out = oracle.sparse_attention(q, k, v, idx)
+    vv = exact_ref.values(v)
+    want = np.stack([[vv[(i * 7) % 40, h] for h in range(2)] for i in range(40)])
+    np.testing.assert_array_equal(out, want.astype(np.float32))
+
+
+def test_attention_padding_order_and_empty_rows():
+    """-1 and out-of-range entries are padding; the order of the entries does
+    not matter (up to rounding); a row without entries is zero."""
+    q, k, v = _att_inputs()
+    rng = np.random.default_rng(5)
+    base = np.stack([np.stack([rng.choice(40, 6, replace=False) for _ in range(2)]) for _ in range(40)]).astype(np.int32)
+    a = oracle.sparse_attention(q, k, v, base)
+    padded = np.concatenate([base[:, :, :3], np.full((40, 2, 2), -1, np.int32), base[:, :, 3:],
+                             np.full((40, 2, 1), 40, np.int32)], axis=2)
+    np.testing.assert_array_equal(oracle.sparse_attention(q, k, v, padded), a)
+    perm = base[:, :, ::-1].copy()
+    np.testing.assert_allclose(oracle.sparse_attention(q, k, v, perm), a, rtol=1e-6, atol=1e-7)
+    empty = np.full((40, 2, 3), -1, np.int32)
+    assert (oracle.sparse_attention(q, k, v, empty) == 0).all()
+
+
+def test_attention_two_keys_is_a_logistic_weight():
+    """Two entries: w_1 = 1 / (1 + exp(-scale (s_1 - s_2)))."""
+    q, k, v = _att_inputs(S=16, H=1, D=4)
+    idx = np.zeros((16, 1, 2), np.int32)
+    idx[:, 0, 0] = 3
+    idx[:, 0, 1] = 11
+    out = oracle.sparse_attention(q, k, v, idx)
+    qv, kv, vv = (a.astype(np.float64) for a in (q, k, v))
+    for i in range(16):
+        d = (qv[i, 0] @ kv[3, 0] - qv[i, 0] @ kv[11, 0]) * 0.5
+        w = 1.0 / (1.0 + np.exp(-d))
+        np.testing.assert_allclose(out[i, 0], w * vv[3, 0] + (1 - w) * vv[11, 0], rtol=1e-6, atol=1e-7)
+
+
+def test_attention_large_scale_selects_the_argmax():
+    q, k, v = _att_inputs(S=32, H=1, D=8)
+    rng = np.random.default_rng(9)
+    idx = np.stack([rng.choice(32, 8, replace=False) for _ in range(32)])[:, None, :].astype(np.int32)
+    out = oracle.sparse_attention(q, k, v, idx, scale=1e6)
+    qv, kv = q.astype(np.float64), k.astype(np.float64)
+    for i in range(32):
+        s = kv[idx[i, 0], 0] @ qv[i, 0]
+        np.testing.assert_array_equal(out[i, 0], v[idx[i, 0, np.argmax(s)], 0])
+
+
+def test_attention_matches_pages_demo_loop_float64():
+    """The pages' quick-test attention loop in torch float64 (positions >= 1;
+    full index rows, no padding)."""
+    import torch
+    import torch.nn.functional as F
+    S, H, D, top_k = 64, 2, 16, 6
+    q, k, v = _att_inputs(S, H, D, 81)
+    rng = np.random.default_rng(4)
+    idx = np.stack([np.stack([rng.choice(S, top_k, replace=False) for _ in range(H)]) for _ in range(S)]).astype(np.int32)
+    out = oracle.sparse_attention(q, k, v, idx)
+    qt, kt, vt = (torch.from_numpy(a.astype(np.float64)) for a in (q, k, v))
+    it = torch.from_numpy(idx.astype(np.int64))
+    scale = D ** -0.5
+    for pos in range(1, S):
+        for h in range(H):
+            sel = it[pos, h]
+            w = F.softmax(qt[pos, h] @ kt[sel, h].T * scale, dim=-1)
+            np.testing.assert_allclose(out[pos, h], (w @ vt[sel, h]).numpy(), rtol=1e-6, atol=1e-7)
