@@ -80,6 +80,23 @@ typedef enum { PIVOT_F32 = 0, PIVOT_BF16 = 1 } pivot_dtype;
  * scans per group where PIVOT_REFINE does one. */
 typedef enum { PIVOT_REFINE = 0, PIVOT_REUSE = 1, PIVOT_REFINE_LITERAL = 2 } pivot_mode;
 
+/* Downstream sparse attention over indexer rows -- the attention the pages
+ * run on the indices ("PIVOT Explained", "Show Me The Code", quick test):
+ *   out[i, h, :] = sum_c w_c v[c, h, :],
+ *   w_c = exp(scale q[i,h,:].k[c,h,:]) / sum_c' exp(scale q[i,h,:].k[c',h,:])
+ * over the entries c of idx[i, h, :] that lie in [0, S) (-1 and anything
+ * else is padding; repeated entries count each time); a row with no such
+ * entry is zero. Scores, softmax and the weighted sum run in float32.
+ *   q, k, v  device (S, H, D) of `dtype`, D in {64, 128}
+ *   idx      device (S, H, top_k) int32 (an indexer's output, or any rows)
+ *   scale    finite; the pages use D^-0.5
+ *   out      device (S, H, D) float32, written completely
+ * Errors as above; no workspace. */
+int pivot_sparse_attention(const void *q, const void *k, const void *v,
+                           int32_t dtype, int64_t S, int32_t H, int32_t D,
+                           const int32_t *idx, int32_t top_k, float scale,
+                           float *out, void *stream);
+
 /* Human-readable text of a status code (static storage). */
 const char *pivot_status_string(int status);
 

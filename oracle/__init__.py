@@ -71,6 +71,8 @@ def _load():
     lib.oracle_decode.restype = ci
     lib.oracle_sparse_attention.argtypes = [vp, vp, vp, ci, i64, i32, i32, vp, i32, f64, vp]
     lib.oracle_sparse_attention.restype = ci
+    lib.oracle_sparse_attention_rows.argtypes = [vp, vp, vp, ci, i64, i32, i32, vp, i32, i64, vp, vp, f64, vp]
+    lib.oracle_sparse_attention_rows.restype = ci
     _lib = lib
     return lib
 
@@ -236,4 +238,23 @@ def sparse_attention(q, k, v, idx, scale=None):
     sc = float(D) ** -0.5 if scale is None else float(scale)
     _check(_load().oracle_sparse_attention(_ptr(q), _ptr(k), _ptr(v), dt, S, H, D, _ptr(idx), idx.shape[2],
                                            sc, _ptr(out)), "oracle_sparse_attention")
+    return out
+
+
+def sparse_attention_rows(q, k, v, idx_rows, rows_i, rows_h, scale=None):
+    """Sparse attention of selected (position, head) rows with their index
+    rows idx_rows (n_rows, top_k): (n_rows, D) float32."""
+    q, k, dt = _prep(q, k)
+    v = np.ascontiguousarray(v)
+    if v.dtype != q.dtype or v.shape != q.shape:
+        raise ValueError("v must match q and k")
+    S, H, D = q.shape
+    ir = np.ascontiguousarray(idx_rows, np.int32)
+    ri = np.ascontiguousarray(rows_i, np.int64)
+    rh = np.ascontiguousarray(rows_h, np.int32)
+    out = np.empty((ri.shape[0], D), np.float32)
+    sc = float(D) ** -0.5 if scale is None else float(scale)
+    _check(_load().oracle_sparse_attention_rows(_ptr(q), _ptr(k), _ptr(v), dt, S, H, D, _ptr(ir), ir.shape[1],
+                                                ri.shape[0], _ptr(ri), _ptr(rh), sc, _ptr(out)),
+           "oracle_sparse_attention_rows")
     return out

@@ -631,6 +631,11 @@ int oracle_decode(const void *q, const void *k_cache, int dt,
  * in double (the exponent is shifted by the row maximum, which leaves the
  * quotient unchanged), rounded once to float. A row without a valid entry
  * is zero. Repeated entries count once each, as in the pages' loop. */
+static int attention_row(const void *q, const void *k, const void *v, int dt, int64_t S,
+                         int32_t H, int32_t D, const int32_t *row, int32_t top_k,
+                         double scale, int64_t i, int32_t h, double *s, double *acc,
+                         float *o);
+
 int oracle_sparse_attention(const void *q, const void *k, const void *v, int dt,
                             int64_t S, int32_t H, int32_t D, const int32_t *idx,
                             int32_t top_k, double scale, float *out)
@@ -646,45 +651,85 @@ int oracle_sparse_attention(const void *q, const void *k, const void *v, int dt,
         free(acc);
         return OR_ENOMEM;
     }
-    for (int64_t i = 0; i < S; ++i) {
-        for (int32_t h = 0; h < H; ++h) {
-            const int32_t *row = idx + ((size_t)i * H + h) * (size_t)top_k;
-            double mx = -INFINITY;
-            int any = 0;
-            for (int t = 0; t < top_k; ++t) {
-                int32_t c = row[t];
-                s[t] = -INFINITY;
-                if (c < 0 || c >= S)
-                    continue;
-                double dot = 0.0;
-                for (int d = 0; d < D; ++d)
-                    dot += (double)load_elem(q, dt, ((size_t)i * H + h) * D + d) *
-                           (double)load_elem(k, dt, ((size_t)c * H + h) * D + d);
-                s[t] = scale * dot;
-                if (s[t] > mx)
-                    mx = s[t];
-                any = 1;
-            }
-            for (int d = 0; d < D; ++d)
-                acc[d] = 0.0;
-            double den = 0.0;
-            if (any) {
-                for (int t = 0; t < top_k; ++t) {
-                    int32_t c = row[t];
-                    if (c < 0 || c >= S)
-                        continue;
-                    double e = exp(s[t] - mx);
-                    den += e;
-                    for (int d = 0; d < D; ++d)
-                        acc[d] += e * (double)load_elem(v, dt, ((size_t)c * H + h) * D + d);
-                }
-            }
-            float *o = out + ((size_t)i * H + h) * (size_t)D;
-            for (int d = 0; d < D; ++d)
-                o[d] = any ? (float)(acc[d] / den) : 0.0f;
+    for (int64_t i = 0; i < S; ++i)
+        for (int32_t h = 0; h < H; ++h)
+            attention_row(q, k, v, dt, S, H, D, idx + ((size_t)i * H + h) * (size_t)top_k, top_k,
+                          scale, i, h, s, acc, out + ((size_t)i * H + h) * (size_t)D);
+    free(s);
+    free(acc);
+    return OR_OK;
+}
+
+/* Selected rows: row r is query rows_i[r], head rows_h[r], with its index
+ * row idx_rows[r, :]; out is (n_rows, D). */
+int oracle_sparse_attention_rows(const void *q, const void *k, const void *v, int dt,
+                                 int64_t S, int32_t H, int32_t D, const int32_t *idx_rows,
+                                 int32_t top_k, int64_t n_rows, const int64_t *rows_i,
+                                 const int32_t *rows_h, double scale, float *out)
+{
+    if (!q || !k || !v || !idx_rows || !rows_i || !rows_h || !out || S < 1 || H < 1 ||
+        D < 1 || top_k < 1 || n_rows < 0)
+        return OR_EINVAL;
+    if (dt != OR_F32 && dt != OR_BF16)
+        return OR_EINVAL;
+    double *s = (double *)malloc(sizeof(double) * (size_t)top_k);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!s || !acc) {
+        free(s);
+        free(acc);
+        return OR_ENOMEM;
+    }
+    int rc = OR_OK;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        if (rows_i[r] < 0 || rows_i[r] >= S || rows_h[r] < 0 || rows_h[r] >= H) {
+            rc = OR_EINVAL;
+            break;
         }
+        attention_row(q, k, v, dt, S, H, D, idx_rows + (size_t)r * top_k, top_k, scale,
+                      rows_i[r], rows_h[r], s, acc, out + (size_t)r * D);
     }
     free(s);
     free(acc);
+    return rc;
+}
+
+/* One row of the attention: scores, shifted exponentials, weighted sum. */
+static int attention_row(const void *q, const void *k, const void *v, int dt, int64_t S,
+                         int32_t H, int32_t D, const int32_t *row, int32_t top_k,
+                         double scale, int64_t i, int32_t h, double *s, double *acc,
+                         float *o)
+{
+    double mx = -INFINITY;
+    int any = 0;
+    for (int t = 0; t < top_k; ++t) {
+        int32_t c = row[t];
+        s[t] = -INFINITY;
+        if (c < 0 || c >= S)
+            continue;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d)
+            dot += (double)load_elem(q, dt, ((size_t)i * H + h) * D + d) *
+                   (double)load_elem(k, dt, ((size_t)c * H + h) * D + d);
+        s[t] = scale * dot;
+        if (s[t] > mx)
+            mx = s[t];
+        any = 1;
+    }
+    for (int d = 0; d < D; ++d)
+        acc[d] = 0.0;
+    double den = 0.0;
+    if (any) {
+        for (int t = 0; t < top_k; ++t) {
+            int32_t c = row[t];
+            if (c < 0 || c >= S)
+                continue;
+            double e = exp(s[t] - mx);
+            den += e;
+            for (int d = 0; d < D; ++d)
+                acc[d] += e * (double)load_elem(v, dt, ((size_t)c * H + h) * D + d);
+        }
+    }
+    for (int d = 0; d < D; ++d)
+        o[d] = any ? (float)(acc[d] / den) : 0.0f;
     return OR_OK;
 }

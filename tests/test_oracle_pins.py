@@ -608,3 +608,14 @@ def test_attention_matches_pages_demo_loop_float64():
             sel = it[pos, h]
             w = F.softmax(qt[pos, h] @ kt[sel, h].T * scale, dim=-1)
             np.testing.assert_allclose(out[pos, h], (w @ vt[sel, h]).numpy(), rtol=1e-6, atol=1e-7)
+
+
+def test_attention_rows_api_matches_full():
+    q, k, v = _att_inputs(S=48, H=3, D=8, seed=91, dtype="bf16")
+    rng = np.random.default_rng(12)
+    idx = rng.integers(-1, 48, (48, 3, 7)).astype(np.int32)
+    full = oracle.sparse_attention(q, k, v, idx)
+    ri = np.array([0, 5, 47, 20], np.int64)
+    rh = np.array([2, 0, 1, 2], np.int32)
+    rows = oracle.sparse_attention_rows(q, k, v, idx[ri, rh], ri, rh)
+    np.testing.assert_array_equal(rows, full[ri, rh])

@@ -35,6 +35,7 @@ EXPORTED = (
     "pivot_status_string", "pivot_candidate_count", "pivot_prefill_workspace_bytes",
     "pivot_index_prefill", "pivot_decode_workspace_bytes", "pivot_index_decode",
     "dense_index_workspace_bytes", "dense_index", "pivot_profile_enable", "pivot_profile_read",
+    "pivot_sparse_attention",
 )
 
 #: kernel stages reported by the stage timer (include/pivot.h)
@@ -69,6 +70,8 @@ lib.pivot_profile_enable.argtypes = [ctypes.c_int]
 lib.pivot_profile_enable.restype = ctypes.c_int
 lib.pivot_profile_read.argtypes = [_vp, _vp, ctypes.c_int]
 lib.pivot_profile_read.restype = ctypes.c_int
+lib.pivot_sparse_attention.argtypes = [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp, _i32, ctypes.c_float, _vp, _vp]
+lib.pivot_sparse_attention.restype = ctypes.c_int
 
 
 class PivotError(RuntimeError):
@@ -244,3 +247,24 @@ def index_decode(q, k_cache, ctx_lens, g, top_k=2048, candidate_ratio=2.0, mode=
                                   _MODES[mode], _ptr(out), _ptr(sc), _ptr(ws), ws.numel(), _stream(q.device)),
            "pivot_index_decode")
     return (out, sc) if return_scores else out
+
+
+def sparse_attention(q, k, v, idx, scale=None, out=None):
+    """Downstream sparse attention over indexer rows: float32 (S, H, D).
+    softmax(scale q_i . k_c) over the entries c of idx[i, h] in [0, S) (-1 is
+    padding), applied to v_c; scale defaults to D**-0.5."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("idx", idx)):
+        _dev(t, name)
+    if q.shape != k.shape or q.shape != v.shape or q.dim() != 3 or len({q.dtype, k.dtype, v.dtype}) != 1:
+        raise ValueError("q, k and v must be (S, H, D) tensors of one dtype")
+    S, H, D = q.shape
+    if idx.dtype != torch.int32 or idx.dim() != 3 or tuple(idx.shape[:2]) != (S, H) or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 (S, H, top_k) tensor")
+    if out is None:
+        out = torch.empty((S, H, D), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (S, H, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 (S, H, D) tensor")
+    sc = float(D) ** -0.5 if scale is None else float(scale)
+    _check(lib.pivot_sparse_attention(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), S, H, D, _ptr(idx), idx.shape[2],
+                                      sc, _ptr(out), _stream(q.device)), "pivot_sparse_attention")
+    return out

@@ -1562,6 +1562,146 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     }
 }
 
+// ----------------------------------------------------- sparse attention
+
+struct AttnParams {
+    const void *q, *k, *v;   // (S, H, D)
+    const int32_t *idx;      // (S, H, top_k); entries outside [0, S) are padding
+    int64_t S;
+    int H, top_k;
+    float scale_log2;        // scale * log2(e)
+    float *out;              // (S, H, D) float32
+};
+
+// Sum over the 16 lanes of a row, left in every lane of the row: DPP
+// quad_perm [1,0,3,2] and [2,3,0,1], then row_half_mirror, then row_mirror.
+__device__ __forceinline__ float row16_sum(float x) {
+    auto step = [](float a, auto ctrl) {
+        return a + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), decltype(ctrl)::value, 0xF, 0xF,
+                                                              false));
+    };
+    x = step(x, std::integral_constant<int, 0xB1>{});
+    x = step(x, std::integral_constant<int, 0x4E>{});
+    x = step(x, std::integral_constant<int, 0x141>{});
+    x = step(x, std::integral_constant<int, 0x140>{});
+    return x;
+}
+
+// NE consecutive elements as float32 through 8- or 16-byte vector loads
+template <typename T, int NE>
+__device__ __forceinline__ void load_slice(const T *src, float (&x)[NE]) {
+    if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+        for (int c = 0; c < NE / 4; ++c) {
+            const float4 f = ((const float4 *)src)[c];
+            x[4 * c] = f.x;
+            x[4 * c + 1] = f.y;
+            x[4 * c + 2] = f.z;
+            x[4 * c + 3] = f.w;
+        }
+    } else {
+        uint32_t wds[NE / 2];
+        if constexpr (NE == 8) {
+            const uint4 u = *(const uint4 *)src;
+            wds[0] = u.x, wds[1] = u.y, wds[2] = u.z, wds[3] = u.w;
+        } else {
+            const uint2 u = *(const uint2 *)src;
+            wds[0] = u.x, wds[1] = u.y;
+        }
+#pragma unroll
+        for (int c = 0; c < NE / 2; ++c) {
+            x[2 * c] = __uint_as_float(wds[c] << 16);
+            x[2 * c + 1] = __uint_as_float(wds[c] & 0xFFFF0000u);
+        }
+    }
+}
+
+// Downstream sparse attention (the pages' quick-test attention, "Show Me
+// The Code"): one wavefront per (head, position), consecutive positions of
+// a head in consecutive wavefronts so that their shared index rows meet in
+// L2. 16 lanes take one key/value row (D/16 elements each), 4 rows per
+// instruction and 4 instructions in flight; the softmax runs online in base
+// 2 (one rescale per 4 rows), the 4 row slots are merged at the end.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_sparse_attn(AttnParams p) {
+    constexpr int NE = D / 16;             // elements per lane per row
+    constexpr int U = 4;                   // rows per lane group in flight
+    const int w = (int)(threadIdx.x >> 6), l = (int)(threadIdx.x & 63), j = l & 15, rr = l >> 4;
+    const int64_t r = (int64_t)blockIdx.x * 4 + w;
+    if (r >= p.S * p.H) return;
+    const int h = (int)(r / p.S);
+    const int64_t i = r % p.S;
+    const int64_t rowq = (i * p.H + h) * (int64_t)D;
+    float qv[NE];
+    load_slice<T, NE>((const T *)p.q + rowq + NE * j, qv);
+    const int32_t *ix = p.idx + (i * p.H + h) * (int64_t)p.top_k;
+    const T *K = (const T *)p.k + (int64_t)h * D + NE * j;
+    const T *V = (const T *)p.v + (int64_t)h * D + NE * j;
+    const int64_t kstride = (int64_t)p.H * D;
+    float m = -INFINITY, lsum = 0.f, acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = 0.f;
+    for (int t0 = 0; t0 < p.top_k; t0 += 4 * U) {
+        int64_t c[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int tt = t0 + 4 * u + rr;
+            const int32_t cv = tt < p.top_k ? ix[tt] : -1;
+            ok[u] = cv >= 0 && (int64_t)cv < p.S;
+            c[u] = ok[u] ? cv : 0;
+        }
+        float kr[U][NE], vr[U][NE];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            load_slice<T, NE>(K + c[u] * kstride, kr[u]);
+            load_slice<T, NE>(V + c[u] * kstride, vr[u]);
+        }
+        float sc[U], mn = m;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) d = fmaf(qv[e], kr[u][e], d);
+            d = row16_sum(d) * p.scale_log2;
+            sc[u] = ok[u] ? d : -INFINITY;
+            mn = fmaxf(mn, sc[u]);
+        }
+        const float ref = mn == -INFINITY ? 0.f : mn;  // no valid entry yet: nothing to rescale
+        const float a = exp2f(m - ref);
+        lsum *= a;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[e] *= a;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float b = exp2f(sc[u] - ref);
+            lsum += b;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) acc[e] = fmaf(b, vr[u][e], acc[e]);
+        }
+        m = mn;
+    }
+    // merge the 4 row slots: lanes j, j+16, j+32, j+48 hold the same dims
+    float ma = fmaxf(m, __shfl_xor(m, 16));
+    ma = fmaxf(ma, __shfl_xor(ma, 32));
+    const float f = ma == -INFINITY ? 0.f : exp2f(m - ma);
+    lsum *= f;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        float x = acc[e] * f;
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        acc[e] = x;
+    }
+    if (rr == 0) {
+        float *o = p.out + rowq + NE * j;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) o[e] = lsum > 0.f ? acc[e] / lsum : 0.f;
+    }
+}
+
 // ==================================================================== host
 
 enum Stage { ST_PROXY = 0, ST_SAMPLE, ST_TAU, ST_SCAN, ST_SELECT, ST_FALLBACK, ST_REFINE,
@@ -2129,6 +2269,27 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
 // =================================================================== C ABI
 
 extern "C" {
+
+int pivot_sparse_attention(const void *q, const void *k, const void *v, int32_t dtype, int64_t S, int32_t H,
+                           int32_t D, const int32_t *idx, int32_t top_k, float scale, float *out, void *stream) {
+    if (!q || !k || !v || !idx || !out) return PIVOT_EINVAL;
+    if (S < 1 || H < 1 || top_k < 1 || !std::isfinite(scale)) return PIVOT_EINVAL;
+    if (dtype != PIVOT_F32 && dtype != PIVOT_BF16) return PIVOT_EINVAL;
+    if (S > (int64_t)INT32_MAX) return PIVOT_EINVAL;
+    if (D != 64 && D != 128) return PIVOT_EUNSUPPORTED;
+    AttnParams ap{q, k, v, idx, S, H, top_k, scale * 1.4426950408889634f, out};
+    const int64_t nblocks = (S * H + 3) / 4;
+    if (nblocks > (int64_t)INT32_MAX) return PIVOT_EUNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == PIVOT_BF16) {
+        if (D == 64) hipLaunchKernelGGL((k_sparse_attn<bf16_t, 64>), dim3((unsigned)nblocks), dim3(256), 0, st, ap);
+        else hipLaunchKernelGGL((k_sparse_attn<bf16_t, 128>), dim3((unsigned)nblocks), dim3(256), 0, st, ap);
+    } else {
+        if (D == 64) hipLaunchKernelGGL((k_sparse_attn<float, 64>), dim3((unsigned)nblocks), dim3(256), 0, st, ap);
+        else hipLaunchKernelGGL((k_sparse_attn<float, 128>), dim3((unsigned)nblocks), dim3(256), 0, st, ap);
+    }
+    return hipGetLastError() == hipSuccess ? PIVOT_OK : PIVOT_EHIP;
+}
 
 const char *pivot_status_string(int status) {
     switch (status) {
