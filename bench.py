@@ -150,6 +150,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip timing the dense indexer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip timing the downstream sparse attention on the indexer's rows")
     ap.add_argument("--no-literal", action="store_true",
                     help="skip the literal per-position Refine comparison (8 heads of the S=65536 workload)")
     ap.add_argument("--no-configs", action="store_true",
@@ -288,6 +290,27 @@ def main():
         recall = {"refine": rec(ref_rows), "reuse": rec(reu_rows), "rows": int(args.recall_rows),
                   "sample": "positions uniform in [g, S), heads uniform, seed 7", "oracle_s": dense_s}
         log(f"recall@{top_k}: {recall}")
+
+    # ------------------------------------ downstream sparse attention
+    attention = None
+    if not args.no_attention:
+        log("drawing values (Pareto-norm, like the keys) for the sparse attention")
+        v = syn.pareto_keys_device(S, H, D, seed + 2000, dev)
+        aout = torch.empty((S, H, D), dtype=torch.float32, device=dev)
+        attention = {}
+        for mode in ("refine", "reuse"):
+            pv.index_prefill(q, k, top_k, g, ratio, mode, workspace=ws, out=out)
+            ams, _, _, _ = time_calls(lambda: pv.sparse_attention(q, k, v, out, out=aout), max(1, args.steps // 2),
+                                      1, pv)
+            # algorithmic bytes: every valid entry's key and value row, plus
+            # the query, index row and output row of every (position, head)
+            nvalid = float((out >= 0).sum().item())
+            abytes = nvalid * D * 2 * 2 + S * H * (D * 2 + top_k * 4 + D * 4)
+            attention[mode] = {"ms": ams, "queries_per_s": S * H / (ams / 1e3), "valid_entries": nvalid,
+                               "gathered_bytes": nvalid * D * 2 * 2, "algorithmic_GBps": abytes / (ams / 1e3) / 1e9}
+            log(f"sparse attention on {mode} rows: {ams:.2f} ms ({abytes / (ams / 1e3) / 1e9:.0f} GB/s of row reads)")
+        del v, aout
+        torch.cuda.empty_cache()
 
     # ------------------------------- literal per-position Refine (comparison)
     literal = None
@@ -491,6 +514,7 @@ def main():
             "decode": decode,
             "recall": recall,
             "literal_refine": literal,
+            "sparse_attention": attention,
             "configs": configs,
             "host": {"cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count(),
                      "gpu": torch.cuda.get_device_name(dev)},
