@@ -159,10 +159,36 @@ def test_decode_bit_exact_integer_inputs(pv, mode, g):
     kc = syn.integers((int(ctx.sum()), H, D), 9001, 4, "bf16")
     q = syn.integers((len(ctx) * g, H, D), 9002 + g, 4, "bf16")
     idx, sc = pv.index_decode(dev_tensor(q), dev_tensor(kc), ctx, g, top_k=top_k, mode=mode, return_scores=True)
+    only = pv.index_decode(dev_tensor(q), dev_tensor(kc), ctx, g, top_k=top_k, mode=mode)
     torch.cuda.synchronize()
     oi, os_ = oracle.decode(q, kc, ctx, g, top_k, 2.0, mode)
     np.testing.assert_array_equal(parity.to_host(idx), oi)
     np.testing.assert_array_equal(parity.to_host(sc), os_)
+    np.testing.assert_array_equal(parity.to_host(only), oi)
+
+
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+def test_decode_long_rows_bit_exact(pv, mode):
+    """Contexts spanning several 4096-key filter chunks with ragged tails
+    and one of a single key, top_k=2048 (K=4096), integer-valued inputs.
+    The queries of one sequence are zero: every key of its rows ties, the
+    rows overflow the survivor buffers and take the exact fallback. Scored
+    and index-only launches (the latter takes the wavefront select for
+    Reuse) both equal the oracle."""
+    H, D, top_k, g = 2, 128, 2048, 2
+    ctx = np.array([4096, 70001, 1, 12289, 33000, 130000, 2500], np.int64)
+    print(f"\n[decode long exact] {mode} ctx={ctx.tolist()}", flush=True)
+    kc = syn.integers((int(ctx.sum()), H, D), 9101, 4, "bf16")
+    q = syn.integers((len(ctx) * g, H, D), 9102, 4, "bf16")
+    q[3 * g:4 * g] = 0
+    qd, kd = dev_tensor(q), dev_tensor(kc)
+    idx, sc = pv.index_decode(qd, kd, ctx, g, top_k=top_k, mode=mode, return_scores=True)
+    only = pv.index_decode(qd, kd, ctx, g, top_k=top_k, mode=mode)
+    torch.cuda.synchronize()
+    oi, os_ = oracle.decode(q, kc, ctx, g, top_k, 2.0, mode)
+    np.testing.assert_array_equal(parity.to_host(idx), oi)
+    np.testing.assert_array_equal(parity.to_host(sc), os_)
+    np.testing.assert_array_equal(parity.to_host(only), oi)
 
 
 # ------------------------------------------------------- degenerate cases

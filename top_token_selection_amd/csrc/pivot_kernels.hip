@@ -24,8 +24,10 @@
 //   k_refine   per group: gather K[C], members' scores on MFMA, per-member
 //              exact sorted top_k
 // Decode replaces the scans by k_decode_scan (an HBM-streaming GEMV that
-// writes every score of each (sequence, head) row) and selects with the
-// streaming selector of k_fallback.
+// writes every score of each (sequence, head) row); k_dec_tau takes the
+// row's threshold from every s-th score, k_dec_filter streams the row once
+// and keeps the scores >= tau as survivors, and the prefill selection
+// (k_select_wave / k_select, queued rows through k_fallback) finishes it.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -511,7 +513,14 @@ struct SelParams {
     uint32_t *big_count;
     int64_t rows;
     int list;
+    // decode: B+1 prefix offsets of the sequences (row length of sequence j
+    // is offs[j+1] - offs[j]); null in prefill (causal prefix of group j)
+    const int64_t *offs;
 };
+
+__device__ __forceinline__ int64_t sel_row_len(const SelParams &p, int64_t j) {
+    return p.offs ? p.offs[j + 1] - p.offs[j] : prefix_len(j, p.g);
+}
 
 // Copies a staged row (LDS, msel valid entries) into every member row of
 // group (hl, j), -1 / -inf past msel; coalesced stores.
@@ -543,7 +552,7 @@ __device__ __forceinline__ void select_row(const SelParams &p, const int64_t r, 
 
     const int64_t j = r % p.G;
     const int hl = (int)(r / p.G);
-    const int64_t n = prefix_len(j, p.g);
+    const int64_t n = sel_row_len(p, j);
     const int c0 = p.cnt[2 * r], c1 = p.cnt[2 * r + 1];
     const uint32_t msel = (uint32_t)min(p.Ksel, n);
     if (c0 > p.cap_half || c1 > p.cap_half || (uint32_t)(c0 + c1) < msel) {
@@ -640,7 +649,7 @@ struct FbParams {
     int g;
     uint32_t *scratch;  // FB_BLOCKS rows of n_max keys
     int64_t n_max;
-    // decode: every (sequence, head) row, scores already in `dense`
+    // decode: queued rows r = head * B + sequence, scores already in `dense`
     int decode;
     const uint32_t *dense;
     const int64_t *offs;  // B+1 prefix offsets of the sequences
@@ -667,7 +676,7 @@ __global__ void __launch_bounds__(SEL_THREADS) k_fallback(FbParams p) {
     Group<4> G{(int)threadIdx.x, red};
     Selector<4, SEL_LOG2NB> sel{G, hist, vars};
     const int tid = threadIdx.x;
-    const uint32_t nrows = p.decode ? (uint32_t)(p.B * p.H) : *p.fb_count;
+    const uint32_t nrows = *p.fb_count;
 
     for (uint32_t it = blockIdx.x; it < nrows; it += gridDim.x) {
         const uint32_t *keys;
@@ -693,8 +702,9 @@ __global__ void __launch_bounds__(SEL_THREADS) k_fallback(FbParams p) {
             __syncthreads();
             keys = dst;
         } else {
-            const int b = (int)(it / p.H);
-            hl = (int)(it % p.H);
+            const uint32_t r = p.fb_list[it];
+            const int b = (int)(r % (uint32_t)p.B);
+            hl = (int)(r / (uint32_t)p.B);
             j = b;
             const int64_t off = p.offs[b];
             n = p.offs[b + 1] - off;
@@ -859,6 +869,123 @@ __global__ void __launch_bounds__(DEC_THREADS) k_decode_scan(DecScanParams p) {
             const int64_t t = tb + w + 4 * u;
             if (j == 15 && live && t < t1) out[t] = score_key(__uint_as_float(x));
         }
+    }
+}
+
+// ---------------------------------------------------- decode thresholds
+
+struct DecTauParams {
+    const uint32_t *dense;  // score keys of k_decode_scan
+    int sshift;             // samples: keys 2^sshift - 1, 2 * 2^sshift - 1, ...
+    const int64_t *offs;
+    int B, H;
+    int64_t keep_all_n, rsel;
+    uint32_t *tau_key;  // per row h * B + b: keys >= it survive
+};
+
+// Per (sequence, head) row: the threshold key is the rsel-th best of the
+// row's samples, every 2^sshift-th key (key 0 -- every key survives -- when
+// the row keeps all its keys or has too few samples; the selection then
+// finds the overflow and queues the row for the exact fallback).
+__global__ void __launch_bounds__(SEL_THREADS) k_dec_tau(DecTauParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *hist = (uint32_t *)smem;
+    uint32_t *vars = hist + (1 << SEL_LOG2NB);
+    uint32_t *red = vars + 8;
+    const int64_t r = blockIdx.x;
+    const int b = (int)(r % p.B);
+    const int hl = (int)(r / p.B);
+    const int64_t off = p.offs[b];
+    const int64_t n = p.offs[b + 1] - off;
+    const int64_t ns = n >> p.sshift;
+    if (n <= p.keep_all_n || ns <= p.rsel) {
+        if (threadIdx.x == 0) p.tau_key[r] = 0u;
+        return;
+    }
+    Group<4> G{(int)threadIdx.x, red};
+    Selector<4, SEL_LOG2NB> sel{G, hist, vars};
+    const int elim = (int)((ns + SEL_THREADS - 1) / SEL_THREADS);
+    const uint32_t *src = p.dense + off * p.H + (int64_t)hl * n + ((int64_t)1 << p.sshift) - 1;
+    uint32_t key[TAU_E];
+#pragma unroll
+    for (int e = 0; e < TAU_E; ++e) {
+        const int64_t gi = e * SEL_THREADS + threadIdx.x;
+        key[e] = e < elim && gi < ns ? src[gi << p.sshift] : 0u;
+    }
+    auto fe = [&](auto f) {
+#pragma unroll
+        for (int e = 0; e < TAU_E; ++e)
+            if (e < elim) f(key[e], e * SEL_THREADS + threadIdx.x);
+    };
+    const Rule rule = sel.select(fe, [](uint32_t x) { return x; }, (uint32_t)elim * SEL_THREADS,
+                                 (uint32_t)p.rsel);
+    if (threadIdx.x == 0) p.tau_key[r] = rule.T;
+}
+
+constexpr int DF_E = 16;                    // keys per thread of the decode filter
+constexpr int DF_KEYS = DF_E * 256;         // keys per decode-filter block
+
+struct DecFilterParams {
+    const uint32_t *dense;
+    const int64_t *offs;
+    int B, H;
+    int64_t chunks;  // DF_KEYS-key chunks per row (longest sequence)
+    const uint32_t *tau_key;
+    uint2 *surv;  // (row, half) streams of (float bits, key index), stride apart
+    int *cnt;     // per (row, half): survivors found (may exceed cap_half)
+    int cap_half, stride;
+};
+
+// Block = (row, chunk of DF_KEYS keys), coalesced reads of the row's score
+// keys. Keys >= the row's threshold leave as survivors: even key indices to
+// the row's first half stream, odd ones to the second (so a row that keeps
+// every key splits evenly). One atomic per half and block claims the slots;
+// slots past cap_half are not written (the count tells the selection).
+__global__ void __launch_bounds__(256) k_dec_filter(DecFilterParams p) {
+    __shared__ uint32_t wtot[2][4];
+    __shared__ uint32_t base[2];
+    const int64_t r = blockIdx.x / p.chunks;
+    const int64_t c0 = (blockIdx.x % p.chunks) * (int64_t)DF_KEYS;
+    const int b = (int)(r % p.B);
+    const int hl = (int)(r / p.B);
+    const int64_t off = p.offs[b];
+    const int64_t n = p.offs[b + 1] - off;
+    if (c0 >= n) return;
+    const uint32_t *keys = p.dense + off * p.H + (int64_t)hl * n;
+    const uint32_t T = p.tau_key[r];
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, half = tid & 1;
+    uint32_t key[DF_E];
+#pragma unroll
+    for (int e = 0; e < DF_E; ++e) {
+        const int64_t c = c0 + e * 256 + tid;
+        key[e] = c < n ? keys[c] : 0u;
+    }
+    auto keep = [&](int e) { return c0 + e * 256 + tid < n && key[e] >= T; };
+    const uint64_t hmask = half ? 0xAAAAAAAAAAAAAAAAull : 0x5555555555555555ull;
+    uint32_t tot = 0;
+#pragma unroll
+    for (int e = 0; e < DF_E; ++e) tot += __popcll(__ballot(keep(e)) & hmask);
+    if (l < 2) wtot[l][w] = tot;
+    __syncthreads();
+    if (tid < 2) {
+        const uint32_t t = wtot[tid][0] + wtot[tid][1] + wtot[tid][2] + wtot[tid][3];
+        base[tid] = t ? (uint32_t)atomicAdd(&p.cnt[2 * r + tid], (int)t) : 0u;
+    }
+    __syncthreads();
+    uint32_t pos = base[half];
+    for (int v = 0; v < w; ++v) pos += wtot[half][v];
+    uint2 *dst = p.surv + (2 * r + half) * (int64_t)p.stride;
+    const uint64_t below = (1ull << l) - 1ull;
+#pragma unroll
+    for (int e = 0; e < DF_E; ++e) {
+        const bool k = keep(e);
+        const uint64_t m = __ballot(k) & hmask;
+        if (k) {
+            const uint32_t slot = pos + (uint32_t)__popcll(m & below);
+            if (slot < (uint32_t)p.cap_half)
+                dst[slot] = make_uint2(__float_as_uint(key_score(key[e])), (uint32_t)(c0 + e * 256 + tid));
+        }
+        pos += (uint32_t)__popcll(m);
     }
 }
 
@@ -1308,7 +1435,7 @@ __global__ void __launch_bounds__(64 * SW_WAVES) k_select_wave(SelParams p) {
     if (r >= p.rows) return;
     const int64_t j = r % p.G;
     const int hl = (int)(r / p.G);
-    const int64_t n = prefix_len(j, p.g);
+    const int64_t n = sel_row_len(p, j);
     const int c0 = p.cnt[2 * r], c1 = p.cnt[2 * r + 1];
     const uint32_t msel = (uint32_t)min(p.Ksel, n);
     if (c0 > p.cap_half || c1 > p.cap_half || (uint32_t)(c0 + c1) < msel) {
@@ -1780,6 +1907,39 @@ int candidate_count(int32_t top_k, double ratio, int64_t *K) {
     return PIVOT_OK;
 }
 
+// Threshold sampling of rows of up to n_max keys from which the best Ksel
+// are wanted: every stride-th key is scored, tau is the rsel-th best sample.
+// stride is a power of two giving about 64 expected samples above the
+// Ksel-th best key (and at most 4080 samples per row, the registers of the
+// threshold kernels); rsel puts tau four standard deviations (Poisson count
+// of samples above the Ksel-th key) below it, so that at least Ksel keys
+// score >= tau with overwhelming probability. A half stream of survivors
+// holds cap_half: half the expected survivor count plus five standard
+// deviations, plus four for the split between the halves. Rows of at most
+// keep_all_n keys keep every key.
+struct Sampling {
+    int64_t stride, rsel, keep_all_n;
+    int cap_half;
+};
+
+Sampling sampling(int64_t Ksel, int64_t n_max) {
+    Sampling r;
+    int64_t s = std::min<int64_t>(64, std::max<int64_t>(1, pow2_floor(std::max<int64_t>(1, Ksel / 64))));
+    while ((n_max + s - 1) / s > 4096 - 16) s *= 2;
+    r.stride = s;
+    const double mu = (double)Ksel / (double)s;
+    const double z = 4.0;
+    const double root = (z + sqrt(z * z + 4.0 * mu)) / 2.0;
+    r.rsel = (int64_t)ceil(root * root) + 1;
+    const double X = (double)r.rsel * s, sig = sqrt((double)r.rsel) * s;
+    int64_t ch = (int64_t)ceil((X + 5.0 * sig) / 2.0 + 4.0 * sqrt(X / 2.0)) + 16;
+    ch = (ch + 63) / 64 * 64;
+    ch = std::min<int64_t>(ch, (int64_t)SEL_E * SEL_THREADS / 2);
+    r.cap_half = (int)ch;
+    r.keep_all_n = 2 * (int64_t)r.cap_half - 16;
+    return r;
+}
+
 int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio, int mode,
               int dtype, bool dense) {
     if (S < 1 || S > (int64_t)INT32_MAX - 1 || H < 1 || g < 1) return PIVOT_EINVAL;
@@ -1809,20 +1969,12 @@ int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio,
     pl.G = (S + pl.g - 1) / pl.g;
     pl.n_max = std::max<int64_t>((pl.G - 1) * pl.g, 1);
     pl.esz = dtype == PIVOT_BF16 ? 2 : 4;
-    // sampling: about 64 expected samples above the Ksel-th best key
-    int64_t s = std::min<int64_t>(64, std::max<int64_t>(1, pow2_floor(std::max<int64_t>(1, pl.Ksel / 64))));
-    while ((pl.n_max + s - 1) / s > 4096 - 16) s *= 2;  // samples fit the registers of k_tau
+    const Sampling sm = sampling(pl.Ksel, pl.n_max);
+    const int64_t s = sm.stride;
     pl.kstride = (int)s;
-    const double mu = (double)pl.Ksel / (double)s;
-    const double z = 4.0;
-    const double root = (z + sqrt(z * z + 4.0 * mu)) / 2.0;
-    pl.rsel = (int64_t)ceil(root * root) + 1;
-    const double X = (double)pl.rsel * s, sig = sqrt((double)pl.rsel) * s;
-    int64_t ch = (int64_t)ceil((X + 5.0 * sig) / 2.0 + 4.0 * sqrt(X / 2.0)) + 16;
-    ch = (ch + 63) / 64 * 64;
-    ch = std::min<int64_t>(ch, (int64_t)SEL_E * SEL_THREADS / 2);
-    pl.cap_half = (int)ch;
-    pl.keep_all_n = 2 * (int64_t)pl.cap_half - 16;
+    pl.rsel = sm.rsel;
+    pl.cap_half = sm.cap_half;
+    pl.keep_all_n = sm.keep_all_n;
     const int64_t vmax = (pl.n_max + s - 1) / s;
     pl.samp_half = (int)((vmax + 1) / 2 + 8);
     pl.n_tiles = (int)((pl.G + SCAN_ROWS - 1) / SCAN_ROWS);
@@ -2113,7 +2265,10 @@ struct DecPlan {
     int B, g, H, D, top_k, mode, dtype;
     int64_t K, Ksel, total, max_ctx;
     size_t esz;
-    size_t o_offs, o_P, o_dense, o_cand, bytes;
+    Sampling sm;
+    int sshift;
+    int64_t chunks;
+    size_t o_offs, o_P, o_dense, o_tau, o_cnt, o_surv, o_fbl, o_big, o_cand, bytes;
 };
 
 int make_dec_plan(DecPlan &dp, int B, const int64_t *ctx, int g, int H, int D, int top_k,
@@ -2145,6 +2300,12 @@ int make_dec_plan(DecPlan &dp, int B, const int64_t *ctx, int g, int H, int D, i
     dp.total = total;
     dp.max_ctx = mx;
     dp.esz = dtype == PIVOT_BF16 ? 2 : 4;
+    dp.sm = sampling(dp.Ksel, mx);
+    dp.sshift = 0;
+    while (((int64_t)1 << dp.sshift) < dp.sm.stride) ++dp.sshift;
+    dp.chunks = (mx + DF_KEYS - 1) / DF_KEYS;
+    const size_t rows = (size_t)H * B;
+    if ((int64_t)rows * dp.chunks > (int64_t)INT32_MAX) return PIVOT_EUNSUPPORTED;
     size_t off = 0;
     dp.o_offs = off;
     off += align256((size_t)(B + 1) * 8);
@@ -2152,6 +2313,16 @@ int make_dec_plan(DecPlan &dp, int B, const int64_t *ctx, int g, int H, int D, i
     off += align256((size_t)H * B * D * dp.esz);
     dp.o_dense = off;
     off += align256((size_t)total * H * 4);
+    dp.o_tau = off;
+    off += align256(rows * 4);
+    dp.o_cnt = off;  // 2 counts per row, then the fallback and list counters
+    off += align256((rows * 2 + 2) * 4);
+    dp.o_surv = off;
+    off += align256(rows * 2 * (size_t)(dp.sm.cap_half + 32) * 8);
+    dp.o_fbl = off;
+    off += align256(rows * 4);
+    dp.o_big = off;
+    off += align256(rows * 4);
     dp.o_cand = off;
     off += mode == PIVOT_REFINE ? align256((size_t)H * B * K * 4) : 0;
     dp.bytes = off;
@@ -2173,6 +2344,13 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
     T *P = (T *)(ws + dp.o_P);
     uint32_t *dense = (uint32_t *)(ws + dp.o_dense);
     uint32_t *cand = (uint32_t *)(ws + dp.o_cand);
+    uint32_t *tau_key = (uint32_t *)(ws + dp.o_tau);
+    int *cnt = (int *)(ws + dp.o_cnt);
+    uint2 *surv = (uint2 *)(ws + dp.o_surv);
+    uint32_t *fbl = (uint32_t *)(ws + dp.o_fbl);
+    uint32_t *bigl = (uint32_t *)(ws + dp.o_big);
+    const int64_t rows = (int64_t)dp.H * dp.B;
+    uint32_t *ctr = (uint32_t *)(cnt + 2 * rows);  // fallback count, list count
     // prefix offsets travel as kernel arguments, 64 per launch
     {
         int64_t run = 0;
@@ -2216,21 +2394,62 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
     ro.h0 = 0;
     ro.S = (int64_t)dp.B * dp.g;
     ro.g = dp.g;
+    const int sorted_out = dp.mode == PIVOT_REUSE ? 1 : 0;
+    {
+        const int64_t nz = 2 * rows + 2;
+        hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)std::min<int64_t>((nz + 255) / 256, 1024)), dim3(256), 0,
+                           st, (uint32_t *)cnt, nz);
+        HIP_TRY(hipGetLastError());
+        DecTauParams tp{dense, dp.sshift, offs, dp.B, dp.H, dp.sm.keep_all_n, dp.sm.rsel, tau_key};
+        const size_t lds = ((size_t)(1 << SEL_LOG2NB) + 8 + 16) * 4;
+        StageTimer tm(ST_TAU, st);
+        hipLaunchKernelGGL(k_dec_tau, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, tp);
+        HIP_TRY(hipGetLastError());
+    }
+    {
+        StageTimer tm(ST_DSELECT, st);
+        DecFilterParams fp{dense, offs, dp.B, dp.H, dp.chunks, tau_key, surv, cnt, dp.sm.cap_half,
+                           dp.sm.cap_half + 32};
+        hipLaunchKernelGGL(k_dec_filter, dim3((unsigned)(rows * dp.chunks)), dim3(256), 0, st, fp);
+        HIP_TRY(hipGetLastError());
+        SelParams se{surv, cnt, dp.sm.cap_half, dp.sm.cap_half + 32, (int64_t)dp.B, dp.g, dp.Ksel, sorted_out,
+                     ro, fbl, ctr};
+        se.big_list = bigl;
+        se.big_count = ctr + 1;
+        se.rows = rows;
+        se.offs = offs;
+        const size_t lds = sel_lds_bytes(0);
+        if (sorted_out && dp.Ksel <= 2048) {
+            const size_t wlds = (size_t)SW_WAVES * SW_REG;
+            HIP_TRY(set_lds((const void *)k_select_wave, wlds));
+            hipLaunchKernelGGL(k_select_wave, dim3((unsigned)((rows + SW_WAVES - 1) / SW_WAVES)),
+                               dim3(64 * SW_WAVES), wlds, st, se);
+            HIP_TRY(hipGetLastError());
+            se.list = 1;
+            hipLaunchKernelGGL(k_select, dim3((unsigned)std::min<int64_t>(rows, 2048)), dim3(SEL_THREADS), lds, st,
+                               se);
+        } else {
+            hipLaunchKernelGGL(k_select, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, se);
+        }
+        HIP_TRY(hipGetLastError());
+    }
     {
         FbParams fp{};
+        fp.fb_list = fbl;
+        fp.fb_count = ctr;
         fp.decode = 1;
         fp.dense = dense;
         fp.offs = offs;
         fp.B = dp.B;
         fp.H = dp.H;
         fp.Ksel = dp.Ksel;
-        fp.sorted_out = dp.mode == PIVOT_REUSE ? 1 : 0;
+        fp.sorted_out = sorted_out;
         fp.o = ro;
         fp.D = dp.D;
         const size_t lds = sel_lds_bytes(dp.D);
-        const int nrows = dp.B * dp.H;
-        StageTimer tm(ST_DSELECT, st);
-        hipLaunchKernelGGL((k_fallback<T>), dim3(nrows), dim3(SEL_THREADS), lds, st, fp);
+        StageTimer tm(ST_FALLBACK, st);
+        hipLaunchKernelGGL((k_fallback<T>), dim3((unsigned)std::min<int64_t>(rows, FB_BLOCKS)), dim3(SEL_THREADS),
+                           lds, st, fp);
         HIP_TRY(hipGetLastError());
     }
     if (dp.mode == PIVOT_REFINE) {
