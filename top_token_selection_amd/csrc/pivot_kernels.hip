@@ -81,6 +81,39 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb) {
     return x * per + min(x, rem) + i;
 }
 
+// s_waitcnt on the vector-memory counter alone: wait until at most N
+// vector memory instructions of the wavefront are outstanding (they retire
+// in issue order). Expcnt and lgkmcnt fields at their maxima (no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// wait_vmcnt<n> for a run-time n: values above 16 wait as for 16 (more
+// than asked, never less)
+__device__ __forceinline__ void wait_vmcnt_upto16(uint32_t n) {
+    switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    default: wait_vmcnt<16>(); break;
+    }
+}
+
 __device__ __forceinline__ int64_t prefix_len(int64_t j, int g) {
     const int64_t s = j * (int64_t)g;
     return s > 1 ? s : 1;
@@ -159,17 +192,18 @@ struct ScanParams {
 // of an instruction lands at base + 16 i), double-buffered, with the 16-byte
 // chunks of a key row XOR-swizzled by the row so that the fragment reads
 // spread over the banks. One step, for tile kt:
-//   wait for own loads/stores, barrier      (tile kt is in LDS)
-//   filter tile kt-1's scores
+//   wait for own loads of tile kt, barrier  (tile kt is in LDS)
 //   issue the loads of tile kt+1            (into the buffer of tile kt-1)
 //   matrix work on tile kt
-// so loads and stores have a whole matrix phase to complete before the wait.
+//   filter tile kt-1's scores (survivor stores)
+// so loads have a whole step to complete before their wait, and stores are
+// never waited for in the loop.
 //
 // Survivors ((float bits, key) pairs) of each (row, half) stream are staged
 // in an LDS ring of RING entries and leave in whole 64-byte chunks of FLUSH
-// entries, so the survivor array is written line by line instead of 8 bytes
-// at a time. A stream that passes cap_half survivors stops keeping (its row
-// takes the exact fallback).
+// entries, four lanes to a chunk, so that one store instruction writes up to
+// 16 whole chunks of different streams. A stream that passes cap_half
+// survivors stops keeping (its row takes the exact fallback).
 template <typename T, int D>
 __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     constexpr int RB = D * (int)sizeof(T);     // bytes per key row
@@ -179,11 +213,14 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     constexpr int NLD = SCAN_KEYS * NCK / SCAN_THREADS;  // loads per thread per tile
     constexpr int NSTREAM = 2 * SCAN_THREADS;  // (row, half) streams per block
     extern __shared__ __align__(16) unsigned char smem[];
-    // survivor rings: score bits [RING][NSTREAM], then key indices likewise
-    uint32_t *ringS = (uint32_t *)(smem + 2 * TILE);
+    // survivor rings (static LDS, so that addresses fold into offsets):
+    // score bits [RING][NSTREAM], then key indices likewise; the key tiles
+    // are the dynamic LDS
+    __shared__ __align__(16) uint32_t ringS[2 * RING * NSTREAM];
     constexpr uint32_t RROW = NSTREAM * 4;         // bytes per ring row
     constexpr uint32_t RKEYS = RING * NSTREAM;     // words from scores to keys
     static_assert((RING & (RING - 1)) == 0 && (RROW & (RROW - 1)) == 0, "ring sizes are powers of two");
+    static_assert(FLUSH == 8, "a chunk is four lanes' 16-byte stores");
 
     const int nb = p.Hc * p.n_tiles;
     const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)nb);
@@ -299,31 +336,49 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
         }
     };
 
-    // the FLUSH oldest staged survivors of stream gb leave as one chunk
-    // (entries fl .. fl+7 sit in ring rows fl % RING .. +7); at most
-    // cap_half + 16 are ever kept, inside the stream's stride
+    uint32_t nst = 0;  // survivor store instructions since the last tile's loads
+    // Every stream of column block gb with FLUSH or more staged survivors
+    // sends its FLUSH oldest (entries fl .. fl+7, ring rows fl % RING ..)
+    // as one 64-byte chunk. The streams are ranked; the r-th one's lane and
+    // flushed count go to lane 4r (forward permute, no LDS memory) and over
+    // its quad (DPP), and lane 4r + q stores entries fl + 2q, fl + 2q + 1:
+    // an instruction writes 16 whole chunks. At most cap_half + 16 are ever
+    // kept, inside the stream's stride. Wavefront-uniform control flow.
     auto flush = [&](int gb) {
-        if (cs[gb] / RROW - fl[gb] >= (uint32_t)FLUSH) {
-            const uint32_t *src = ringS + (fl[gb] % RING) * NSTREAM + gb * SCAN_THREADS + stream0;
-            uint32_t sv[FLUSH], kv[FLUSH];
-#pragma unroll
-            for (int i = 0; i < FLUSH; ++i) {
-                sv[i] = src[i * NSTREAM];
-                kv[i] = src[i * NSTREAM + RKEYS];
+        // counts its store instructions in nst: one per pass below (the
+        // pass's first quad always stores)
+        const bool need = cs[gb] / RROW - fl[gb] >= (uint32_t)FLUSH;
+        const uint64_t M = __ballot(need);
+        if (M == 0) return;
+        const uint32_t rank =
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(M >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)M, 0u));
+        const int nf = __popcll(M);
+        for (int r0 = 0; r0 < nf; r0 += 16) {
+            // senders target lane 4 (rank - r0); the others an odd lane
+            const bool mine = need && rank - (uint32_t)r0 < 16u;
+            const int to = mine ? (int)(rank - (uint32_t)r0) * 16 : (l | 1) * 4;
+            const uint32_t sid = dpp_u32<0x00>(0u, (uint32_t)__builtin_amdgcn_ds_permute(to, l));
+            const uint32_t sfl = dpp_u32<0x00>(0u, (uint32_t)__builtin_amdgcn_ds_permute(to, (int)fl[gb]));
+            if ((l >> 2) < nf - r0) {
+                const uint32_t e = sfl + 2u * (uint32_t)(l & 3);
+                const uint32_t *src = ringS + gb * SCAN_THREADS + w * 64 + (int)sid;
+                const uint32_t ia = (e % RING) * NSTREAM, ib = ((e + 1) % RING) * NSTREAM;
+                const uint2 a = make_uint2(src[ia], src[ia + RKEYS]);
+                const uint2 b = make_uint2(src[ib], src[ib + RKEYS]);
+                const uint32_t so = (uint32_t)(((64 * w + 32 * gb + (int)(sid & 31)) * 2 + (int)(sid >> 5)) * p.stride) * 8u;
+                *(uint4 *)(sb + so + e * 8u) = make_uint4(a.x, a.y, b.x, b.y);
             }
-            uint4 *dst = (uint4 *)(sb + soff0[gb] + fl[gb] * 8u);
-#pragma unroll
-            for (int i = 0; i < FLUSH / 2; ++i) dst[i] = make_uint4(sv[2 * i], kv[2 * i], sv[2 * i + 1], kv[2 * i + 1]);
-            fl[gb] += FLUSH;
+            ++nst;
         }
+        fl[gb] += need ? (uint32_t)FLUSH : 0u;
     };
 
     // keep the scores of tile kt that reach the row's threshold; at most 16
     // per stream and tile. Tiles below every row's prefix end skip the causal
     // test. A flush check after every 8 scores keeps the ring from filling.
     // Per score: one compare (two on causal tiles), the count update, the
-    // ring row address from the count (one and-or), and two 32-bit LDS
-    // stores (score bits, key index); the 16 key indices of the tile are
+    // ring row address from the count (one and-or), and one LDS instruction
+    // storing score bits and key index; the 16 key indices of the tile are
     // shared by both column blocks. A slot is written whether kept or not
     // (row cnt % RING is free: fewer than RING entries wait); only kept ones
     // are counted.
@@ -360,12 +415,18 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
         else run(std::true_type{});
     };
 
+    // The loads of tile kt were the last vector-memory instructions before
+    // the nst survivor stores of the previous step's filter: waiting for at
+    // most nst outstanding completes the tile and leaves the stores in
+    // flight. After the barrier every wavefront is done with tile kt-1, so
+    // tile kt+1 may load into its buffer.
     auto step = [&](int kt, const acc_t &prev, acc_t &cur) {
-        __builtin_amdgcn_s_waitcnt(0);  // tile kt (and older stores) complete
-        __syncthreads();
-        if (kt > 0) filter(kt - 1, prev);
+        wait_vmcnt_upto16(__builtin_amdgcn_readfirstlane(nst));  // nst is wavefront-uniform
+        nst = 0;
+        __builtin_amdgcn_s_barrier();
         if (kt + 1 < ntiles_k) issue_tile(kt + 1);
         matrix(kt, cur);
+        if (kt > 0) filter(kt - 1, prev);
     };
     // every proxy fragment has arrived before the loop: the loop then waits
     // on its own loads and stores only. Even tiles accumulate in accA, odd
@@ -2063,7 +2124,8 @@ int dispatch_refine(int D, const RefParams &rp, int nblocks, size_t lds, hipStre
 
 template <typename T, int D>
 int launch_scan(const ScanParams &sp, hipStream_t st) {
-    const size_t lds = 2 * SCAN_KEYS * (size_t)D * sizeof(T) + (size_t)RING * 2 * SCAN_THREADS * 8;
+    // dynamic LDS: the two key tiles (the survivor rings are static)
+    const size_t lds = 2 * SCAN_KEYS * (size_t)D * sizeof(T);
     HIP_TRY(set_lds((const void *)k_scan<T, D>, lds));
     hipLaunchKernelGGL((k_scan<T, D>), dim3(sp.Hc * sp.n_tiles), dim3(SCAN_THREADS), lds, st, sp);
     HIP_TRY(hipGetLastError());
