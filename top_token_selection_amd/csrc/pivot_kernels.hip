@@ -1559,8 +1559,19 @@ __global__ void __launch_bounds__(64 * SW_WAVES) k_select_wave(SelParams p) {
             for (int t = 0; t < m; ++t) dst0[t * rstride + fin] = (int32_t)idx;
         },
         [&](const uint32_t *row) {
+            // the row's first msel & ~3 entries as 16-byte loads and stores
+            // when the member rows are 16-byte aligned, the rest one by one
+            int cs0 = row ? 0 : (int)msel;
+            if (row && (p.o.top_k & 3) == 0 && ((uintptr_t)dst0 & 15u) == 0) {
+                const int nv4 = (int)(msel & ~3u);
+                for (int c = 4 * l; c < nv4; c += 256) {
+                    const uint4 v = *(const uint4 *)(row + c);
+                    for (int t = 0; t < m; ++t) *(uint4 *)(dst0 + t * rstride + c) = v;
+                }
+                cs0 = nv4;
+            }
             for (int t = 0; t < m; ++t)
-                for (int c = row ? l : (int)msel + l; c < p.o.top_k; c += 64)
+                for (int c = cs0 + l; c < p.o.top_k; c += 64)
                     dst0[t * rstride + c] = c < (int)msel ? (int32_t)row[c] : -1;
         });
     if (!done) to_list();
@@ -1701,8 +1712,16 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
             key, e4, nc, msel, smp, my, (uint32_t)p.ref_cap, [&](uint32_t pos) { return cl[pos]; },
             [&](uint32_t fin, uint32_t idx) { p.out_idx[obase + fin] = (int32_t)idx; },
             [&](const uint32_t *row) {
-                for (int c = row ? l : (int)msel + l; c < p.top_k; c += 64)
-                    p.out_idx[obase + c] = c < (int)msel ? (int32_t)row[c] : -1;
+                // 16-byte loads and stores for the first msel & ~3 entries
+                // when the output row is 16-byte aligned
+                int32_t *dst = p.out_idx + obase;
+                int cs0 = row ? 0 : (int)msel;
+                if (row && ((uintptr_t)dst & 15u) == 0) {
+                    const int nv4 = (int)(msel & ~3u);
+                    for (int c = 4 * l; c < nv4; c += 256) *(uint4 *)(dst + c) = *(const uint4 *)(row + c);
+                    cs0 = nv4;
+                }
+                for (int c = cs0 + l; c < p.top_k; c += 64) dst[c] = c < (int)msel ? (int32_t)row[c] : -1;
             }))
         return;
 
