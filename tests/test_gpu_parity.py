@@ -56,6 +56,8 @@ EXACT_CASES = [
     (513, 2, 128, 8, 1, 2.0, "bf16"),     # g = 1
     (300, 2, 64, 40, 16, 2.0, "f32"),     # top_k beyond early prefixes
     (2100, 1, 128, 100, 8, 2.0, "bf16"),  # > 8 scan tiles, rows that need sampling
+    (1500, 3, 128, 37, 8, 2.0, "bf16"),   # odd top_k: output rows off 16-byte alignment
+    (900, 2, 64, 101, 4, 1.5, "f32"),     # odd top_k and K = floor(151.5)
 ]
 
 

@@ -318,7 +318,7 @@ struct Selector {
         narrow(fe,
                [&](uint32_t key, uint32_t pl, bool &v, uint32_t &k) {
                    v = (key == Tk);
-                   k = ~idx(pl);
+                   k = v ? ~idx(pl) : 0u;  // idx may be a memory read: only for ties
                },
                mn2, mx2, rem, T2, rem2, whole2);
         // indices are distinct, so the narrowing always ends whole (or on a

@@ -603,6 +603,7 @@ __device__ __forceinline__ void write_member_rows(const RowOut &o, int hl, int64
 // row's best Ksel keys when the row is not queued) are held in registers and
 // the exact best min(Ksel, n) of them selected. Slots past the survivors
 // hold key 0 (below every score) and never rank.
+template <bool SORTED>
 __device__ __forceinline__ void select_row(const SelParams &p, const int64_t r, unsigned char *smem) {
     uint32_t *hist = (uint32_t *)smem;
     uint32_t *vars = hist + (1 << SEL_LOG2NB);
@@ -627,43 +628,65 @@ __device__ __forceinline__ void select_row(const SelParams &p, const int64_t r, 
     const int elim = (int)((ns + SEL_THREADS - 1) / SEL_THREADS);
     Group<4> G{(int)threadIdx.x, red};
     Selector<4, SEL_LOG2NB> sel{G, hist, vars};
-    uint32_t key[SEL_E], pl[SEL_E];
     const uint2 *b0 = p.surv + (2 * r) * (int64_t)p.stride;
     const uint2 *b1 = p.surv + (2 * r + 1) * (int64_t)p.stride;
-    // all loads first (independent, in flight together), then the keys
-#pragma unroll
-    for (int e = 0; e < SEL_E; ++e) {
-        const uint32_t gi = e * SEL_THREADS + threadIdx.x;
-        uint2 x = make_uint2(0u, 0xFFFFFFFFu);
-        if (e < elim && gi < ns) x = gi < (uint32_t)c0 ? b0[gi] : b1[gi - c0];
-        key[e] = x.x;
-        pl[e] = x.y;
-    }
-#pragma unroll
-    for (int e = 0; e < SEL_E; ++e)
-        key[e] = pl[e] == 0xFFFFFFFFu ? 0u : score_key(__uint_as_float(key[e]));
-    auto fe = [&](auto f) {
-#pragma unroll
-        for (int e = 0; e < SEL_E; ++e)
-            if (e < elim) f(key[e], pl[e]);
-    };
     auto ident = [](uint32_t x) { return x; };
-    const Rule rule = msel >= ns ? Rule{0u, 0u}
-                                 : sel.select(fe, ident, (uint32_t)elim * SEL_THREADS, msel);
-    auto fs = [&](auto f) {
+    if constexpr (!SORTED) {
+        uint32_t key[SEL_E], pl[SEL_E];
+        // all loads first (independent, in flight together), then the keys
+#pragma unroll
+        for (int e = 0; e < SEL_E; ++e) {
+            const uint32_t gi = e * SEL_THREADS + threadIdx.x;
+            uint2 x = make_uint2(0u, 0xFFFFFFFFu);
+            if (e < elim && gi < ns) x = gi < (uint32_t)c0 ? b0[gi] : b1[gi - c0];
+            key[e] = x.x;
+            pl[e] = x.y;
+        }
 #pragma unroll
         for (int e = 0; e < SEL_E; ++e)
-            if (e < elim && key[e] != 0u && rule.sel(key[e], pl[e])) f(key[e], pl[e]);
-    };
-    if (!p.sorted_out) {
+            key[e] = pl[e] == 0xFFFFFFFFu ? 0u : score_key(__uint_as_float(key[e]));
+        auto fe = [&](auto f) {
+#pragma unroll
+            for (int e = 0; e < SEL_E; ++e)
+                if (e < elim) f(key[e], pl[e]);
+        };
+        const Rule rule = msel >= ns ? Rule{0u, 0u}
+                                     : sel.select(fe, ident, (uint32_t)elim * SEL_THREADS, msel);
         if (threadIdx.x == 0) ctr[0] = 0;
         __syncthreads();
         uint32_t *dst = p.o.cand + r * p.o.K;
-        fs([&](uint32_t, uint32_t idx) {
-            const uint32_t slot = atomicAdd(&ctr[0], 1u);
-            if (slot < msel) dst[slot] = idx;
-        });
+#pragma unroll
+        for (int e = 0; e < SEL_E; ++e)
+            if (e < elim && key[e] != 0u && rule.sel(key[e], pl[e])) {
+                const uint32_t slot = atomicAdd(&ctr[0], 1u);
+                if (slot < msel) dst[slot] = pl[e];
+            }
     } else {
+        uint32_t key[SEL_E], pl[SEL_E];
+        // all loads first (independent, in flight together), then the keys
+#pragma unroll
+        for (int e = 0; e < SEL_E; ++e) {
+            const uint32_t gi = e * SEL_THREADS + threadIdx.x;
+            uint2 x = make_uint2(0u, 0xFFFFFFFFu);
+            if (e < elim && gi < ns) x = gi < (uint32_t)c0 ? b0[gi] : b1[gi - c0];
+            key[e] = x.x;
+            pl[e] = x.y;
+        }
+#pragma unroll
+        for (int e = 0; e < SEL_E; ++e)
+            key[e] = pl[e] == 0xFFFFFFFFu ? 0u : score_key(__uint_as_float(key[e]));
+        auto fe = [&](auto f) {
+#pragma unroll
+            for (int e = 0; e < SEL_E; ++e)
+                if (e < elim) f(key[e], pl[e]);
+        };
+        const Rule rule = msel >= ns ? Rule{0u, 0u}
+                                     : sel.select(fe, ident, (uint32_t)elim * SEL_THREADS, msel);
+        auto fs = [&](auto f) {
+#pragma unroll
+            for (int e = 0; e < SEL_E; ++e)
+                if (e < elim && key[e] != 0u && rule.sel(key[e], pl[e])) f(key[e], pl[e]);
+        };
         constexpr int MP = MAX_TOPK / SEL_THREADS;
         uint32_t rpos[MP], rkey[MP], rpl[MP];
         sel.template sort_ranks<MP>(fs, ident, msel, bufk, bufp, rpos, rkey, rpl);
@@ -683,15 +706,18 @@ __device__ __forceinline__ void select_row(const SelParams &p, const int64_t r, 
     }
 }
 
-__global__ void __launch_bounds__(SEL_THREADS) k_select(SelParams p) {
+// SORTED: sorted member rows (Reuse, dense); otherwise candidate lists
+// (Refine), which need fewer registers: three blocks share a CU.
+template <bool SORTED>
+__global__ void __launch_bounds__(SEL_THREADS, SORTED ? 2 : 3) k_select(SelParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     if (!p.list) {
-        select_row(p, blockIdx.x, smem);
+        select_row<SORTED>(p, blockIdx.x, smem);
         return;
     }
     const uint32_t nl = *p.big_count;
     for (uint32_t it = blockIdx.x; it < nl; it += gridDim.x) {
-        select_row(p, (int64_t)p.big_list[it], smem);
+        select_row<SORTED>(p, (int64_t)p.big_list[it], smem);
         __syncthreads();
     }
 }
@@ -2090,6 +2116,9 @@ size_t sel_lds_bytes(int D) {
     return ((size_t)(1 << SEL_LOG2NB) + 8 + 16 + 4 + 2 * MAX_TOPK) * 4 + (size_t)D * 4;
 }
 
+// k_select<false> (candidate lists) uses no staging buffers
+size_t sel_cand_lds_bytes() { return ((size_t)(1 << SEL_LOG2NB) + 8 + 16 + 4) * 4; }
+
 // LDS layout of k_refine: candidate list + one region per query wavefront.
 // A region holds the query's scores first, then either the fused select
 // (header + staged keys/positions) or the general selector's arrays; spare
@@ -2277,10 +2306,14 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
                                    dim3(64 * SW_WAVES), wlds, st, se);
                 HIP_TRY(hipGetLastError());
                 se.list = 1;
-                hipLaunchKernelGGL(k_select, dim3((unsigned)std::min<int64_t>(rows, 2048)), dim3(SEL_THREADS), lds,
+                hipLaunchKernelGGL(k_select<true>, dim3((unsigned)std::min<int64_t>(rows, 2048)), dim3(SEL_THREADS), lds,
                                    st, se);
             } else {
-                hipLaunchKernelGGL(k_select, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, se);
+                if (sorted_out)
+                    hipLaunchKernelGGL(k_select<true>, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, se);
+                else
+                    hipLaunchKernelGGL(k_select<false>, dim3((unsigned)rows), dim3(SEL_THREADS), sel_cand_lds_bytes(),
+                                       st, se);
             }
             HIP_TRY(hipGetLastError());
         }
@@ -2507,10 +2540,14 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
                                dim3(64 * SW_WAVES), wlds, st, se);
             HIP_TRY(hipGetLastError());
             se.list = 1;
-            hipLaunchKernelGGL(k_select, dim3((unsigned)std::min<int64_t>(rows, 2048)), dim3(SEL_THREADS), lds, st,
+            hipLaunchKernelGGL(k_select<true>, dim3((unsigned)std::min<int64_t>(rows, 2048)), dim3(SEL_THREADS), lds, st,
                                se);
         } else {
-            hipLaunchKernelGGL(k_select, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, se);
+            if (sorted_out)
+                hipLaunchKernelGGL(k_select<true>, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, se);
+            else
+                hipLaunchKernelGGL(k_select<false>, dim3((unsigned)rows), dim3(SEL_THREADS), sel_cand_lds_bytes(), st,
+                                   se);
         }
         HIP_TRY(hipGetLastError());
     }
