@@ -61,7 +61,8 @@ __device__ __forceinline__ int bit_width(uint32_t x) { return x ? 32 - __clz((in
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
 // Cross-lane steps use DPP (data-parallel primitives of the VALU): row_shr:n
-// shifts within each row of 16 lanes, row_bcast:15 / row_bcast:31 carry lane
+// (row_shl:n) gives lane l the value of lane l - n (l + n) of its row of 16
+// lanes, row_bcast:15 / row_bcast:31 carry lane
 // 15 of a row into the next row / lane 31 into rows 2 and 3. A lane with no
 // source (or in a row left out by the row mask) gets `old`.
 template <int CTRL, int ROW_MASK = 0xF>
@@ -69,6 +70,7 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
+constexpr int DPP_ROW_SHL4 = 0x104;
 constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
 
 // op over lanes 0..l for every lane l (inclusive scan); lane 63 ends with
