@@ -40,6 +40,9 @@
  *               score); padding holds -inf
  *   Valid counts: Refine min(top_k, min(K, n)), Reuse min(top_k, n),
  *   dense min(top_k, max(i, 1)), with n the group's prefix length.
+ *   Alignment: q, k, k_cache, v and the workspace start on 16-byte
+ *   boundaries, int32 / float32 arrays on 4-byte boundaries (PIVOT_EINVAL,
+ *   or PIVOT_EWORKSPACE for the workspace, otherwise).
  *
  * Ownership and execution: the caller owns every buffer; the library never
  * allocates device memory and keeps no state between calls (apart from the

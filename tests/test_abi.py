@@ -84,8 +84,8 @@ def test_workspace_sizes(pv):
 
 
 def _prefill(pv, **kw):
-    a = dict(q=1, k=1, dtype=1, S=64, H=2, D=64, top_k=8, g=8, ratio=2.0, mode=0,
-             out=1, sc=None, ws=1, wsb=1 << 40, st=None)
+    a = dict(q=256, k=256, dtype=1, S=64, H=2, D=64, top_k=8, g=8, ratio=2.0, mode=0,
+             out=256, sc=None, ws=256, wsb=1 << 40, st=None)
     a.update(kw)
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     return pv.lib.pivot_index_prefill(vp(a["q"]), vp(a["k"]), a["dtype"], a["S"], a["H"], a["D"],
@@ -99,6 +99,7 @@ def _prefill(pv, **kw):
     (dict(dtype=7), -1), (dict(mode=3), -1), (dict(ratio=0.5), -1),
     (dict(D=96), -2), (dict(top_k=5000, ratio=1.0), -2), (dict(top_k=4096, ratio=2.0), -2),
     (dict(ws=None), -3), (dict(wsb=16), -3),
+    (dict(q=264), -1), (dict(k=258), -1), (dict(out=258), -1), (dict(sc=257), -1), (dict(ws=264), -3),
 ])
 def test_prefill_validation_before_any_device_work(pv, kw, code):
     # pointers here are fake: an argument error must be found on the host
@@ -106,22 +107,52 @@ def test_prefill_validation_before_any_device_work(pv, kw, code):
 
 
 def test_decode_validation(pv):
-    vp = ctypes.c_void_p
+    vp = lambda x: ctypes.c_void_p(x)
+    A = 256  # a fake, 16-byte aligned address: argument errors are found on the host
     ctx = (ctypes.c_int64 * 2)(10, 20)
     zero = (ctypes.c_int64 * 2)(10, 0)
     L = pv.lib.pivot_index_decode
-    assert L(vp(1), vp(1), 1, zero, 2, 2, 8, 128, 8, 2.0, 0, vp(1), None, vp(1), 1 << 40, None) == -1
-    assert L(vp(1), vp(1), 1, None, 2, 2, 8, 128, 8, 2.0, 0, vp(1), None, vp(1), 1 << 40, None) == -1
-    assert L(None, vp(1), 1, ctx, 2, 2, 8, 128, 8, 2.0, 0, vp(1), None, vp(1), 1 << 40, None) == -1
-    assert L(vp(1), vp(1), 1, ctx, 2, 0, 8, 128, 8, 2.0, 0, vp(1), None, vp(1), 1 << 40, None) == -1
-    assert L(vp(1), vp(1), 1, ctx, 2, 2, 8, 80, 8, 2.0, 0, vp(1), None, vp(1), 1 << 40, None) == -2
-    assert L(vp(1), vp(1), 1, ctx, 2, 2, 8, 128, 8, 2.0, 0, vp(1), None, vp(1), 8, None) == -3
+    assert L(vp(A), vp(A), 1, zero, 2, 2, 8, 128, 8, 2.0, 0, vp(A), None, vp(A), 1 << 40, None) == -1
+    assert L(vp(A), vp(A), 1, None, 2, 2, 8, 128, 8, 2.0, 0, vp(A), None, vp(A), 1 << 40, None) == -1
+    assert L(None, vp(A), 1, ctx, 2, 2, 8, 128, 8, 2.0, 0, vp(A), None, vp(A), 1 << 40, None) == -1
+    assert L(vp(A), vp(A), 1, ctx, 2, 0, 8, 128, 8, 2.0, 0, vp(A), None, vp(A), 1 << 40, None) == -1
+    assert L(vp(A), vp(A), 1, ctx, 2, 2, 8, 80, 8, 2.0, 0, vp(A), None, vp(A), 1 << 40, None) == -2
+    assert L(vp(A), vp(A), 1, ctx, 2, 2, 8, 128, 8, 2.0, 0, vp(A), None, vp(A), 8, None) == -3
+    assert L(vp(A + 8), vp(A), 1, ctx, 2, 2, 8, 128, 8, 2.0, 0, vp(A), None, vp(A), 1 << 40, None) == -1
+    assert L(vp(A), vp(A + 2), 1, ctx, 2, 2, 8, 128, 8, 2.0, 0, vp(A), None, vp(A), 1 << 40, None) == -1
+    assert L(vp(A), vp(A), 1, ctx, 2, 2, 8, 128, 8, 2.0, 0, vp(A), None, vp(A + 4), 1 << 40, None) == -3
 
 
 def test_dense_validation(pv):
     vp = ctypes.c_void_p
+    A = 256
     L = pv.lib.dense_index
-    assert L(None, vp(1), 1, 64, 2, 64, 8, vp(1), None, vp(1), 1 << 40, None) == -1
-    assert L(vp(1), vp(1), 1, 64, 2, 64, 0, vp(1), None, vp(1), 1 << 40, None) == -1
-    assert L(vp(1), vp(1), 1, 64, 2, 128, 5000, vp(1), None, vp(1), 1 << 40, None) == -2
-    assert L(vp(1), vp(1), 1, 64, 2, 64, 8, vp(1), None, None, 0, None) == -3
+    assert L(None, vp(A), 1, 64, 2, 64, 8, vp(A), None, vp(A), 1 << 40, None) == -1
+    assert L(vp(A), vp(A), 1, 64, 2, 64, 0, vp(A), None, vp(A), 1 << 40, None) == -1
+    assert L(vp(A), vp(A), 1, 64, 2, 128, 5000, vp(A), None, vp(A), 1 << 40, None) == -2
+    assert L(vp(A), vp(A), 1, 64, 2, 64, 8, vp(A), None, None, 0, None) == -3
+    assert L(vp(A + 4), vp(A), 1, 64, 2, 64, 8, vp(A), None, vp(A), 1 << 40, None) == -1
+
+
+def test_sparse_attention_validation(pv):
+    vp = ctypes.c_void_p
+    A = 256
+    L = pv.lib.pivot_sparse_attention
+    ok = dict(q=A, k=A, v=A, dtype=1, S=64, H=2, D=64, idx=A, top_k=8, scale=0.125, out=A)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        p = lambda x: None if x is None else vp(x)
+        return L(p(a["q"]), p(a["k"]), p(a["v"]), a["dtype"], a["S"], a["H"], a["D"], p(a["idx"]),
+                 a["top_k"], a["scale"], p(a["out"]), None)
+
+    assert call(q=None) == -1
+    assert call(idx=None) == -1
+    assert call(v=A + 8) == -1
+    assert call(out=A + 2) == -1
+    assert call(S=0) == -1
+    assert call(top_k=0) == -1
+    assert call(scale=float("nan")) == -1
+    assert call(dtype=5) == -1
+    assert call(D=96) == -2

@@ -130,18 +130,38 @@ __device__ __forceinline__ int64_t virt_count(int64_t n, int kstride, int koff) 
 template <typename T>
 __global__ void k_proxy(const T *__restrict__ q, int64_t S, int H, int D, int g,
                         int h0, int Hc, int64_t G, int rep, T *__restrict__ P) {
-    const int64_t total = (int64_t)Hc * G * D;
+    // each thread: V consecutive dims (16 bytes) of one proxy row, the
+    // members read as 16-byte loads; per dimension the sum runs in position
+    // order, as one element at a time would
+    constexpr int V = 16 / (int)sizeof(T);
+    const int DV = D / V;
+    const int64_t total = (int64_t)Hc * G * DV;
     for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
          t += (int64_t)gridDim.x * blockDim.x) {
-        const int d = (int)(t % D);
-        const int64_t j = (t / D) % G / rep;  // rep proxy rows per group
-        const int hl = (int)(t / ((int64_t)D * G));
+        const int d0 = (int)(t % DV) * V;
+        const int64_t row = t / DV;              // proxy row (hl, jr)
+        const int64_t j = row % G / rep;         // rep proxy rows per group
+        const int hl = (int)(row / G);
         const int64_t i0 = j * g;
         const int64_t m = min((int64_t)g, S - i0);
-        const T *src = q + (i0 * H + (h0 + hl)) * (int64_t)D + d;
-        float sum = 0.f;  // sequential float32 sum in position order
-        for (int64_t i = 0; i < m; ++i) sum += load_f32(src + i * (int64_t)H * D);
-        store_from_f32(P + t, __fdiv_rn(sum, (float)m));
+        const T *src = q + (i0 * H + (h0 + hl)) * (int64_t)D + d0;
+        float sum[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) sum[v] = 0.f;
+        for (int64_t i = 0; i < m; ++i) {
+            const uint4 x = *(const uint4 *)(src + i * (int64_t)H * D);
+            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                float f;
+                if constexpr (sizeof(T) == 4) f = __uint_as_float(w[v]);
+                else f = __uint_as_float((v & 1) ? (w[v >> 1] & 0xFFFF0000u) : (w[v >> 1] << 16));
+                sum[v] += f;
+            }
+        }
+        T *dst = P + row * (int64_t)D + d0;
+#pragma unroll
+        for (int v = 0; v < V; ++v) store_from_f32(dst + v, __fdiv_rn(sum[v], (float)m));
     }
 }
 
@@ -2043,6 +2063,10 @@ struct Plan {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// the kernels move q, k and workspace data in 16-byte vectors
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
 int64_t pow2_floor(int64_t x) {
     int64_t p = 1;
     while (p * 2 <= x) p *= 2;
@@ -2267,7 +2291,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             sp.p_row = (int64_t)pl.H * D;
             sp.p_head = D;
         } else {
-            const int64_t total = rows * D;
+            const int64_t total = rows * D / (16 / (int64_t)sizeof(T));  // 16 bytes per thread
             const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
             StageTimer tm(ST_PROXY, st);
             hipLaunchKernelGGL((k_proxy<T>), dim3(blocks), dim3(256), 0, st, q, pl.S, pl.H, pl.D, pl.gp,
@@ -2529,7 +2553,7 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
         }
     }
     {
-        const int64_t total = (int64_t)dp.H * dp.B * dp.D;
+        const int64_t total = (int64_t)dp.H * dp.B * dp.D / (16 / (int64_t)sizeof(T));  // 16 bytes per thread
         const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
         StageTimer tm(ST_PROXY, st);
         hipLaunchKernelGGL((k_proxy<T>), dim3(blocks), dim3(256), 0, st, q, (int64_t)dp.B * dp.g, dp.H,
@@ -2656,6 +2680,7 @@ extern "C" {
 int pivot_sparse_attention(const void *q, const void *k, const void *v, int32_t dtype, int64_t S, int32_t H,
                            int32_t D, const int32_t *idx, int32_t top_k, float scale, float *out, void *stream) {
     if (!q || !k || !v || !idx || !out) return PIVOT_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(idx) || !aligned4(out)) return PIVOT_EINVAL;
     if (S < 1 || H < 1 || top_k < 1 || !std::isfinite(scale)) return PIVOT_EINVAL;
     if (dtype != PIVOT_F32 && dtype != PIVOT_BF16) return PIVOT_EINVAL;
     if (S > (int64_t)INT32_MAX) return PIVOT_EINVAL;
@@ -2715,7 +2740,9 @@ static int prefill_common(const void *q, const void *k, int32_t dtype, int64_t S
     int rc = make_plan(pl, S, H, D, top_k, g, ratio, mode, dtype, dense);
     if (rc) return rc;
     if (!q || !k || !out_idx) return PIVOT_EINVAL;
-    if (!workspace) return PIVOT_EWORKSPACE;
+    if (!aligned16(q) || !aligned16(k) || !aligned4(out_idx) || (out_score && !aligned4(out_score)))
+        return PIVOT_EINVAL;
+    if (!workspace || !aligned16(workspace)) return PIVOT_EWORKSPACE;
     if (workspace_bytes < pl.fixed + per_head_bytes(pl)) return PIVOT_EWORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     if (dtype == PIVOT_BF16)
@@ -2753,7 +2780,9 @@ int pivot_index_decode(const void *q, const void *k_cache, int32_t dtype, const 
     int rc = make_dec_plan(dp, B, ctx_lens_host, g, H, D, top_k, candidate_ratio, mode, dtype);
     if (rc) return rc;
     if (!q || !k_cache || !out_idx) return PIVOT_EINVAL;
-    if (!workspace || workspace_bytes < dp.bytes) return PIVOT_EWORKSPACE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned4(out_idx) || (out_score && !aligned4(out_score)))
+        return PIVOT_EINVAL;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < dp.bytes) return PIVOT_EWORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     if (dtype == PIVOT_BF16)
         return run_decode<bf16_t>(dp, ctx_lens_host, (const bf16_t *)q, (const bf16_t *)k_cache, out_idx,
