@@ -1623,7 +1623,10 @@ __global__ void __launch_bounds__(64 * SW_WAVES) k_select_wave(SelParams p) {
     if (!done) to_list();
 }
 
-template <typename T, int D>
+// LINES: key rows are gathered as whole 128-byte lines and rearranged into
+// the MFMA layout in registers (bf16 blocks of several queries); otherwise
+// the loads take the MFMA layout directly.
+template <typename T, int D, bool LINES>
 __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int nblk = (int)(p.NG * p.Hc) * p.nqb;
@@ -1692,16 +1695,21 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
         // a list entry is always a key of the prefix; past the list the slot
         // holds stale LDS words: the clamp keeps every gather inside the
         // tensor, and scores past nc are never read
-        if constexpr (F32) {
+        if constexpr (!LINES) {
+            // MFMA-layout loads (16-byte pieces, lanes 16 apart): fp32, and
+            // single-query blocks, whose many resident wavefronts hide the
+            // latency better than the rearrangement below pays
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int pidx = (b0 + u) * 16 + qcol;
                 const uint32_t c = min(cl[pidx], (uint32_t)(n - 1));
                 const T *kr = Kx + ((kbase + c) * p.H + h) * (int64_t)D;
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) a[u][ks] = *(const frag_t *)(kr + 16 * ks + 4 * lq);
+                for (int ks = 0; ks < NKS; ++ks)
+                    a[u][ks] = *(const frag_t *)(kr + (F32 ? 16 * ks + 4 * lq : 32 * ks + 8 * lq));
             }
         } else {
+            static_assert(!F32, "whole-line gathers are for bf16 keys");
             // Loads: 8 consecutive lanes read one whole 128-byte line of a key
             // row (the memory pipeline merges consecutive lanes only; the
             // MFMA layout would put 16 rows and 64 bytes of each in one load,
@@ -2229,8 +2237,14 @@ RefLayout refine_layout(int64_t K, int top_k, int g) {
 
 template <typename T, int D>
 int launch_refine(const RefParams &rp, int nblocks, size_t lds, hipStream_t st) {
-    HIP_TRY(set_lds((const void *)k_refine<T, D>, lds));
-    hipLaunchKernelGGL((k_refine<T, D>), dim3(nblocks), dim3(64 * rp.nqw), lds, st, rp);
+    if (sizeof(T) == 2 && rp.nqw > 1) {
+        constexpr bool LINES = sizeof(T) == 2;
+        HIP_TRY(set_lds((const void *)k_refine<T, D, LINES>, lds));
+        hipLaunchKernelGGL((k_refine<T, D, LINES>), dim3(nblocks), dim3(64 * rp.nqw), lds, st, rp);
+    } else {
+        HIP_TRY(set_lds((const void *)k_refine<T, D, false>, lds));
+        hipLaunchKernelGGL((k_refine<T, D, false>), dim3(nblocks), dim3(64 * rp.nqw), lds, st, rp);
+    }
     HIP_TRY(hipGetLastError());
     return PIVOT_OK;
 }
