@@ -1690,73 +1690,10 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     // gather + MFMA, four 16-candidate blocks per step so that 4*NKS row
     // loads per lane are in flight together
     const int nblocks = (nc + 15) / 16;
-    for (int b0 = 4 * w; b0 < nblocks; b0 += 4 * p.nqw) {
-        frag_t a[4][NKS];
-        // a list entry is always a key of the prefix; past the list the slot
-        // holds stale LDS words: the clamp keeps every gather inside the
-        // tensor, and scores past nc are never read
-        if constexpr (!LINES) {
-            // MFMA-layout loads (16-byte pieces, lanes 16 apart): fp32, and
-            // single-query blocks, whose many resident wavefronts hide the
-            // latency better than the rearrangement below pays
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int pidx = (b0 + u) * 16 + qcol;
-                const uint32_t c = min(cl[pidx], (uint32_t)(n - 1));
-                const T *kr = Kx + ((kbase + c) * p.H + h) * (int64_t)D;
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    a[u][ks] = *(const frag_t *)(kr + (F32 ? 16 * ks + 4 * lq : 32 * ks + 8 * lq));
-            }
-        } else {
-            static_assert(!F32, "whole-line gathers are for bf16 keys");
-            // Loads: 8 consecutive lanes read one whole 128-byte line of a key
-            // row (the memory pipeline merges consecutive lanes only; the
-            // MFMA layout would put 16 rows and 64 bytes of each in one load,
-            // as 16-byte pieces of lanes 16 apart). Load (h, g), lane l: line
-            // h, 16-byte chunk l & 7 of block row 2 (l >> 3) + g.
-            constexpr int NL = D / 64;  // 128-byte lines per key row
-            u32x4_t sv[4][NL][2];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    const int pidx = (b0 + u) * 16 + 2 * (l >> 3) + g;
-                    const uint32_t c = min(cl[pidx], (uint32_t)(n - 1));
-                    const T *kr = Kx + ((kbase + c) * p.H + h) * (int64_t)D + 8 * (l & 7);
-#pragma unroll
-                    for (int hh = 0; hh < NL; ++hh) sv[u][hh][g] = *(const u32x4_t *)(kr + 64 * hh);
-                }
-            }
-            // Into the MFMA layout (MFMA 2 h + q, lane 16 j + i: block row i,
-            // chunk 4 q + j of line h): the two row halves trade across lane
-            // bit 2 (DPP row shifts by 4), so that the register index becomes
-            // the chunk's bit 2, then lane 16 j + i takes lane 4 i + j's word
-            // (bpermute).
-            const bool hi2 = (l & 4) != 0;
-            const int from = (((l & 15) << 2) | (l >> 4)) << 2;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-#pragma unroll
-                for (int hh = 0; hh < NL; ++hh) {
-                    u32x4_t t0, t1;
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        // the shifts run on every lane (a DPP source lane
-                        // must be active), then each lane picks
-                        const uint32_t x0 = sv[u][hh][0][d], x1 = sv[u][hh][1][d];
-                        const uint32_t up = dpp_u32<DPP_ROW_SHR4>(0u, x1);
-                        const uint32_t dn = dpp_u32<DPP_ROW_SHL4>(0u, x0);
-                        const uint32_t n0 = hi2 ? up : x0;
-                        const uint32_t n1 = hi2 ? x1 : dn;
-                        t0[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)n0);
-                        t1[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)n1);
-                    }
-                    a[u][2 * hh] = __builtin_bit_cast(frag_t, t0);
-                    a[u][2 * hh + 1] = __builtin_bit_cast(frag_t, t1);
-                }
-            }
-        }
+    // a list entry is always a key of the prefix; past the list the slot
+    // holds stale LDS words: the clamp keeps every gather inside the tensor,
+    // and scores past nc are never read
+    auto mfma_store = [&](int b0, const frag_t (&a)[4][NKS]) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             f32x4_t acc = f32x4_t{};
@@ -1778,6 +1715,93 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
                 *(uint4 *)dst = make_uint4(score_key(acc[0]), score_key(acc[1]), score_key(acc[2]),
                                            score_key(acc[3]));
             }
+        }
+    };
+    if constexpr (!LINES) {
+        // MFMA-layout loads (16-byte pieces, lanes 16 apart): fp32, and
+        // single-query blocks, whose many resident wavefronts hide the
+        // latency better than the rearrangement below pays
+        for (int b0 = 4 * w; b0 < nblocks; b0 += 4 * p.nqw) {
+            frag_t a[4][NKS];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int pidx = (b0 + u) * 16 + qcol;
+                const uint32_t c = min(cl[pidx], (uint32_t)(n - 1));
+                const T *kr = Kx + ((kbase + c) * p.H + h) * (int64_t)D;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    a[u][ks] = *(const frag_t *)(kr + (F32 ? 16 * ks + 4 * lq : 32 * ks + 8 * lq));
+            }
+            mfma_store(b0, a);
+        }
+    } else {
+        static_assert(!F32, "whole-line gathers are for bf16 keys");
+        // Loads: 8 consecutive lanes read one whole 128-byte line of a key
+        // row (the memory pipeline merges consecutive lanes only; the MFMA
+        // layout would put 16 rows and 64 bytes of each in one load, as
+        // 16-byte pieces of lanes 16 apart). Load (h, g), lane l: line h,
+        // 16-byte chunk l & 7 of block row 2 (l >> 3) + g. The next step's
+        // loads are issued before this step's rearrangement and MFMA.
+        constexpr int NL = D / 64;  // 128-byte lines per key row
+        typedef u32x4_t step_t[4][NL][2];
+        auto load_step = [&](int b0, step_t &sv) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const int pidx = (b0 + u) * 16 + 2 * (l >> 3) + g;
+                    const uint32_t c = min(cl[pidx], (uint32_t)(n - 1));
+                    const T *kr = Kx + ((kbase + c) * p.H + h) * (int64_t)D + 8 * (l & 7);
+#pragma unroll
+                    for (int hh = 0; hh < NL; ++hh) sv[u][hh][g] = *(const u32x4_t *)(kr + 64 * hh);
+                }
+            }
+        };
+        // Into the MFMA layout (MFMA 2 h + q, lane 16 j + i: block row i,
+        // chunk 4 q + j of line h): the two row halves trade across lane bit
+        // 2 (DPP row shifts by 4), so that the register index becomes the
+        // chunk's bit 2, then lane 16 j + i takes lane 4 i + j's word
+        // (bpermute).
+        const bool hi2 = (l & 4) != 0;
+        const int from = (((l & 15) << 2) | (l >> 4)) << 2;
+        auto compute_step = [&](int b0, const step_t &sv) {
+            frag_t a[4][NKS];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int hh = 0; hh < NL; ++hh) {
+                    u32x4_t t0, t1;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        // the shifts run on every lane (a DPP source lane
+                        // must be active), then each lane picks
+                        const uint32_t x0 = sv[u][hh][0][d], x1 = sv[u][hh][1][d];
+                        const uint32_t up = dpp_u32<DPP_ROW_SHR4>(0u, x1);
+                        const uint32_t dn = dpp_u32<DPP_ROW_SHL4>(0u, x0);
+                        const uint32_t n0 = hi2 ? up : x0;
+                        const uint32_t n1 = hi2 ? x1 : dn;
+                        t0[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)n0);
+                        t1[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)n1);
+                    }
+                    a[u][2 * hh] = __builtin_bit_cast(frag_t, t0);
+                    a[u][2 * hh + 1] = __builtin_bit_cast(frag_t, t1);
+                }
+            }
+            mfma_store(b0, a);
+        };
+        const int stride = 4 * p.nqw;
+        step_t svA, svB;
+        int b0 = 4 * w;
+        if (b0 < nblocks) load_step(b0, svA);
+        while (b0 < nblocks) {
+            const int b1 = b0 + stride;
+            if (b1 < nblocks) load_step(b1, svB);
+            compute_step(b0, svA);
+            if (b1 >= nblocks) break;
+            const int b2 = b1 + stride;
+            if (b2 < nblocks) load_step(b2, svA);
+            compute_step(b1, svB);
+            b0 = b2;
         }
     }
     __syncthreads();
