@@ -1255,8 +1255,9 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
     //    0.9 * count * 2048 / nt (rounded down instead when that
     //    overshoots 2048 in all), at least 2^(sh1 - 20) so that a key's
     //    bits inside its fine bucket fit LOWB bits, at most 2^sh1. Table
-    //    word = fine base | log2(n) << 12 (an empty bin at or above b1:
-    //    the running base | 1 << 17).
+    //    word = fine base | (sh1 - log2(n)) << 12 | (fine base + n - 1)
+    //    << 18, the last fine bucket of the bin (an empty bin at or above
+    //    b1: the running base | 1 << 17).
     const uint32_t lgmin = sh1 > LOWB ? (uint32_t)(sh1 - LOWB) : 0u;
     const float scl = (float)(REF_NB * 9 / 10) / (float)nt;
     for (int round_down = 0; round_down < 2; ++round_down) {
@@ -1287,7 +1288,8 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
             const uint32_t bin = NC - CPL * (l + 1) + i;
             // empty bins at or above b1 take no bucket but keep the base
             // running, so bases never increase with the bin
-            mine[i] = lg != 0xFFu ? (run | (lg << 12)) : (bin >= b1 ? (run | (1u << 17)) : 0xFFFFFFFFu);
+            mine[i] = lg != 0xFFu ? (run | (((uint32_t)sh1 - lg) << 12) | ((run + (1u << lg) - 1u) << 18))
+                                  : (bin >= b1 ? (run | (1u << 17)) : 0xFFFFFFFFu);
             if (lg != 0xFFu) run += 1u << lg;
         }
         if (l == 63) vars[2] = run;  // fine buckets in use
@@ -1306,8 +1308,8 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
             else lo = mid + 1;
         }
         const uint32_t t = h1[lo];
-        const uint32_t lg = (t >> 12) & 31u;
-        const uint32_t sub = ((uint32_t)sh1 - lg) & 31u;
+        const uint32_t sub = (t >> 12) & 31u;
+        const uint32_t lg = (uint32_t)sh1 - sub;
         const uint32_t top = (1u << lg) - 1u - (fb - (t & 0xFFFu));
         const uint32_t low = (top << sub) | (w & ((1u << sub) - 1u));
         return klo + (lo << sh1) + low;
@@ -1315,17 +1317,20 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
     if (vars[2] <= (uint32_t)REF_NB) {
         // packed word of a key: fine bucket << 20 | its bits inside the
         // fine bucket (0 = best bucket); 0xFFFFFFFF when not wanted
-        // (below the range, below b1, or an empty slot)
-        auto packed = [&](uint32_t k) -> uint32_t {
+        // (below the range, below b1, or an empty slot). f = the counter
+        // the key goes to: its fine bucket, or the lane's trash counter.
+        const uint32_t trash_f = (uint32_t)(REF_NB + 2 * l);
+        auto packed = [&](uint32_t k, uint32_t &f) -> uint32_t {
             const uint32_t rel = k - klo;
             const uint32_t bin = rel >> sh1;
             const uint32_t t = h1[min(bin, (uint32_t)(NC - 1))];
-            const uint32_t lg = (t >> 12) & 31u;
-            const uint32_t sub = ((uint32_t)sh1 - lg) & 31u;
+            const uint32_t sub = (t >> 12) & 31u;
             const uint32_t low = rel & ((1u << sh1) - 1u);
-            const uint32_t w =
-                (((t & 0xFFFu) + ((1u << lg) - 1u - (low >> sub))) << 20) | (low & ((1u << sub) - 1u));
-            return (k < klo || bin < b1) ? 0xFFFFFFFFu : w;
+            const uint32_t fb = (t >> 18) - (low >> sub);
+            const uint32_t w = (fb << 20) | (low & ((1u << sub) - 1u));
+            const bool ok = k >= klo && bin >= b1;
+            f = ok ? fb : trash_f;
+            return ok ? w : 0xFFFFFFFFu;
         };
         // -- 3. fine histogram, crossing, offsets. From here on each key
         //    register holds its packed word (every slot, so empty ones
@@ -1336,9 +1341,8 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
             if (e < e4) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const uint32_t w = packed(key[4 * e + v]);
-                    key[4 * e + v] = w;
-                    const uint32_t f = w == 0xFFFFFFFFu ? (uint32_t)(REF_NB + 2 * l) : (w >> 20);
+                    uint32_t f;
+                    key[4 * e + v] = packed(key[4 * e + v], f);
                     atomicAdd(&h2[f >> 1], 1u << ((f & 1u) << 4));
                 }
             } else {
