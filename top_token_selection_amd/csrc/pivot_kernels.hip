@@ -1176,32 +1176,46 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
     uint32_t *h2 = h1 + NC + 64;                  // fine counters, two per word
     uint32_t *vars = h2 + REF_NB / 2 + 64;
     uint32_t *buf = (uint32_t *)(my + REF_HDR);   // ref_cap staged entries
-    uint32_t mx = 0u, mnm1 = 0xFFFFFFFFu;
+    uint32_t mx = 0u;
 #pragma unroll
     for (int e = 0; e < E / 4; ++e)
         if (e < e4) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint32_t k = key[4 * e + v];
-                mx = max(mx, k);
-                mnm1 = min(mnm1, k - 1u);  // empty slots (0) wrap to the top
-            }
+            for (int v = 0; v < 4; ++v) mx = max(mx, key[4 * e + v]);
         }
     mx = wave_max(mx);
-    const uint32_t mn = wave_min(mnm1) + 1u;
-    uint32_t klo = mn;
+    // the smallest key (empty slots, 0, wrap to the top): only when the
+    // sampled lower end is not used or not below the msel-th key
+    auto min_key = [&]() -> uint32_t {
+        uint32_t mnm1 = 0xFFFFFFFFu;
+#pragma unroll
+        for (int e = 0; e < E / 4; ++e)
+            if (e < e4) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) mnm1 = min(mnm1, key[4 * e + v] - 1u);
+            }
+        return wave_min(mnm1) + 1u;
+    };
+    uint32_t klo;
     {
         const float pf = (float)msel / (float)nc;
         const int rs = (int)ceilf(64.f * pf + 4.f * sqrtf(64.f * pf * (1.f - pf))) + 2;
         if (nc >= 64 && rs <= 64) {
-            uint32_t rk = 0;
+            // the rs-th largest sample: a bitonic sort of the 64 samples,
+            // largest in lane 0
+            uint32_t v = smp;
 #pragma unroll
-            for (int m = 0; m < 64; ++m) {
-                const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)smp, m);
-                rk += (o > smp || (o == smp && m < l)) ? 1u : 0u;
+            for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+                for (int jj = k >> 1; jj > 0; jj >>= 1) {
+                    const uint32_t o = (uint32_t)__shfl_xor((int)v, jj);
+                    const bool keep_max = ((l & k) == 0) == ((l & jj) == 0);
+                    v = keep_max ? max(v, o) : min(v, o);
+                }
             }
-            const unsigned long long bal = __ballot(rk == (uint32_t)(rs - 1));
-            klo = (uint32_t)__builtin_amdgcn_readlane((int)smp, (int)__builtin_ctzll(bal));
+            klo = (uint32_t)__builtin_amdgcn_readlane((int)v, rs - 1);
+        } else {
+            klo = min_key();
         }
     }
     // lane l owns coarse bins [NC - CPL (l + 1), NC - CPL l), the top first
@@ -1249,7 +1263,7 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
         b1 = vars[0];
         nt = vars[1];
         if (b1 != 0xFFFFFFFFu) break;
-        klo = mn;  // the sample was not below the msel-th key
+        klo = min_key();  // the sample was not below the msel-th key
     }
     // -- 2. fine buckets per coarse bin: n = the power of two nearest to
     //    0.9 * count * 2048 / nt (rounded down instead when that
@@ -1405,8 +1419,10 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
                     uint32_t got[8], fb[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
+                        // a word of a key not wanted (all ones) has bucket
+                        // 4095, past every fine bucket
                         const uint32_t w = key[4 * e0 + i];
-                        fb[i] = (w == 0xFFFFFFFFu || (w >> 20) > fstar) ? trashf : (w >> 20);
+                        fb[i] = (w >> 20) > fstar ? trashf : (w >> 20);
                         got[i] = atomicAdd(&h2[fb[i] >> 1], 1u << ((fb[i] & 1u) << 4));
                     }
 #pragma unroll
