@@ -1631,8 +1631,9 @@ __global__ void __launch_bounds__(64 * SW_WAVES) k_select_wave(SelParams p) {
             if (row && (p.o.top_k & 3) == 0 && ((uintptr_t)dst0 & 15u) == 0) {
                 const int nv4 = (int)(msel & ~3u);
                 for (int c = 4 * l; c < nv4; c += 256) {
-                    const uint4 v = *(const uint4 *)(row + c);
-                    for (int t = 0; t < m; ++t) *(uint4 *)(dst0 + t * rstride + c) = v;
+                    const u32x4_t v = *(const u32x4_t *)(row + c);
+                    // rows are not read again here: nontemporal stores
+                    for (int t = 0; t < m; ++t) __builtin_nontemporal_store(v, (u32x4_t *)(dst0 + t * rstride + c));
                 }
                 cs0 = nv4;
             }
@@ -1862,7 +1863,10 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
                 int cs0 = row ? 0 : (int)msel;
                 if (row && ((uintptr_t)dst & 15u) == 0) {
                     const int nv4 = (int)(msel & ~3u);
-                    for (int c = 4 * l; c < nv4; c += 256) *(uint4 *)(dst + c) = *(const uint4 *)(row + c);
+                    // output rows are not read again here: nontemporal
+                    // stores keep the cache for the candidate gathers
+                    for (int c = 4 * l; c < nv4; c += 256)
+                        __builtin_nontemporal_store(*(const u32x4_t *)(row + c), (u32x4_t *)(dst + c));
                     cs0 = nv4;
                 }
                 for (int c = cs0 + l; c < p.top_k; c += 64) dst[c] = c < (int)msel ? (int32_t)row[c] : -1;
