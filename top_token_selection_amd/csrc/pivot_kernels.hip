@@ -1346,6 +1346,7 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
             f = ok ? fb : trash_f;
             return ok ? w : 0xFFFFFFFFu;
         };
+        uint32_t cmax;  // largest count of the buckets up to fstar this lane scans
         // -- 3. fine histogram, crossing, offsets. From here on each key
         //    register holds its packed word (every slot, so empty ones
         //    read as "not wanted" in all passes); unpack() gives the key
@@ -1369,6 +1370,7 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
         {
             uint32_t *fw = h2 + (REF_NB / 128) * l;  // lane l: fine buckets 32 l .. 32 l + 31
             uint32_t loc = 0;
+            cmax = 0u;
 #pragma unroll
             for (int i = 0; i < REF_NB / 512; ++i) {
                 const uint4 c4 = *(const uint4 *)(fw + 4 * i);
@@ -1384,6 +1386,7 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     const uint32_t c = (w4[t >> 1] >> ((t & 1) << 4)) & 0xFFFFu;
+                    if (run < msel) cmax = max(cmax, c);  // buckets 0 .. fstar only
                     if (t & 1) o4[t >> 1] |= run << 16;
                     else o4[t >> 1] = run;
                     if (run < msel && msel <= run + c) {
@@ -1398,6 +1401,7 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
         wave_lds_sync();
         const uint32_t fstar = vars[3];
         const uint32_t nsc = vars[4];
+        const uint32_t bmax = wave_max(cmax);  // the largest staged bucket
         // h1 (the table, dead once every key is packed) then holds a 16-bit
         // bucket tag per staged entry; h1..h2 (dead once every rank is
         // known) then hold the finished row.
@@ -1487,8 +1491,12 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
             const uint32_t tr = (uint32_t)(A[NW - 1] >> (32 + LOWB));
             const bool edge = own && ((tl != 0u && tl == tf) || (tb <= (uint32_t)REF_NB && tb == tr));
             if (__ballot(edge) == 0ull) {
-                for (int it = 0; it <= NW / 2; ++it) {
-                    bool sw = false;
+                // entries only move inside their bucket, and odd-even
+                // transposition orders m entries in m phases: ceil(bmax / 2)
+                // rounds of both parities order every bucket (no test
+                // round); more are never needed than the window holds
+                const int rounds = (int)min((bmax + 1u) / 2u, (uint32_t)(NW / 2 + 1));
+                for (int it = 0; it < rounds; ++it) {
 #pragma unroll
                     for (int par = 0; par < 2; ++par) {
 #pragma unroll
@@ -1497,10 +1505,8 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
                             const uint64_t a = A[i];
                             A[i] = c ? A[i + 1] : a;
                             A[i + 1] = c ? a : A[i + 1];
-                            sw |= c;
                         }
                     }
-                    if (__ballot(sw) == 0ull) break;
                 }
                 wave_lds_sync();
                 // -- 6. finished row into LDS (every lane stores its whole
