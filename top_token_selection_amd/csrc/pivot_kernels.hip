@@ -81,37 +81,11 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb) {
     return x * per + min(x, rem) + i;
 }
 
-// s_waitcnt on the vector-memory counter alone: wait until at most N
-// vector memory instructions of the wavefront are outstanding (they retire
-// in issue order). Expcnt and lgkmcnt fields at their maxima (no wait).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// wait_vmcnt<n> for a run-time n: values above 16 wait as for 16 (more
-// than asked, never less)
-__device__ __forceinline__ void wait_vmcnt_upto16(uint32_t n) {
-    switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 13: wait_vmcnt<13>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    case 15: wait_vmcnt<15>(); break;
-    default: wait_vmcnt<16>(); break;
-    }
+// s_waitcnt on the LDS counter alone: wait until every LDS access of the
+// wavefront is done (vmcnt and expcnt fields at their maxima: no wait on
+// vector memory).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
 __device__ __forceinline__ int64_t prefix_len(int64_t j, int g) {
@@ -208,16 +182,18 @@ struct ScanParams {
 // i.e. one group, for 16 keys -- its threshold and running survivor count
 // stay in registers. Two blocks share a CU.
 //
-// Key tiles go from global memory straight into LDS (global_load_lds, lane i
-// of an instruction lands at base + 16 i), double-buffered, with the 16-byte
-// chunks of a key row XOR-swizzled by the row so that the fragment reads
+// Key tiles are loaded into registers two steps ahead (the keys of a head
+// are shared by the blocks of its groups, which are not in step: many loads
+// miss the L2), then written to one of two LDS buffers with the 16-byte
+// chunks of a key row XOR-swizzled by the row, so that the fragment reads
 // spread over the banks. One step, for tile kt:
-//   wait for own loads of tile kt, barrier  (tile kt is in LDS)
-//   issue the loads of tile kt+1            (into the buffer of tile kt-1)
+//   barrier                                 (tile kt is in LDS)
+//   tile kt+1 from registers into LDS       (the buffer of tile kt-1)
+//   issue the loads of tile kt+3            (into tile kt+1's registers)
 //   matrix work on tile kt
 //   filter tile kt-1's scores (survivor stores)
-// so loads have a whole step to complete before their wait, and stores are
-// never waited for in the loop.
+// so loads have two whole steps to complete before their wait, and stores
+// are never waited for in the loop.
 //
 // Survivors ((float bits, key) pairs) of each (row, half) stream are staged
 // in an LDS ring of RING entries and leave in whole 64-byte chunks of FLUSH
@@ -312,22 +288,29 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     const uint32_t kstr = (uint32_t)p.kstride;
     const uint32_t lane_key = (uint32_t)p.koff + kstr * (uint32_t)(4 * half);
 
-    // tile kt into LDS buffer kt & 1: instruction i of wavefront w fills
-    // slots (i*4 + w)*64 .. +63; slot q holds chunk (q % NCK) ^ swz(row) of
-    // key row q / NCK. Keys past the last row's prefix repeat the last key:
-    // their scores are never kept (that tile takes the causal test).
-    auto issue_tile = [&](int kt) {
+    // tile kt, staged through registers: piece i of a thread is 16-byte
+    // chunk c = q % NCK of key row r = q / NCK of the tile, q = (4 i + w) 64
+    // + l (consecutive lanes read consecutive chunks of a row), and goes to
+    // LDS buffer kt & 1 at slot r NCK + (c ^ swz(r)): slot (r, pos) holds
+    // chunk pos ^ swz(r). Keys past the last row's prefix repeat the last
+    // key: their scores are never kept (that tile takes the causal test).
+    typedef u32x4_t piece_t[NLD];
+    auto load_tile = [&](int kt, piece_t &pr) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            const int blk = i * (SCAN_THREADS / 64) + w;
-            const int q = blk * 64 + l;
-            const int r = q / NCK, pos = q % NCK;
-            const int c = pos ^ (r & SWZ);
+            const int q = (i * (SCAN_THREADS / 64) + w) * 64 + l;
+            const int r = q / NCK, c = q % NCK;
             const int64_t v = min((int64_t)kt * SCAN_KEYS + r, vmax - 1);
             const int64_t key = p.koff + (int64_t)p.kstride * v;
-            __builtin_amdgcn_global_load_lds((const void *)(Kb + key * krow_bytes + c * 16),
-                                             (__attribute__((address_space(3))) void *)(smem + (kt & 1) * TILE + blk * 1024),
-                                             16, 0, 0);
+            pr[i] = *(const u32x4_t *)(Kb + key * krow_bytes + c * 16);
+        }
+    };
+    auto store_tile = [&](int kt, const piece_t &pr) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int q = (i * (SCAN_THREADS / 64) + w) * 64 + l;
+            const int r = q / NCK, c = q % NCK;
+            *(u32x4_t *)(smem + (kt & 1) * TILE + (r * NCK + (c ^ (r & SWZ))) * 16) = pr[i];
         }
     };
 
@@ -356,39 +339,39 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
         }
     };
 
-    uint32_t nst = 0;  // survivor store instructions since the last tile's loads
     // Every stream of column block gb with FLUSH or more staged survivors
     // sends its FLUSH oldest (entries fl .. fl+7, ring rows fl % RING ..)
-    // as one 64-byte chunk. The streams are ranked; the r-th one's lane and
-    // flushed count go to lane 4r (forward permute, no LDS memory) and over
-    // its quad (DPP), and lane 4r + q stores entries fl + 2q, fl + 2q + 1:
-    // an instruction writes 16 whole chunks. At most cap_half + 16 are ever
-    // kept, inside the stream's stride. Wavefront-uniform control flow.
+    // as one 64-byte chunk. The streams are ranked; the r-th one passes its
+    // chunk's byte offset in the survivor array and its lane with the
+    // chunk's first ring row to lane 4r (forward permute, no LDS memory)
+    // and over its quad (DPP), and lane 4r + q stores entries fl + 2q,
+    // fl + 2q + 1: an instruction writes 16 whole chunks. At most cap_half
+    // + 16 are ever kept, inside the stream's stride. Wavefront-uniform
+    // control flow.
+    static_assert(RING % FLUSH == 0, "a chunk's ring rows do not wrap");
     auto flush = [&](int gb) {
-        // counts its store instructions in nst: one per pass below (the
-        // pass's first quad always stores)
         const bool need = cs[gb] / RROW - fl[gb] >= (uint32_t)FLUSH;
         const uint64_t M = __ballot(need);
         if (M == 0) return;
         const uint32_t rank =
             __builtin_amdgcn_mbcnt_hi((uint32_t)(M >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)M, 0u));
         const int nf = __popcll(M);
+        const uint32_t mydst = soff0[gb] + fl[gb] * 8u;
+        const uint32_t mysrc = (uint32_t)l | ((fl[gb] % RING) << 6);
         for (int r0 = 0; r0 < nf; r0 += 16) {
             // senders target lane 4 (rank - r0); the others an odd lane
             const bool mine = need && rank - (uint32_t)r0 < 16u;
             const int to = mine ? (int)(rank - (uint32_t)r0) * 16 : (l | 1) * 4;
-            const uint32_t sid = dpp_u32<0x00>(0u, (uint32_t)__builtin_amdgcn_ds_permute(to, l));
-            const uint32_t sfl = dpp_u32<0x00>(0u, (uint32_t)__builtin_amdgcn_ds_permute(to, (int)fl[gb]));
+            const uint32_t sdst = dpp_u32<0x00>(0u, (uint32_t)__builtin_amdgcn_ds_permute(to, (int)mydst));
+            const uint32_t ssrc = dpp_u32<0x00>(0u, (uint32_t)__builtin_amdgcn_ds_permute(to, (int)mysrc));
             if ((l >> 2) < nf - r0) {
-                const uint32_t e = sfl + 2u * (uint32_t)(l & 3);
-                const uint32_t *src = ringS + gb * SCAN_THREADS + w * 64 + (int)sid;
-                const uint32_t ia = (e % RING) * NSTREAM, ib = ((e + 1) % RING) * NSTREAM;
+                const uint32_t q2 = 2u * (uint32_t)(l & 3);
+                const uint32_t *src = ringS + gb * SCAN_THREADS + w * 64 + (int)(ssrc & 63u);
+                const uint32_t ia = ((ssrc >> 6) + q2) * NSTREAM, ib = ia + NSTREAM;
                 const uint2 a = make_uint2(src[ia], src[ia + RKEYS]);
                 const uint2 b = make_uint2(src[ib], src[ib + RKEYS]);
-                const uint32_t so = (uint32_t)(((64 * w + 32 * gb + (int)(sid & 31)) * 2 + (int)(sid >> 5)) * p.stride) * 8u;
-                *(uint4 *)(sb + so + e * 8u) = make_uint4(a.x, a.y, b.x, b.y);
+                *(uint4 *)(sb + (sdst + 8u * q2)) = make_uint4(a.x, a.y, b.x, b.y);
             }
-            ++nst;
         }
         fl[gb] += need ? (uint32_t)FLUSH : 0u;
     };
@@ -435,32 +418,42 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
         else run(std::true_type{});
     };
 
-    // The loads of tile kt were the last vector-memory instructions before
-    // the nst survivor stores of the previous step's filter: waiting for at
-    // most nst outstanding completes the tile and leaves the stores in
-    // flight. After the barrier every wavefront is done with tile kt-1, so
-    // tile kt+1 may load into its buffer.
-    auto step = [&](int kt, const acc_t &prev, acc_t &cur) {
-        wait_vmcnt_upto16(__builtin_amdgcn_readfirstlane(nst));  // nst is wavefront-uniform
-        nst = 0;
+    // Two tiles are in flight in registers while a third is in LDS. Step
+    // kt: the barrier (after this wavefront's LDS writes are done) makes
+    // tile kt, written by every wavefront in the previous step, readable,
+    // and frees the buffer of tile kt-1; tile kt+1 (loaded two steps ago)
+    // goes there, and its registers take the loads of tile kt+3. The
+    // compiler waits for exactly those loads before the LDS writes, so
+    // survivor stores issued since are never waited for.
+    auto step = [&](int kt, const acc_t &prev, acc_t &cur, piece_t &nxt) {
+        wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
-        if (kt + 1 < ntiles_k) issue_tile(kt + 1);
+        // unconditional (tiles past the last repeat its last key), so that
+        // the compiler's count of loads in flight is exact
+        store_tile(kt + 1, nxt);
+        load_tile(kt + 3, nxt);
         matrix(kt, cur);
         if (kt > 0) filter(kt - 1, prev);
     };
-    // every proxy fragment has arrived before the loop: the loop then waits
-    // on its own loads and stores only. Even tiles accumulate in accA, odd
-    // ones in accB (two steps per iteration keep the names static).
+    // every proxy fragment has arrived before the loop. Even tiles
+    // accumulate in accA and stage in pA, odd ones in accB and pB (two
+    // steps per iteration keep the names static).
     __builtin_amdgcn_s_waitcnt(0);
     acc_t accA, accB;
-    if (ntiles_k > 0) issue_tile(0);
+    piece_t pA, pB;
+    if (ntiles_k > 0) {
+        load_tile(0, pA);
+        load_tile(1, pB);
+        store_tile(0, pA);
+        load_tile(2, pA);
+    }
     int kt = 0;
     for (; kt + 2 <= ntiles_k; kt += 2) {
-        step(kt, accB, accA);
-        step(kt + 1, accA, accB);
+        step(kt, accB, accA, pB);
+        step(kt + 1, accA, accB, pA);
     }
     if (kt < ntiles_k) {
-        step(kt, accB, accA);
+        step(kt, accB, accA, pB);
         filter(kt, accA);
     } else if (ntiles_k > 0) {
         filter(ntiles_k - 1, accB);
