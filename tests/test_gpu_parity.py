@@ -58,6 +58,9 @@ EXACT_CASES = [
     (2100, 1, 128, 100, 8, 2.0, "bf16"),  # > 8 scan tiles, rows that need sampling
     (1500, 3, 128, 37, 8, 2.0, "bf16"),   # odd top_k: output rows off 16-byte alignment
     (900, 2, 64, 101, 4, 1.5, "f32"),     # odd top_k and K = floor(151.5)
+    (800, 2, 128, 50, 8, 1.0, "bf16"),    # ratio 1: K = top_k
+    (1200, 2, 128, 30, 8, 4.0, "bf16"),   # ratio 4: K = 4 top_k
+    (2000, 2, 64, 48, 32, 2.0, "bf16"),   # g = 32: four blocks of 8 members per group
 ]
 
 
