@@ -69,6 +69,12 @@ template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
+// v of another lane by DPP, 0 where the source lane is outside the row
+// (bound_ctrl): there is no old value to keep, so no register is set first
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_zero(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
 constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
 constexpr int DPP_ROW_SHL4 = 0x104;
 constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;

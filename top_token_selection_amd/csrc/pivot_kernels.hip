@@ -1796,8 +1796,8 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
                         // the shifts run on every lane (a DPP source lane
                         // must be active), then each lane picks
                         const uint32_t x0 = sv[u][hh][0][d], x1 = sv[u][hh][1][d];
-                        const uint32_t up = dpp_u32<DPP_ROW_SHR4>(0u, x1);
-                        const uint32_t dn = dpp_u32<DPP_ROW_SHL4>(0u, x0);
+                        const uint32_t up = dpp_zero<DPP_ROW_SHR4>(x1);
+                        const uint32_t dn = dpp_zero<DPP_ROW_SHL4>(x0);
                         const uint32_t n0 = hi2 ? up : x0;
                         const uint32_t n1 = hi2 ? x1 : dn;
                         t0[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(from, (int)n0);
