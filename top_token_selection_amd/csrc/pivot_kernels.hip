@@ -218,10 +218,18 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     static_assert((RING & (RING - 1)) == 0 && (RROW & (RROW - 1)) == 0, "ring sizes are powers of two");
     static_assert(FLUSH == 8, "a chunk is four lanes' 16-byte stores");
 
+    // Heads go to XCDs in groups of ceil(Hc / 8) (each XCD's contiguous range
+    // of logical blocks then covers about one group, whose blocks share the
+    // keys in its L2), and inside a group the tiles run longest first across
+    // all of its heads, so that no long tile starts late.
     const int nb = p.Hc * p.n_tiles;
     const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)nb);
-    const int hl = (int)(L / p.n_tiles);
-    const int tile = p.n_tiles - 1 - (int)(L % p.n_tiles);  // longest first
+    const int hg = (p.Hc + 7) / 8;                      // heads per group
+    const int grp = (int)(L / (uint32_t)(hg * p.n_tiles));
+    const int in_grp = (int)(L % (uint32_t)(hg * p.n_tiles));
+    const int hgc = min(hg, p.Hc - grp * hg);           // heads of this group
+    const int hl = grp * hg + in_grp % hgc;
+    const int tile = p.n_tiles - 1 - in_grp / hgc;      // longest first
     const int64_t j0 = (int64_t)tile * SCAN_ROWS;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int half = l >> 5;
