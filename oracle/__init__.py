@@ -33,7 +33,7 @@ _lib = None
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
     if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
+        tmp = f"{_LIB_PATH}.tmp{os.getpid()}"
         subprocess.check_call([
             "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
             "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm",
@@ -69,6 +69,8 @@ def _load():
     lib.oracle_dense_rows.restype = ci
     lib.oracle_decode.argtypes = [vp, vp, ci, vp, i32, i32, i32, i32, i32, f64, ci, i32, i32, vp, vp]
     lib.oracle_decode.restype = ci
+    lib.oracle_decode_candidates.argtypes = [vp, vp, ci, vp, i32, i32, i32, i32, i32, f64, i32, i32, vp, vp]
+    lib.oracle_decode_candidates.restype = i64
     lib.oracle_sparse_attention.argtypes = [vp, vp, vp, ci, i64, i32, i32, vp, i32, f64, vp]
     lib.oracle_sparse_attention.restype = ci
     lib.oracle_sparse_attention_rows.argtypes = [vp, vp, vp, ci, i64, i32, i32, vp, i32, i64, vp, vp, f64, vp]
@@ -221,6 +223,26 @@ def decode(q, k_cache, ctx_lens, g, top_k=64, candidate_ratio=2.0, mode="refine"
                                  candidate_ratio, MODES[mode], hb, he, _ptr(idx), _ptr(sc)),
            "oracle_decode")
     return idx, sc
+
+
+def decode_candidates(q, k_cache, ctx_lens, g, h, b, top_k=64, candidate_ratio=2.0):
+    """Candidate set C (in total order, indices relative to the sequence) of
+    sequence b, head h of a decode step, with its proxy scores."""
+    q = np.ascontiguousarray(q)
+    kc = np.ascontiguousarray(k_cache)
+    if q.dtype != kc.dtype:
+        raise TypeError("q and k_cache must share a dtype")
+    ctx = np.ascontiguousarray(ctx_lens, np.int64)
+    B = ctx.shape[0]
+    rows, H, D = q.shape
+    K = candidate_count(top_k, candidate_ratio)
+    cand = np.empty(max(K, 1), np.int32)
+    sc = np.empty(max(K, 1), np.float32)
+    n = _load().oracle_decode_candidates(_ptr(q), _ptr(kc), _dtype_code(q), _ptr(ctx), B, g, H, D, top_k,
+                                         candidate_ratio, h, b, _ptr(cand), _ptr(sc))
+    if n < 0:
+        raise RuntimeError(f"oracle_decode_candidates failed with code {n}")
+    return cand[:n].copy(), sc[:n].copy()
 
 
 def sparse_attention(q, k, v, idx, scale=None):

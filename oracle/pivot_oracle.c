@@ -621,6 +621,46 @@ int oracle_decode(const void *q, const void *k_cache, int dt,
     return OR_OK;
 }
 
+/* Candidate set C of sequence b, head h of a decode step (layouts as for
+ * oracle_decode), in total order: writes min(K, ctx_b) indices relative to
+ * the sequence (and their proxy scores) and returns that count, or a
+ * negative error. */
+int64_t oracle_decode_candidates(const void *q, const void *k_cache, int dt,
+                                 const int64_t *ctx_lens, int32_t B, int32_t g,
+                                 int32_t H, int32_t D, int32_t top_k,
+                                 double candidate_ratio, int32_t h, int32_t b,
+                                 int32_t *out_cand, float *out_score)
+{
+    if (!q || !k_cache || !ctx_lens || !out_cand || B < 1 || g < 1 || H < 1 ||
+        D < 1 || top_k < 1 || (dt != OR_F32 && dt != OR_BF16) || h < 0 ||
+        h >= H || b < 0 || b >= B)
+        return OR_EINVAL;
+    int64_t K = oracle_candidate_count(top_k, candidate_ratio);
+    if (K < 0)
+        return OR_EINVAL;
+    int64_t off = 0;
+    for (int32_t t = 0; t < b; ++t)
+        off += ctx_lens[t];
+    int64_t n = ctx_lens[b];
+    if (n < 1)
+        return OR_EINVAL;
+    scored_t *cand = (scored_t *)malloc(sizeof(scored_t) * (size_t)min64(K, n));
+    if (!cand)
+        return OR_ENOMEM;
+    int64_t nc = 0;
+    int rc = one_group(q, k_cache, dt, H, D, top_k, K, OR_REUSE, h, (int64_t)b * g,
+                       g, off, n, NULL, NULL, 0, cand, &nc);
+    if (rc == OR_OK) {
+        for (int64_t t = 0; t < nc; ++t) {
+            out_cand[t] = cand[t].idx;
+            if (out_score)
+                out_score[t] = cand[t].score;
+        }
+    }
+    free(cand);
+    return rc ? rc : nc;
+}
+
 /* ---------------------------------------------- downstream sparse attention */
 
 /* The attention the pages run on the indices ("Show Me The Code", the quick

@@ -291,18 +291,109 @@ def test_tiny_workload_gaussian_tolerant(pv, mode):
     errs = []
     qv = q.astype(np.float64)
     for h in range(H):
+        kv_all = parity.key_values(k, h)
         for j in range(S // g):
+            n = max(j * g, 1)
             proxy = oracle.proxy(q, g, h, j).astype(np.float64)
-            cand = csc = None
+            cand = None
             if mode == "refine":
-                cand, csc = oracle.prefill_candidates(q, k, h, j, top_k, g, 2.0)
+                cand, _ = oracle.prefill_candidates(q, k, h, j, top_k, g, 2.0)
             for i in range(j * g, j * g + g):
                 avec = qv[i, h] if mode == "refine" else proxy
-                e = parity.tolerant_row_match(gi[i, h], gs[i, h], oi[i, h], os_[i, h], avec, k, h, D,
-                                              cand_idx=cand, cand_sc=csc, proxy=proxy)
+                e = parity.row_match(gi[i, h], gs[i, h], oi[i, h], os_[i, h], avec, kv_all[:n], proxy=proxy,
+                                     cand_idx=cand)
                 if e:
                     errs.append((i, h, e))
     assert not errs, errs[:5]
+
+
+# ------------------------------------------------- proxy rounding on the GPU
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_proxy_rounding_matches_hand_derived_values(pv, dtype):
+    """The proxies of tests/test_oracle_proxy_pins.py, read back through
+    Reuse scores: key c of the prefix is the unit vector e_c, so the proxy
+    score of key c is the proxy's component c, exactly. Group 1 (positions
+    8..15) holds the members whose float32 sums round (expected proxies 0,
+    0.5, 0.75, 0.75 by hand); a ragged group 2 (positions 16..18) holds
+    [5, 0, 0], whose float32 quotient is 0x3FD55555 (fp32) or 213/128 (bf16)."""
+    from tests.test_oracle_proxy_pins import SUM_MEMBERS, SUM_PROXY, DIV_BITS
+    S, H, D = 19, 1, 64
+    qf = np.zeros((S, H, D), np.float32)
+    qf[8:16, 0, :4] = SUM_MEMBERS
+    qf[16, 0, 0] = 5.0
+    kf = np.zeros((S, H, D), np.float32)
+    for c in range(16):
+        kf[c, 0, c] = 1.0
+    q = qf if dtype == "f32" else syn.to_bf16_bits(qf)
+    k = kf if dtype == "f32" else syn.to_bf16_bits(kf)
+    gi, gs = run_prefill(pv, q, k, 16, 8, 2.0, "reuse")
+    # group 1 sees keys 0..7: components 0..3 carry the sums, 4..7 are zero
+    want = {c: float(SUM_PROXY[c]) for c in range(4)}
+    want.update({c: 0.0 for c in range(4, 8)})
+    order = sorted(want, key=lambda c: (-want[c], c))
+    for i in range(8, 16):
+        np.testing.assert_array_equal(gi[i, 0, :8], order)
+        np.testing.assert_array_equal(gs[i, 0, :8], np.array([want[c] for c in order], np.float32))
+    # group 2 sees keys 0..15: component 0 is the quotient, the rest zero
+    for i in range(16, 19):
+        assert gi[i, 0, 0] == 0
+        if dtype == "f32":
+            assert int(gs[i, 0, 0:1].view(np.uint32)[0]) == DIV_BITS
+        else:
+            assert float(gs[i, 0, 0]) == 213.0 / 128.0
+
+
+# ------------------------------------------ top_k beyond the wavefront sorts
+
+LARGE_TOPK = [
+    # S, H, top_k, ratio, g: K = floor(top_k * ratio)
+    (9000, 2, 3000, 1.3, 8),   # K = 3900: selectors past the 2048-entry staging
+    (9000, 1, 4096, 1.0, 8),   # K = top_k = 4096: the largest K and top_k
+]
+
+
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+@pytest.mark.parametrize("S,H,top_k,ratio,g", LARGE_TOPK)
+def test_large_top_k_bit_exact_integer_inputs(pv, mode, S, H, top_k, ratio, g):
+    """top_k above 2048 against the oracle, bit for bit on integer inputs
+    (index-only and with scores)."""
+    from tests.oracle_pool import OraclePool
+    print(f"\n[large top_k] S={S} H={H} k={top_k} r={ratio} g={g} {mode}", flush=True)
+    D = 128
+    q = syn.integers((S, H, D), 7600 + top_k, 4, "bf16")
+    k = syn.integers((S, H, D), 7700 + top_k, 4, "bf16")
+    gi, gs = run_prefill(pv, q, k, top_k, g, ratio, mode)
+    only = pv.index_prefill(dev_tensor(q), dev_tensor(k), top_k=top_k, g=g, candidate_ratio=ratio, mode=mode)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(parity.to_host(only), gi)
+    with OraclePool() as pool:
+        res = pool.map([("prefill", dict(q=pool.put(q[:, h:h + 1]), k=pool.put(k[:, h:h + 1]), top_k=top_k, g=g,
+                                         candidate_ratio=ratio, mode=mode)) for h in range(H)])
+    for h, (oi, os_) in enumerate(res):
+        np.testing.assert_array_equal(gi[:, h], oi[:, 0], err_msg=f"head {h}")
+        np.testing.assert_array_equal(gs[:, h], os_[:, 0], err_msg=f"head {h}")
+
+
+@pytest.mark.parametrize("mode", ["refine", "reuse"])
+@pytest.mark.parametrize("top_k,ratio,g", [(3000, 1.3, 2), (4096, 1.0, 4)])
+def test_decode_large_top_k_bit_exact_integer_inputs(pv, mode, top_k, ratio, g):
+    print(f"\n[decode large top_k] k={top_k} r={ratio} g={g} {mode}", flush=True)
+    H, D = 2, 128
+    ctx = np.array([9000, 3100, 12000, 4096, 1], np.int64)
+    B = len(ctx)
+    kc = syn.integers((int(ctx.sum()), H, D), 7800 + top_k, 4, "bf16")
+    q = syn.integers((B * g, H, D), 7900 + top_k, 4, "bf16")
+    for scores in (True, False):
+        r = pv.index_decode(dev_tensor(q), dev_tensor(kc), ctx, g, top_k=top_k, candidate_ratio=ratio, mode=mode,
+                            return_scores=scores)
+        torch.cuda.synchronize()
+        oi, os_ = oracle.decode(q, kc, ctx, g, top_k, ratio, mode)
+        if scores:
+            np.testing.assert_array_equal(parity.to_host(r[0]), oi)
+            np.testing.assert_array_equal(parity.to_host(r[1]), os_)
+        else:
+            np.testing.assert_array_equal(parity.to_host(r), oi)
 
 
 # ------------------------------- literal per-position Refine (comparison)

@@ -1,22 +1,27 @@
-"""GPU parity at the full workload sizes, on sampled rows the oracle
-computes one by one (in the same launch configuration the bench times).
+"""GPU parity at the full workload sizes, in the launch configuration the
+bench times (index-only rows, the wavefront selectors), against the oracle
+run over the host's cores (tests/oracle_pool.py).
 
   * S=16384, H=16, D=128 bf16 integers in [-4, 4], top_k=512, g=8, K=1024:
-    every float32 score is exact, so sampled rows are compared bit for bit;
-    every row's structure (padding, causality, uniqueness) is checked.
-  * S=65536, H=64 and S=131072, H=32 (D=128 bf16, AR(1) queries,
-    Pareto-norm keys, top_k=2048, K=4096): sampled rows, tie-tolerant.
+    every float32 score is exact, so every row of every head is compared
+    bit for bit with the oracle, for the index-only launch and for the
+    launch that also returns scores.
+  * S=65536, H=64, g=8 (heads 0 and 37) and S=131072, H=32, g=16 (heads 0
+    and 19), D=128 bf16, AR(1) queries, Pareto-norm keys, top_k=2048,
+    K=4096: at least 1024 rows per head (whole groups) against the oracle,
+    tie-tolerantly; every row of the tensor is checked for structure, and
+    the index-only launch equals the scored one in every row.
   * decode: 64 sequences with contexts U[32768, 131072], H=8, g in {2, 4}:
-    every sequence of one head against the oracle, tie-tolerant.
+    every row of every head against the oracle, tie-tolerantly.
 """
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
-import oracle
 import synthetic as syn
 from tests import parity
+from tests.oracle_pool import OraclePool
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -36,177 +41,180 @@ def to_dev(a):
     return torch.from_numpy(a).to(DEV)
 
 
+def head_bits(t, h):
+    """Host bf16 bits of head h of a device (rows, H, D) tensor, as (rows, 1, D)."""
+    return syn.bf16_tensor_to_bits(t[:, h:h + 1].contiguous())
+
+
+def prefill_valid(S, H, g, top_k, K, mode):
+    i = torch.arange(S, device=DEV, dtype=torch.int64)
+    lim = torch.clamp((i // g) * g, min=1)
+    val = torch.clamp(lim, max=min(top_k, K) if mode == "refine" else top_k)
+    return val.repeat_interleave(H), lim.repeat_interleave(H)
+
+
+# ------------------------------------------------- integer workload (bit-exact)
+
 @pytest.mark.parametrize("mode", ["refine", "reuse"])
-def test_int_workload_sampled_rows_bit_exact(pv, mode):
-    print(f"\n[int workload] S=16384 H=16 {mode}", flush=True)
+def test_int_workload_every_row_bit_exact(pv, mode):
+    print(f"\n[int workload] S=16384 H=16 {mode}: every row of every head", flush=True)
     cfg = syn.int_prefill()
     q, k, top_k, g = cfg["q"], cfg["k"], cfg["top_k"], cfg["g"]
     S, H, D = q.shape
-    idx, sc = pv.index_prefill(to_dev(q), to_dev(k), top_k=top_k, g=g, mode=mode, return_scores=True)
+    qd, kd = to_dev(q), to_dev(k)
+    only = pv.index_prefill(qd, kd, top_k=top_k, g=g, mode=mode)
+    idx, sc = pv.index_prefill(qd, kd, top_k=top_k, g=g, mode=mode, return_scores=True)
     torch.cuda.synchronize()
+    assert torch.equal(only, idx)
+    val, lim = prefill_valid(S, H, g, top_k, 2 * top_k, mode)
+    parity.structure_ok_device(idx.view(S * H, top_k), val, lim, sc.view(S * H, top_k))
     gi, gs = parity.to_host(idx), parity.to_host(sc)
-    K = 2 * top_k
-    lim = np.maximum((np.arange(S) // g) * g, 1)[:, None]
-    parity.structure_ok(gi, gs, lim, np.minimum(top_k, np.minimum(K, lim)))
-    rng = np.random.default_rng(3)
-    ri = np.concatenate([rng.integers(0, S, 120), [0, 1, 7, 8, 9, 1023, 1024, 1025, S - 1]])
-    rh = rng.integers(0, H, len(ri)).astype(np.int32)
-    oi, os_ = oracle.prefill_rows(q, k, ri, rh, top_k, g, 2.0, mode)
-    np.testing.assert_array_equal(gi[ri, rh], oi)
-    np.testing.assert_array_equal(gs[ri, rh], os_)
+    del only, idx, sc
+    with OraclePool() as pool:
+        tasks = []
+        for h in range(H):
+            tasks.append(("prefill", dict(q=pool.put(q[:, h:h + 1]), k=pool.put(k[:, h:h + 1]), top_k=top_k, g=g,
+                                          candidate_ratio=2.0, mode=mode)))
+        res = pool.map(tasks)
+    for h, (oi, os_) in enumerate(res):
+        np.testing.assert_array_equal(gi[:, h], oi[:, 0], err_msg=f"head {h}")
+        np.testing.assert_array_equal(gs[:, h], os_[:, 0], err_msg=f"head {h}")
 
 
-@pytest.mark.parametrize("mode", ["refine", "reuse"])
-def test_int_workload_index_only_bit_exact(pv, mode):
-    """Index-only rows (wavefront bucket sorts) on the integer workload."""
-    print(f"\n[int workload] S=16384 H=16 {mode} index-only", flush=True)
-    cfg = syn.int_prefill()
-    q, k, top_k, g = cfg["q"], cfg["k"], cfg["top_k"], cfg["g"]
-    S, H, D = q.shape
-    idx = pv.index_prefill(to_dev(q), to_dev(k), top_k=top_k, g=g, mode=mode)
-    torch.cuda.synchronize()
-    gi = parity.to_host(idx)
-    rng = np.random.default_rng(4)
-    ri = np.concatenate([rng.integers(0, S, 120), [0, 1, 7, 8, 9, 1023, 1024, 1025, S - 1]])
-    rh = rng.integers(0, H, len(ri)).astype(np.int32)
-    oi, _ = oracle.prefill_rows(q, k, ri, rh, top_k, g, 2.0, mode)
-    np.testing.assert_array_equal(gi[ri, rh], oi)
+# ------------------------------------------- long workloads (tie-tolerant)
+
+LONG = {False: (65536, 64, 8, 1003, (0, 37), 128), True: (131072, 32, 16, 1004, (0, 19), 64)}
 
 
 @pytest.mark.parametrize("long", [False, True])
 @pytest.mark.parametrize("mode", ["refine", "reuse"])
-def test_long_workload_index_only_equals_scored(pv, mode, long):
-    """At full size, the index-only launch (the bench's: wavefront bucket
-    sorts) returns exactly the indices of the launch that also returns scores
-    (general selectors), in every row."""
-    S, H, g, seed = (131072, 32, 16, 1004) if long else (65536, 64, 8, 1003)
-    print(f"\n[long workload] S={S} H={H} g={g} {mode} index-only vs scored", flush=True)
+def test_long_workload_two_heads_tolerant(pv, mode, long):
+    S, H, g, seed, heads, ngroups = LONG[long]
+    top_k, K = 2048, 4096
+    print(f"\n[long workload] S={S} H={H} g={g} {mode}: heads {heads}, {ngroups} groups each", flush=True)
     cfg = syn.long_prefill_device(DEV, S=S, H=H, g=g, seed=seed)
-    q, k, top_k = cfg["q"], cfg["k"], cfg["top_k"]
-    a = pv.index_prefill(q, k, top_k=top_k, g=g, mode=mode)
-    b, sc = pv.index_prefill(q, k, top_k=top_k, g=g, mode=mode, return_scores=True)
-    del sc
+    q, k = cfg["q"], cfg["k"]
+    only = pv.index_prefill(q, k, top_k=top_k, g=g, mode=mode)
     torch.cuda.synchronize()
-    same = torch.eq(a, b).all(dim=2)
-    bad = torch.nonzero(~same)[:5].tolist()
-    assert not bad, bad
-
-
-@pytest.mark.parametrize("long", [False, True])
-@pytest.mark.parametrize("mode", ["refine", "reuse"])
-def test_long_workloads_sampled_rows_tolerant(pv, mode, long):
-    S, H, g, seed = (131072, 32, 16, 1004) if long else (65536, 64, 8, 1003)
-    print(f"\n[long workload] S={S} H={H} g={g} {mode}", flush=True)
-    cfg = syn.long_prefill_device(DEV, S=S, H=H, g=g, seed=seed)
-    q, k, top_k = cfg["q"], cfg["k"], cfg["top_k"]
-    D = q.shape[2]
+    val, lim = prefill_valid(S, H, g, top_k, K, mode)
+    parity.structure_ok_device(only.view(S * H, top_k), val, lim)
     idx, sc = pv.index_prefill(q, k, top_k=top_k, g=g, mode=mode, return_scores=True)
     torch.cuda.synchronize()
+    bad = torch.nonzero(~torch.eq(only, idx).all(dim=2))[:5].tolist()
+    assert not bad, f"index-only rows differ from the scored launch at {bad}"
+    del only
+    parity.structure_ok_device(idx.view(S * H, top_k), val, lim, sc.view(S * H, top_k))
+    G = S // g
     rng = np.random.default_rng(5)
-    n_rows = 24
-    ri = np.concatenate([rng.integers(0, S, n_rows - 4), [1, g * 600, S // 2, S - 1]])
-    rh = rng.integers(0, H, n_rows).astype(np.int32)
-    ri_d = torch.from_numpy(ri).to(DEV)
-    rh_d = torch.from_numpy(rh.astype(np.int64)).to(DEV)
-    gi = idx[ri_d, rh_d].cpu().numpy()
-    gs = sc[ri_d, rh_d].cpu().numpy()
+    groups = np.unique(np.concatenate([rng.integers(1, G, ngroups - 4), [0, 1, 600, G - 1]]))
+    gi = {h: idx[:, h].cpu().numpy() for h in heads}
+    gs = {h: sc[:, h].cpu().numpy() for h in heads}
     del idx, sc
-    qh = syn.bf16_tensor_to_bits(q)
-    kh = syn.bf16_tensor_to_bits(k)
-    oi, os_ = oracle.prefill_rows(qh, kh, ri, rh, top_k, g, 2.0, mode)
     errs = []
-    for r in range(n_rows):
-        i, h = int(ri[r]), int(rh[r])
-        j = i // g
-        proxy = oracle.proxy(qh, g, h, j).astype(np.float64)
-        cand = csc = None
-        if mode == "refine":
-            cand, csc = oracle.prefill_candidates(qh, kh, h, j, top_k, g, 2.0)
-            avec = syn.bf16_bits_to_f32(qh[i, h]).astype(np.float64)
-        else:
-            avec = proxy
-        e = parity.tolerant_row_match(gi[r], gs[r], oi[r], os_[r], avec, kh, h, D,
-                                      cand_idx=cand, cand_sc=csc, proxy=proxy)
-        if e:
-            errs.append((i, h, e))
+    qb = {h: head_bits(q, h) for h in heads}
+    kb = {h: head_bits(k, h) for h in heads}
+    del q, k, cfg
+    with OraclePool() as pool:
+        tasks, owner = [], []
+        for h in heads:
+            qr, kr = pool.put(qb[h]), pool.put(kb[h])
+            for c in np.array_split(groups, 8):
+                tasks.append(("prefill_groups_of_head", dict(q=qr, k=kr, groups=c, top_k=top_k, g=g,
+                                                             candidate_ratio=2.0, mode=mode)))
+                owner.append((h, c))
+        res = pool.map(tasks)
+    rows = 0
+    kv_h = {h: parity.key_values(kb[h], 0) for h in heads}
+    qv_h = {h: syn.bf16_bits_to_f32(qb[h][:, 0]).astype(np.float64) for h in heads}
+    for (h, chunk), (oi, os_, proxies, cands) in zip(owner, res):
+        kv_all, qv = kv_h[h], qv_h[h]
+        for t, j in enumerate(chunk):
+            j = int(j)
+            n = max(j * g, 1)
+            proxy = proxies[t].astype(np.float64)
+            for u in range(g):
+                i = j * g + u
+                avec = qv[i] if mode == "refine" else proxy
+                e = parity.row_match(gi[h][i], gs[h][i], oi[t, u], os_[t, u], avec, kv_all[:n], proxy=proxy,
+                                     cand_idx=None if cands is None else cands[t])
+                rows += 1
+                if e:
+                    errs.append((i, h, e))
+    print(f"  {rows} rows compared", flush=True)
+    assert rows >= 1000 * len(heads)
     assert not errs, errs[:5]
 
 
-def test_dense_index_only_equals_scored(pv):
-    """The dense indexer at S=32768, H=4 on the long-workload distribution:
-    index-only rows (one wavefront per query row) equal the scored launch's
-    (block selector) in every row."""
-    print("\n[dense] S=32768 H=4 index-only vs scored", flush=True)
-    cfg = syn.long_prefill_device(DEV, S=32768, H=4, g=8, seed=1006)
-    q, k, top_k = cfg["q"], cfg["k"], cfg["top_k"]
-    a = pv.dense_index(q, k, top_k=top_k)
-    b, sc = pv.dense_index(q, k, top_k=top_k, return_scores=True)
-    del sc
-    torch.cuda.synchronize()
-    bad = torch.nonzero(~torch.eq(a, b).all(dim=2))[:5].tolist()
-    assert not bad, bad
-
+# ------------------------------------------------------------------- decode
 
 @pytest.mark.parametrize("g", [2, 4])
 @pytest.mark.parametrize("mode", ["refine", "reuse"])
-def test_decode_workload_tolerant(pv, mode, g):
-    print(f"\n[decode workload] g={g} {mode}", flush=True)
+def test_decode_workload_every_head_tolerant(pv, mode, g):
+    print(f"\n[decode workload] g={g} {mode}: every sequence of every head", flush=True)
     dc = syn.decode_step_device(DEV, g=g)
     q, kc, ctx, top_k = dc["q"], dc["k_cache"], dc["ctx_lens"], dc["top_k"]
+    B, H = len(ctx), q.shape[1]
+    only = pv.index_decode(q, kc, ctx, g, top_k=top_k, mode=mode)
     idx, sc = pv.index_decode(q, kc, ctx, g, top_k=top_k, mode=mode, return_scores=True)
     torch.cuda.synchronize()
-    h = 3
-    gi = idx[:, h].cpu().numpy()
-    gs = sc[:, h].cpu().numpy()
-    qh = syn.bf16_tensor_to_bits(q[:, h:h + 1].contiguous())
-    kh = syn.bf16_tensor_to_bits(kc[:, h:h + 1].contiguous())
+    assert torch.equal(only, idx)
+    del only
+    ctx_d = torch.from_numpy(ctx).to(DEV)
+    lim = ctx_d.repeat_interleave(g).repeat_interleave(H)
+    val = torch.clamp(lim, max=top_k)
+    parity.structure_ok_device(idx.view(B * g * H, top_k), val, lim, sc.view(B * g * H, top_k))
+    gi, gs = idx.cpu().numpy(), sc.cpu().numpy()
     del idx, sc
-    oi, os_ = oracle.decode(qh, kh, ctx, g, top_k, 2.0, mode)
-    D = q.shape[2]
+    offs = np.concatenate([[0], np.cumsum(ctx)])
     errs = []
-    off = 0
-    for b in range(len(ctx)):
-        n = int(ctx[b])
-        qv = syn.bf16_bits_to_f32(qh[b * g:(b + 1) * g, 0]).astype(np.float64)
-        # proxy: float32 sum, one float32 division, bf16 rounding
-        ps = np.zeros(D, np.float32)
-        for t in range(g):
-            ps = (ps + qv[t].astype(np.float32)).astype(np.float32)
-        proxy = syn.bf16_bits_to_f32(syn.to_bf16_bits(ps / np.float32(g))).astype(np.float64)
-        kslice = kh[off:off + n]
-        cand = csc = None
-        if mode == "refine":
-            kv = syn.bf16_bits_to_f32(kslice[:, 0]).astype(np.float64)
-            ps_all = kv @ proxy
-            order = np.lexsort((np.arange(n), -ps_all))
-            cand = order[:min(2 * top_k, n)]
-            csc = ps_all[cand]
-        for t in range(g):
-            r = b * g + t
-            avec = qv[t] if mode == "refine" else proxy
-            e = parity.tolerant_row_match(gi[r], gs[r], oi[r, 0], os_[r, 0], avec, kslice, 0, D,
-                                          cand_idx=cand, cand_sc=csc, proxy=proxy)
-            if e:
-                errs.append((b, t, e))
-        off += n
+    rows = 0
+    with OraclePool(need_bytes=int(ctx.sum()) * 128 * 2) as pool:
+        for h in range(H):
+            qh, kh = head_bits(q, h), head_bits(kc, h)
+            qr, kr = pool.put(qh), pool.put(kh)
+            tasks = [("decode_sequence", dict(q=qr.rows(b * g, b * g + g), kc=kr.rows(int(offs[b]), int(offs[b + 1])),
+                                              ctx=int(ctx[b]), g=g, top_k=top_k, candidate_ratio=2.0, mode=mode))
+                     for b in range(B)]
+            res = pool.map(tasks)
+            qv = syn.bf16_bits_to_f32(qh[:, 0]).astype(np.float64)
+            for b, (oi, os_, proxy, cand) in enumerate(res):
+                kv = parity.PrefixKeys(kh, 0, int(offs[b]), int(ctx[b]))
+                proxy = proxy.astype(np.float64)
+                for t in range(g):
+                    r = b * g + t
+                    avec = qv[r] if mode == "refine" else proxy
+                    e = parity.row_match(gi[r, h], gs[r, h], oi[t], os_[t], avec, kv, proxy=proxy, cand_idx=cand)
+                    rows += 1
+                    if e:
+                        errs.append((b, h, t, e))
+            pool.drop(qr)
+            pool.drop(kr)
+    print(f"  {rows} rows compared", flush=True)
+    assert rows == B * g * H
     assert not errs, errs[:5]
 
+
+# ------------------------------------------------ literal Refine (comparison)
 
 def test_literal_refine_long_distribution_tolerant(pv):
     """The per-position rescan at S=16384, H=8 on the long-workload
     distribution (AR(1) queries, Pareto-norm keys, top_k=2048, K=4096):
     sampled rows against the oracle, tie-tolerant; the index-only launch
     equals the scored one in every row."""
+    import oracle
     S, H, g = 16384, 8, 8
     print(f"\n[literal] S={S} H={H} g={g}", flush=True)
     cfg = syn.long_prefill_device(DEV, S=S, H=H, g=g, seed=1007)
     q, k, top_k = cfg["q"], cfg["k"], cfg["top_k"]
-    D = q.shape[2]
     idx, sc = pv.index_prefill(q, k, top_k=top_k, g=g, mode="refine_literal", return_scores=True)
     only = pv.index_prefill(q, k, top_k=top_k, g=g, mode="refine_literal")
     torch.cuda.synchronize()
     bad = torch.nonzero(~torch.eq(idx, only).all(dim=2))[:5].tolist()
     assert not bad, bad
+    i_all = torch.arange(S, device=DEV, dtype=torch.int64)
+    lim = torch.clamp(i_all, min=1).repeat_interleave(H)
+    val = torch.clamp(i_all, max=top_k).repeat_interleave(H)
+    parity.structure_ok_device(only.view(S * H, top_k), val, lim)
     rng = np.random.default_rng(8)
     ri = np.concatenate([rng.integers(0, S, 12), [0, 1, 9, 4097, S - 1]])
     rh = rng.integers(0, H, len(ri)).astype(np.int32)
@@ -226,13 +234,30 @@ def test_literal_refine_long_distribution_tolerant(pv):
             continue
         j = i // g
         proxy = oracle.proxy(qh, g, h, j).astype(np.float64)
-        kv = syn.bf16_bits_to_f32(kh[:i, h]).astype(np.float64)
+        kv = parity.key_values(kh, h, 0, i)
         ps = kv @ proxy
         order = np.lexsort((np.arange(i), -ps))
         cand = order[:min(4096, i)]
         avec = syn.bf16_bits_to_f32(qh[i, h]).astype(np.float64)
-        e = parity.tolerant_row_match(gi[r], gs[r], oi[r], os_[r], avec, kh, h, D,
-                                      cand_idx=cand, cand_sc=ps[cand], proxy=proxy)
+        e = parity.row_match(gi[r], gs[r], oi[r], os_[r], avec, kv, proxy=proxy, cand_idx=cand)
         if e:
             errs.append((i, h, e))
     assert not errs, errs[:5]
+
+
+def test_dense_index_only_equals_scored(pv):
+    """The dense indexer at S=32768, H=4 on the long-workload distribution:
+    index-only rows (one wavefront per query row) equal the scored launch's
+    (block selector) in every row, and every row is well formed."""
+    print("\n[dense] S=32768 H=4 index-only vs scored", flush=True)
+    cfg = syn.long_prefill_device(DEV, S=32768, H=4, g=8, seed=1006)
+    q, k, top_k = cfg["q"], cfg["k"], cfg["top_k"]
+    S, H = q.shape[0], q.shape[1]
+    a = pv.dense_index(q, k, top_k=top_k)
+    b, sc = pv.dense_index(q, k, top_k=top_k, return_scores=True)
+    torch.cuda.synchronize()
+    bad = torch.nonzero(~torch.eq(a, b).all(dim=2))[:5].tolist()
+    assert not bad, bad
+    i_all = torch.arange(S, device=DEV, dtype=torch.int64)
+    lim = torch.clamp(i_all, min=1).repeat_interleave(H)
+    parity.structure_ok_device(b.view(S * H, top_k), torch.clamp(lim, max=top_k), lim, sc.view(S * H, top_k))

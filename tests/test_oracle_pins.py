@@ -334,28 +334,46 @@ def test_recall_nested_in_K_and_refine_beats_reuse():
 
 # ------------------------------------------------- the pages' Reuse loop
 
+def _group_means(qv_h, g):
+    """(G, D) means of consecutive blocks of g rows (a shorter last block)."""
+    import torch
+    S = qv_h.shape[0]
+    member_of = torch.arange(S) // g
+    G = int(member_of[-1]) + 1
+    sums = torch.zeros(G, qv_h.shape[1], dtype=torch.float64).index_add_(0, member_of, qv_h)
+    return sums / torch.bincount(member_of, minlength=G)[:, None].double(), member_of
+
+
+def _ranked(scores):
+    """Column order of each row by descending score, earlier column first on
+    equal scores (a stable sort)."""
+    import torch
+    return torch.argsort(scores, dim=1, descending=True, stable=True)
+
+
 def pages_reuse_torch(q, k, top_k, group_size, candidate_ratio):
-    """The Reuse loop of "Show Me The Code", re-expressed in torch float64:
-    per head, per group: proxy = mean of the group, one scan over
-    k[:max(g_start, 1)], top-K, and every member takes the first top_k.
-    Zero-initialised output as on the pages."""
+    """PIVOT-Reuse by its definition ("Show Me The Code", pivot_reuse),
+    vectorised per head in torch float64: all group means at once, one
+    prefix-masked score matrix (group j sees keys [0, max(j*g, 1))), every
+    row ranked, and each member takes its group's first min(top_k, K, n_j)
+    keys. Unfilled slots hold 0, as the pages' zero-initialised output does."""
     import torch
     qv = torch.from_numpy(exact_ref.values(q))
     kv = torch.from_numpy(exact_ref.values(k))
     S, H, D = q.shape
-    K = int(top_k * candidate_ratio)
-    out = torch.zeros(S, H, top_k, dtype=torch.long)
-    for h in range(H):
-        for g_start in range(0, S, group_size):
-            g_end = min(g_start + group_size, S)
-            ref_pos = max(g_start, 1)
-            proxy = qv[g_start:g_end, h].mean(dim=0)
-            scores = kv[:ref_pos, h] @ proxy
-            n_take = min(K, ref_pos)
-            cand = torch.topk(scores, n_take).indices
-            kk = min(top_k, n_take)
-            out[g_start:g_end, h, :kk] = cand[:kk]
-    return out.numpy()
+    n_cand = int(top_k * candidate_ratio)
+    res = torch.zeros(S, H, top_k, dtype=torch.long)
+    slot = torch.arange(top_k)
+    for head in range(H):
+        means, member_of = _group_means(qv[:, head], group_size)
+        seen = torch.clamp(torch.arange(means.shape[0]) * group_size, min=1)
+        sc = means @ kv[:, head].T
+        sc[torch.arange(S)[None, :] >= seen[:, None]] = -torch.inf
+        lead = _ranked(sc)[:, :top_k]
+        take = torch.minimum(torch.minimum(seen, torch.tensor(n_cand)), torch.tensor(top_k))
+        lead = torch.where(slot[None, :] < take[:, None], lead, 0)
+        res[:, head] = lead[member_of]
+    return res.numpy()
 
 
 def test_reuse_matches_pages_loop_float64():
@@ -412,29 +430,33 @@ def test_literal_refine_identities():
 
 
 def pages_refine_torch(q, k, top_k, group_size, candidate_ratio):
-    """The pivot_refine loop of "Show Me The Code", re-expressed in torch
-    float64: per head, per group: proxy = mean of the group; per position pos
-    > 0: scan k[:pos], top-K, re-score with q[pos], top-k. Zero-initialised
-    output as on the pages."""
+    """The per-position Refine of "Show Me The Code" (pivot_refine as
+    written), by its definition and vectorised per head in torch float64:
+    position p ranks keys [0, p) by its group's mean, keeps the first
+    min(K, p) as its candidates, ranks those by q_p and keeps the first
+    min(top_k, |C|). Position 0 has no key before it and stays zero, like
+    every unfilled slot of the pages' zero-initialised output."""
     import torch
     qv = torch.from_numpy(exact_ref.values(q))
     kv = torch.from_numpy(exact_ref.values(k))
     S, H, D = q.shape
-    K = int(top_k * candidate_ratio)
-    out = torch.zeros(S, H, top_k, dtype=torch.long)
-    for h in range(H):
-        for g_start in range(0, S, group_size):
-            g_end = min(g_start + group_size, S)
-            proxy = qv[g_start:g_end, h].mean(dim=0)
-            for pos in range(g_start, g_end):
-                if pos == 0:
-                    continue
-                n_take = min(K, pos)
-                cand = torch.topk(kv[:pos, h] @ proxy, n_take).indices
-                kk = min(top_k, n_take)
-                best = torch.topk(kv[cand, h] @ qv[pos, h], kk).indices
-                out[pos, h, :kk] = cand[best]
-    return out.numpy()
+    n_cand = int(top_k * candidate_ratio)
+    res = torch.zeros(S, H, top_k, dtype=torch.long)
+    pos = torch.arange(S)
+    for head in range(H):
+        means, member_of = _group_means(qv[:, head], group_size)
+        sc = means[member_of] @ kv[:, head].T                  # (S, S) by each position's group mean
+        sc[pos[None, :] >= pos[:, None]] = -torch.inf          # keys strictly before the position
+        cand = _ranked(sc)[:, :n_cand]                         # (S, K)
+        n_c = torch.minimum(pos, torch.tensor(n_cand))
+        ok = torch.arange(cand.shape[1])[None, :] < n_c[:, None]
+        own = torch.einsum("pcd,pd->pc", kv[:, head][cand], qv[:, head])
+        own = torch.where(ok, own, -torch.inf)
+        pick = torch.gather(cand, 1, _ranked(own)[:, :top_k])
+        keep = torch.minimum(n_c, torch.tensor(top_k))
+        pick = torch.where(torch.arange(pick.shape[1])[None, :] < keep[:, None], pick, 0)
+        res[:, head, :pick.shape[1]] = pick
+    return res.numpy()
 
 
 def test_literal_refine_matches_pages_loop_float64():
