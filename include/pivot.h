@@ -118,8 +118,9 @@ size_t pivot_prefill_workspace_bytes(int64_t S, int32_t H, int32_t D,
 
 /* Prefill indexer (abstract: fixed-size groups of consecutive queries).
  *   q, k      device (S, H, D) of `dtype` (PIVOT_F32 or PIVOT_BF16)
- *   S >= 1, H >= 1, D in {64, 128}, 1 <= top_k <= 4096, g >= 1,
- *   K = floor(top_k * candidate_ratio) with top_k <= K <= 4096,
+ *   S >= 1, H >= 1, D in {64, 128}, 1 <= top_k <= 8192, g >= 1,
+ *   K = floor(top_k * candidate_ratio) with top_k <= K <= 8192 (the
+ *   resource limit of the selection kernels; larger -> PIVOT_EUNSUPPORTED),
  *   mode      PIVOT_REFINE, PIVOT_REUSE or PIVOT_REFINE_LITERAL
  *   out_idx   device (S, H, top_k) int32, written completely
  *   out_score device (S, H, top_k) float32 or NULL
@@ -162,7 +163,7 @@ size_t dense_index_workspace_bytes(int64_t S, int32_t H, int32_t D,
 /* Dense indexer, for comparison (abstract: score every preceding token and
  * keep the top-k; "The Problem" section of "PIVOT Explained"): row (i, h)
  * ranks keys [0, max(i, 1)) by q[i, h] . k[c, h]. Arguments as for prefill;
- * 1 <= top_k <= 4096. */
+ * 1 <= top_k <= 8192. */
 int dense_index(const void *q, const void *k, int32_t dtype, int64_t S,
                 int32_t H, int32_t D, int32_t top_k, int32_t *out_idx,
                 float *out_score, void *workspace, size_t workspace_bytes,

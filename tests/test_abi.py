@@ -74,8 +74,12 @@ def test_workspace_sizes(pv):
     # the literal per-position Refine scans one row per position: its
     # workspace grows like g = 1 Refine's, not like one row per group
     assert f(4096, 1, 128, 64, 8, 2.0, 2, 1) > f(4096, 1, 128, 64, 8, 2.0, 0, 1)
-    assert f(64, 1, 64, 4097, 8, 1.0, 0, 1) == 0      # top_k above 4096
-    assert f(64, 1, 64, 2048, 8, 2.5, 0, 1) == 0      # K above 4096
+    assert f(64, 1, 64, 8193, 8, 1.0, 0, 1) == 0      # top_k above 8192
+    assert f(64, 1, 64, 4096, 8, 2.5, 0, 1) == 0      # K above 8192
+    # K up to 8192 is accepted; beyond 4096 candidates Refine adds the
+    # global score rows of its row select to the workspace
+    assert f(64, 1, 64, 2048, 8, 4.0, 0, 1) > f(64, 1, 64, 2048, 8, 2.0, 0, 1) > 0
+    assert f(64, 1, 64, 8192, 8, 1.0, 1, 1) > 0
     assert pv.lib.dense_index_workspace_bytes(1024, 8, 64, 64, 0) > 0
     ctx = (ctypes.c_int64 * 3)(5, 9, 100)
     assert pv.lib.pivot_decode_workspace_bytes(3, ctx, 2, 8, 128, 64, 2.0, 0, 1) > 0
@@ -97,7 +101,8 @@ def _prefill(pv, **kw):
     (dict(q=None), -1), (dict(k=None), -1), (dict(out=None), -1),
     (dict(S=0), -1), (dict(H=0), -1), (dict(g=0), -1), (dict(top_k=0), -1),
     (dict(dtype=7), -1), (dict(mode=3), -1), (dict(ratio=0.5), -1),
-    (dict(D=96), -2), (dict(top_k=5000, ratio=1.0), -2), (dict(top_k=4096, ratio=2.0), -2),
+    (dict(D=96), -2), (dict(top_k=8193, ratio=1.0), -2), (dict(top_k=8192, ratio=1.5), -2),
+    (dict(top_k=4096, ratio=2.001), -2),
     (dict(ws=None), -3), (dict(wsb=16), -3),
     (dict(q=264), -1), (dict(k=258), -1), (dict(out=258), -1), (dict(sc=257), -1), (dict(ws=264), -3),
 ])
@@ -129,7 +134,7 @@ def test_dense_validation(pv):
     L = pv.lib.dense_index
     assert L(None, vp(A), 1, 64, 2, 64, 8, vp(A), None, vp(A), 1 << 40, None) == -1
     assert L(vp(A), vp(A), 1, 64, 2, 64, 0, vp(A), None, vp(A), 1 << 40, None) == -1
-    assert L(vp(A), vp(A), 1, 64, 2, 128, 5000, vp(A), None, vp(A), 1 << 40, None) == -2
+    assert L(vp(A), vp(A), 1, 64, 2, 128, 8193, vp(A), None, vp(A), 1 << 40, None) == -2
     assert L(vp(A), vp(A), 1, 64, 2, 64, 8, vp(A), None, None, 0, None) == -3
     assert L(vp(A + 4), vp(A), 1, 64, 2, 64, 8, vp(A), None, vp(A), 1 << 40, None) == -1
 

@@ -54,17 +54,21 @@ constexpr int RING = 16;           // staged survivors per (row, half) stream
 constexpr int FLUSH = 8;           // survivors written per flush (64 bytes)
 constexpr int SEL_THREADS = 256;
 constexpr int SEL_LOG2NB = 11;
-constexpr int SEL_E = 48;          // survivors per thread held in registers
+constexpr int SEL_E = 48;          // survivors per thread held in registers (Ksel <= 4096)
+constexpr int SEL_E_BIG = 96;      // the same for Ksel up to MAX_K
 constexpr int TAU_E = 16;          // samples per thread held in registers
 constexpr int REF_LOG2NB = 10;
-constexpr int REF_E = 64;          // candidates per lane (K <= 4096)
+constexpr int REF_E = 64;          // candidates per lane (K <= REF_MAXK)
+constexpr int REF_MAXK = 64 * REF_E;  // candidates one wavefront's registers hold
 constexpr int REF_FIX = 48;        // staging entries per lane at most (top_k + slack <= 3072)
 constexpr int REF_LOG2 = 11;       // fused select: 2048 buckets
 constexpr int REF_NB = 1 << REF_LOG2;
 constexpr int REF_LOG2C = 10;      // fused select: coarse bins
 constexpr int REF_HDR = ((1 << REF_LOG2C) + 64 + REF_NB / 2 + 64 + 16) * 4;  // bytes before the staged entries
-constexpr int MAX_K = 4096;
-constexpr int MAX_TOPK = 4096;
+constexpr int MAX_K = 8192;
+constexpr int MAX_TOPK = 8192;
+constexpr int RS_E = MAX_K / SEL_THREADS;  // row select: candidate scores per thread
+constexpr int SORT_MP = 16;        // sorted rows ranked in registers: up to SORT_MP * SEL_THREADS
 constexpr int FB_BLOCKS = 256;
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_TOKENS = 512;    // tokens per decode-scan block
@@ -598,6 +602,7 @@ struct SelParams {
     // decode: B+1 prefix offsets of the sequences (row length of sequence j
     // is offs[j+1] - offs[j]); null in prefill (causal prefix of group j)
     const int64_t *offs;
+    int buf_cap;      // entries of each LDS sort buffer (>= Ksel)
 };
 
 __device__ __forceinline__ int64_t sel_row_len(const SelParams &p, int64_t j) {
@@ -624,14 +629,14 @@ __device__ __forceinline__ void write_member_rows(const RowOut &o, int hl, int64
 // row's best Ksel keys when the row is not queued) are held in registers and
 // the exact best min(Ksel, n) of them selected. Slots past the survivors
 // hold key 0 (below every score) and never rank.
-template <bool SORTED>
+template <bool SORTED, int E>
 __device__ __forceinline__ void select_row(const SelParams &p, const int64_t r, unsigned char *smem) {
     uint32_t *hist = (uint32_t *)smem;
     uint32_t *vars = hist + (1 << SEL_LOG2NB);
     uint32_t *red = vars + 8;
     uint32_t *ctr = red + 16;
     uint32_t *bufk = ctr + 4;
-    uint32_t *bufp = bufk + MAX_TOPK;
+    uint32_t *bufp = bufk + p.buf_cap;
 
     const int64_t j = r % p.G;
     const int hl = (int)(r / p.G);
@@ -653,10 +658,10 @@ __device__ __forceinline__ void select_row(const SelParams &p, const int64_t r, 
     const uint2 *b1 = p.surv + (2 * r + 1) * (int64_t)p.stride;
     auto ident = [](uint32_t x) { return x; };
     if constexpr (!SORTED) {
-        uint32_t key[SEL_E], pl[SEL_E];
+        uint32_t key[E], pl[E];
         // all loads first (independent, in flight together), then the keys
 #pragma unroll
-        for (int e = 0; e < SEL_E; ++e) {
+        for (int e = 0; e < E; ++e) {
             const uint32_t gi = e * SEL_THREADS + threadIdx.x;
             uint2 x = make_uint2(0u, 0xFFFFFFFFu);
             if (e < elim && gi < ns) x = gi < (uint32_t)c0 ? b0[gi] : b1[gi - c0];
@@ -664,11 +669,11 @@ __device__ __forceinline__ void select_row(const SelParams &p, const int64_t r, 
             pl[e] = x.y;
         }
 #pragma unroll
-        for (int e = 0; e < SEL_E; ++e)
+        for (int e = 0; e < E; ++e)
             key[e] = pl[e] == 0xFFFFFFFFu ? 0u : score_key(__uint_as_float(key[e]));
         auto fe = [&](auto f) {
 #pragma unroll
-            for (int e = 0; e < SEL_E; ++e)
+            for (int e = 0; e < E; ++e)
                 if (e < elim) f(key[e], pl[e]);
         };
         const Rule rule = msel >= ns ? Rule{0u, 0u}
@@ -677,16 +682,16 @@ __device__ __forceinline__ void select_row(const SelParams &p, const int64_t r, 
         __syncthreads();
         uint32_t *dst = p.o.cand + r * p.o.K;
 #pragma unroll
-        for (int e = 0; e < SEL_E; ++e)
+        for (int e = 0; e < E; ++e)
             if (e < elim && key[e] != 0u && rule.sel(key[e], pl[e])) {
                 const uint32_t slot = atomicAdd(&ctr[0], 1u);
                 if (slot < msel) dst[slot] = pl[e];
             }
     } else {
-        uint32_t key[SEL_E], pl[SEL_E];
+        uint32_t key[E], pl[E];
         // all loads first (independent, in flight together), then the keys
 #pragma unroll
-        for (int e = 0; e < SEL_E; ++e) {
+        for (int e = 0; e < E; ++e) {
             const uint32_t gi = e * SEL_THREADS + threadIdx.x;
             uint2 x = make_uint2(0u, 0xFFFFFFFFu);
             if (e < elim && gi < ns) x = gi < (uint32_t)c0 ? b0[gi] : b1[gi - c0];
@@ -694,32 +699,42 @@ __device__ __forceinline__ void select_row(const SelParams &p, const int64_t r, 
             pl[e] = x.y;
         }
 #pragma unroll
-        for (int e = 0; e < SEL_E; ++e)
+        for (int e = 0; e < E; ++e)
             key[e] = pl[e] == 0xFFFFFFFFu ? 0u : score_key(__uint_as_float(key[e]));
         auto fe = [&](auto f) {
 #pragma unroll
-            for (int e = 0; e < SEL_E; ++e)
+            for (int e = 0; e < E; ++e)
                 if (e < elim) f(key[e], pl[e]);
         };
         const Rule rule = msel >= ns ? Rule{0u, 0u}
                                      : sel.select(fe, ident, (uint32_t)elim * SEL_THREADS, msel);
         auto fs = [&](auto f) {
 #pragma unroll
-            for (int e = 0; e < SEL_E; ++e)
+            for (int e = 0; e < E; ++e)
                 if (e < elim && key[e] != 0u && rule.sel(key[e], pl[e])) f(key[e], pl[e]);
         };
-        constexpr int MP = MAX_TOPK / SEL_THREADS;
-        uint32_t rpos[MP], rkey[MP], rpl[MP];
-        sel.template sort_ranks<MP>(fs, ident, msel, bufk, bufp, rpos, rkey, rpl);
+        if constexpr (E > SEL_E) {
+            if (msel > (uint32_t)(SORT_MP * SEL_THREADS)) {
+                // more than the registers rank: every entry straight to its
+                // member rows
+                sel.sort_selected(fs, ident, msel, bufk, bufp, [&](uint32_t pos, uint32_t k, uint32_t idx) {
+                    put_member_rows(p.o, hl, j, pos, k, idx);
+                });
+                pad_member_rows(p.o, hl, j, msel, (int)threadIdx.x, SEL_THREADS);
+                return;
+            }
+        }
+        uint32_t rpos[SORT_MP], rkey[SORT_MP], rpl[SORT_MP];
+        sel.template sort_ranks<SORT_MP>(fs, ident, msel, bufk, bufp, rpos, rkey, rpl);
 #pragma unroll
-        for (int t = 0; t < MP; ++t)
+        for (int t = 0; t < SORT_MP; ++t)
             if (threadIdx.x + t * SEL_THREADS < msel) bufk[rpos[t]] = rpl[t];
         __syncthreads();
         write_member_rows(p.o, hl, j, bufk, msel, false);
         if (p.o.out_score) {
             __syncthreads();
 #pragma unroll
-            for (int t = 0; t < MP; ++t)
+            for (int t = 0; t < SORT_MP; ++t)
                 if (threadIdx.x + t * SEL_THREADS < msel) bufk[rpos[t]] = rkey[t];
             __syncthreads();
             write_member_rows(p.o, hl, j, bufk, msel, true);
@@ -728,17 +743,18 @@ __device__ __forceinline__ void select_row(const SelParams &p, const int64_t r, 
 }
 
 // SORTED: sorted member rows (Reuse, dense); otherwise candidate lists
-// (Refine), which need fewer registers: three blocks share a CU.
-template <bool SORTED>
-__global__ void __launch_bounds__(SEL_THREADS, SORTED ? 2 : 3) k_select(SelParams p) {
+// (Refine), which need fewer registers: three blocks share a CU. E: survivors
+// per thread (SEL_E_BIG for Ksel above 4096, one block per CU).
+template <bool SORTED, int E>
+__global__ void __launch_bounds__(SEL_THREADS, E > SEL_E ? 1 : (SORTED ? 2 : 3)) k_select(SelParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     if (!p.list) {
-        select_row<SORTED>(p, blockIdx.x, smem);
+        select_row<SORTED, E>(p, blockIdx.x, smem);
         return;
     }
     const uint32_t nl = *p.big_count;
     for (uint32_t it = blockIdx.x; it < nl; it += gridDim.x) {
-        select_row<SORTED>(p, (int64_t)p.big_list[it], smem);
+        select_row<SORTED, E>(p, (int64_t)p.big_list[it], smem);
         __syncthreads();
     }
 }
@@ -766,6 +782,7 @@ struct FbParams {
     int sorted_out;
     RowOut o;
     int D;
+    int buf_cap;  // entries of each LDS sort buffer (>= Ksel)
 };
 
 // Streaming exact selection over a whole score row in global memory (the
@@ -778,8 +795,8 @@ __global__ void __launch_bounds__(SEL_THREADS) k_fallback(FbParams p) {
     uint32_t *red = vars + 8;
     uint32_t *ctr = red + 16;
     uint32_t *bufk = ctr + 4;
-    uint32_t *bufp = bufk + MAX_TOPK;
-    float *prow = (float *)(bufp + MAX_TOPK);  // D floats
+    uint32_t *bufp = bufk + p.buf_cap;
+    float *prow = (float *)(bufp + p.buf_cap);  // D floats
 
     Group<4> G{(int)threadIdx.x, red};
     Selector<4, SEL_LOG2NB> sel{G, hist, vars};
@@ -1119,6 +1136,11 @@ struct RefParams {
     int pad_first;         // literal per-position Refine: position 0 is padding
     int32_t *out_idx;
     float *out_score;
+    // candidate sets larger than REF_MAXK: the gather writes every member's
+    // candidate scores (orderable keys) to row (group * g + member) of gsc,
+    // gstride words apart, and k_rowsel selects from there
+    uint32_t *gsc;
+    int64_t gstride;
 };
 
 // One block per (group, block of <= 8 member queries): gathers the keys of
@@ -1653,8 +1675,9 @@ __global__ void __launch_bounds__(64 * SW_WAVES) k_select_wave(SelParams p) {
 
 // LINES: key rows are gathered as whole 128-byte lines and rearranged into
 // the MFMA layout in registers (bf16 blocks of several queries); otherwise
-// the loads take the MFMA layout directly.
-template <typename T, int D, bool LINES>
+// the loads take the MFMA layout directly. GOUT: the scores go to global
+// rows (p.gsc) and the kernel ends after the gather.
+template <typename T, int D, bool LINES, bool GOUT>
 __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int nblk = (int)(p.NG * p.Hc) * p.nqb;
@@ -1739,7 +1762,9 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
             // (a region has room for 64 scores past the last block)
             const int pp = (b0 + u) * 16 + 4 * lq;
             if (qcol < nq) {
-                uint32_t *dst = (uint32_t *)(regs + qcol * p.reg_bytes) + pp;
+                uint32_t *dst;
+                if constexpr (GOUT) dst = p.gsc + (grp * p.g + q0 + qcol) * p.gstride + pp;
+                else dst = (uint32_t *)(regs + qcol * p.reg_bytes) + pp;
                 *(uint4 *)dst = make_uint4(score_key(acc[0]), score_key(acc[1]), score_key(acc[2]),
                                            score_key(acc[3]));
             }
@@ -1832,6 +1857,7 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
             b0 = b2;
         }
     }
+    if constexpr (GOUT) return;
     __syncthreads();
     if (w >= nq) return;
 
@@ -1919,6 +1945,77 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
                           if (p.out_score) p.out_score[obase + pos] = key_score(k);
                       });
     for (int pos = msel + l; pos < p.top_k; pos += 64) {
+        p.out_idx[obase + pos] = -1;
+        if (p.out_score) p.out_score[obase + pos] = -INFINITY;
+    }
+}
+
+// Exact per-query top_k over candidate scores that a k_refine gather wrote
+// to global rows (candidate sets larger than one wavefront's registers): one
+// block per score row (group * g + member), RS_E scores per thread in
+// registers, narrowing selection and bucket sort as in k_select. Slots past
+// the list hold key 0, below every score.
+__global__ void __launch_bounds__(SEL_THREADS) k_rowsel(RefParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *hist = (uint32_t *)smem;
+    uint32_t *vars = hist + (1 << SEL_LOG2NB);
+    uint32_t *red = vars + 8;
+    uint32_t *bufk = red + 16;
+    uint32_t *bufp = bufk + p.top_k;
+    const int64_t r = blockIdx.x;
+    const int u = (int)(r % p.g);
+    const int64_t grp = r / p.g;
+    const int hl = (int)(grp / p.NG);
+    const int64_t j = grp % p.NG;
+    const int h = p.h0 + hl;
+    int64_t qrow0, m, n;
+    if (!p.decode) {
+        qrow0 = j * p.g;
+        m = min((int64_t)p.g, p.S - qrow0);
+        n = prefix_len(j, p.g);
+    } else {
+        qrow0 = j * p.g;
+        m = p.g;
+        n = p.offs[j + 1] - p.offs[j];
+    }
+    // members past a ragged group have no row; the literal mode's position
+    // 0 was padded by k_refine
+    if (u >= m || (p.pad_first && qrow0 == 0)) return;
+    const int nc = (int)min(p.Kc, n);
+    const uint32_t msel = (uint32_t)min((int64_t)p.top_k, (int64_t)nc);
+    const uint32_t *keys = p.gsc + r * p.gstride;
+    const uint32_t *cl = p.cand + grp * p.Kc;
+    const int tid = threadIdx.x;
+    uint32_t key[RS_E];
+#pragma unroll
+    for (int e = 0; e < RS_E; ++e) {
+        const int pos = e * SEL_THREADS + tid;
+        key[e] = pos < nc ? keys[pos] : 0u;
+    }
+    Group<4> G{tid, red};
+    Selector<4, SEL_LOG2NB> sel{G, hist, vars};
+    auto idx_of = [&](uint32_t pos) { return cl[pos]; };
+    auto fe = [&](auto f) {
+#pragma unroll
+        for (int e = 0; e < RS_E; ++e) f(key[e], (uint32_t)(e * SEL_THREADS + tid));
+    };
+    const Rule rule = msel >= (uint32_t)nc ? Rule{0u, 0u}
+                                           : sel.select(fe, idx_of, (uint32_t)(RS_E * SEL_THREADS), msel);
+    auto fs = [&](auto f) {
+#pragma unroll
+        for (int e = 0; e < RS_E; ++e) {
+            const uint32_t k = key[e];
+            const uint32_t pos = (uint32_t)(e * SEL_THREADS + tid);
+            // empty slots (key 0, past the list) never read the list
+            if (k != 0u && (k > rule.T || (k == rule.T && (~cl[pos]) >= rule.I))) f(k, pos);
+        }
+    };
+    const int64_t obase = ((qrow0 + u) * p.H + h) * (int64_t)p.top_k;
+    sel.sort_selected(fs, idx_of, msel, bufk, bufp, [&](uint32_t pos, uint32_t k, uint32_t pl) {
+        p.out_idx[obase + pos] = (int32_t)cl[pl];
+        if (p.out_score) p.out_score[obase + pos] = key_score(k);
+    });
+    for (int pos = (int)msel + tid; pos < p.top_k; pos += SEL_THREADS) {
         p.out_idx[obase + pos] = -1;
         if (p.out_score) p.out_score[obase + pos] = -INFINITY;
     }
@@ -2119,8 +2216,11 @@ struct Plan {
     int64_t keep_all_n;
     int n_tiles;
     size_t esz;
+    int sel_e;       // survivors per thread of k_select (SEL_E or SEL_E_BIG)
+    int buf_cap;     // entries of the selectors' LDS sort buffers
+    int64_t gstride; // Refine with K > REF_MAXK: words per global score row (else 0)
     // per-head bytes of each workspace array
-    size_t b_P, b_tau, b_cnt, b_scnt, b_surv, b_samp, b_cand, b_fbl, b_big;
+    size_t b_P, b_tau, b_cnt, b_scnt, b_surv, b_samp, b_cand, b_fbl, b_big, b_gsc;
     size_t fixed;  // fb_count + fallback scratch
 };
 
@@ -2161,7 +2261,7 @@ struct Sampling {
     int cap_half;
 };
 
-Sampling sampling(int64_t Ksel, int64_t n_max) {
+Sampling sampling(int64_t Ksel, int64_t n_max, int sel_e) {
     Sampling r;
     int64_t s = std::min<int64_t>(64, std::max<int64_t>(1, pow2_floor(std::max<int64_t>(1, Ksel / 64))));
     while ((n_max + s - 1) / s > 4096 - 16) s *= 2;
@@ -2173,7 +2273,7 @@ Sampling sampling(int64_t Ksel, int64_t n_max) {
     const double X = (double)r.rsel * s, sig = sqrt((double)r.rsel) * s;
     int64_t ch = (int64_t)ceil((X + 5.0 * sig) / 2.0 + 4.0 * sqrt(X / 2.0)) + 16;
     ch = (ch + 63) / 64 * 64;
-    ch = std::min<int64_t>(ch, (int64_t)SEL_E * SEL_THREADS / 2);
+    ch = std::min<int64_t>(ch, (int64_t)sel_e * SEL_THREADS / 2);
     r.cap_half = (int)ch;
     r.keep_all_n = 2 * (int64_t)r.cap_half - 16;
     return r;
@@ -2208,7 +2308,10 @@ int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio,
     pl.G = (S + pl.g - 1) / pl.g;
     pl.n_max = std::max<int64_t>((pl.G - 1) * pl.g, 1);
     pl.esz = dtype == PIVOT_BF16 ? 2 : 4;
-    const Sampling sm = sampling(pl.Ksel, pl.n_max);
+    pl.sel_e = pl.Ksel > SORT_MP * SEL_THREADS ? SEL_E_BIG : SEL_E;
+    pl.buf_cap = (int)std::max<int64_t>(SORT_MP * SEL_THREADS, pl.Ksel);
+    pl.gstride = pl.mode == PIVOT_REFINE && K > REF_MAXK ? ((K + 15) & ~(int64_t)15) + 64 : 0;
+    const Sampling sm = sampling(pl.Ksel, pl.n_max, pl.sel_e);
     const int64_t s = sm.stride;
     pl.kstride = (int)s;
     pl.rsel = sm.rsel;
@@ -2227,12 +2330,14 @@ int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio,
     pl.b_cand = pl.mode == PIVOT_REFINE ? align256(rows * (size_t)K * 4) : 0;
     pl.b_fbl = align256(rows * 4);
     pl.b_big = pl.mode == PIVOT_REUSE ? align256(rows * 4) : 0;
+    pl.b_gsc = align256(rows * (size_t)pl.g * (size_t)pl.gstride * 4);
     pl.fixed = 256 + align256((size_t)FB_BLOCKS * (size_t)pl.n_max * 4);
     return PIVOT_OK;
 }
 
 size_t per_head_bytes(const Plan &pl) {
-    return pl.b_P + pl.b_tau + pl.b_cnt + pl.b_scnt + pl.b_surv + pl.b_samp + pl.b_cand + pl.b_fbl + pl.b_big;
+    return pl.b_P + pl.b_tau + pl.b_cnt + pl.b_scnt + pl.b_surv + pl.b_samp + pl.b_cand + pl.b_fbl + pl.b_big +
+           pl.b_gsc;
 }
 
 hipError_t set_lds(const void *fn, size_t bytes) {
@@ -2245,8 +2350,8 @@ hipError_t set_lds(const void *fn, size_t bytes) {
         if ((x) != hipSuccess) return PIVOT_EHIP;     \
     } while (0)
 
-size_t sel_lds_bytes(int D) {
-    return ((size_t)(1 << SEL_LOG2NB) + 8 + 16 + 4 + 2 * MAX_TOPK) * 4 + (size_t)D * 4;
+size_t sel_lds_bytes(int D, int buf_cap) {
+    return ((size_t)(1 << SEL_LOG2NB) + 8 + 16 + 4 + 2 * (size_t)buf_cap) * 4 + (size_t)D * 4;
 }
 
 // k_select<false> (candidate lists) uses no staging buffers
@@ -2290,23 +2395,70 @@ RefLayout refine_layout(int64_t K, int top_k, int g) {
     return L;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool GOUT>
 int launch_refine(const RefParams &rp, int nblocks, size_t lds, hipStream_t st) {
     if (sizeof(T) == 2 && rp.nqw > 1) {
         constexpr bool LINES = sizeof(T) == 2;
-        HIP_TRY(set_lds((const void *)k_refine<T, D, LINES>, lds));
-        hipLaunchKernelGGL((k_refine<T, D, LINES>), dim3(nblocks), dim3(64 * rp.nqw), lds, st, rp);
+        HIP_TRY(set_lds((const void *)k_refine<T, D, LINES, GOUT>, lds));
+        hipLaunchKernelGGL((k_refine<T, D, LINES, GOUT>), dim3(nblocks), dim3(64 * rp.nqw), lds, st, rp);
     } else {
-        HIP_TRY(set_lds((const void *)k_refine<T, D, false>, lds));
-        hipLaunchKernelGGL((k_refine<T, D, false>), dim3(nblocks), dim3(64 * rp.nqw), lds, st, rp);
+        HIP_TRY(set_lds((const void *)k_refine<T, D, false, GOUT>, lds));
+        hipLaunchKernelGGL((k_refine<T, D, false, GOUT>), dim3(nblocks), dim3(64 * rp.nqw), lds, st, rp);
     }
     HIP_TRY(hipGetLastError());
     return PIVOT_OK;
 }
 
+// Refine stage over rows groups (nqb blocks each). Candidate sets of up to
+// REF_MAXK: k_refine gathers, scores and selects in one kernel (LDS layout
+// from refine_layout). Larger sets: the gather writes the scores to rp.gsc
+// and k_rowsel selects, one block per member row.
 template <typename T>
-int dispatch_refine(int D, const RefParams &rp, int nblocks, size_t lds, hipStream_t st) {
-    return D == 64 ? launch_refine<T, 64>(rp, nblocks, lds, st) : launch_refine<T, 128>(rp, nblocks, lds, st);
+int dispatch_refine(int D, RefParams rp, int64_t groups, int top_k, hipStream_t st) {
+    if (rp.Kc <= REF_MAXK) {
+        const RefLayout lay = refine_layout(rp.Kc, top_k, rp.g);
+        rp.nqw = lay.nqw;
+        rp.nqb = (rp.g + rp.nqw - 1) / rp.nqw;
+        rp.reg_bytes = lay.reg_bytes;
+        rp.ref_cap = lay.cap;
+        const int nblocks = (int)(groups * rp.nqb);
+        return D == 64 ? launch_refine<T, 64, false>(rp, nblocks, lay.lds, st)
+                       : launch_refine<T, 128, false>(rp, nblocks, lay.lds, st);
+    }
+    rp.nqw = std::min(rp.g, 8);
+    rp.nqb = (rp.g + rp.nqw - 1) / rp.nqw;
+    rp.reg_bytes = 0;
+    rp.ref_cap = 0;
+    // the candidate list, and room for the reads of 64 slots past it
+    const size_t lds = (((size_t)rp.Kc * 4 + 15) & ~(size_t)15) + 256;
+    const int nblocks = (int)(groups * rp.nqb);
+    int rc = D == 64 ? launch_refine<T, 64, true>(rp, nblocks, lds, st)
+                     : launch_refine<T, 128, true>(rp, nblocks, lds, st);
+    if (rc) return rc;
+    const size_t rlds = ((size_t)(1 << SEL_LOG2NB) + 8 + 16 + 2 * (size_t)top_k) * 4;
+    HIP_TRY(set_lds((const void *)k_rowsel, rlds));
+    hipLaunchKernelGGL(k_rowsel, dim3((unsigned)(groups * rp.g)), dim3(SEL_THREADS), rlds, st, rp);
+    HIP_TRY(hipGetLastError());
+    return PIVOT_OK;
+}
+
+// Launches k_select (one block per row, or list mode when se.list) in the
+// instance that holds Ksel's survivors.
+int launch_select(const SelParams &se, bool sorted, int sel_e, unsigned blocks, hipStream_t st) {
+    size_t lds = sorted ? sel_lds_bytes(0, se.buf_cap) : sel_cand_lds_bytes();
+    const void *fn;
+    if (sorted) fn = sel_e > SEL_E ? (const void *)k_select<true, SEL_E_BIG> : (const void *)k_select<true, SEL_E>;
+    else fn = sel_e > SEL_E ? (const void *)k_select<false, SEL_E_BIG> : (const void *)k_select<false, SEL_E>;
+    HIP_TRY(set_lds(fn, lds));
+    if (sorted) {
+        if (sel_e > SEL_E) hipLaunchKernelGGL((k_select<true, SEL_E_BIG>), dim3(blocks), dim3(SEL_THREADS), lds, st, se);
+        else hipLaunchKernelGGL((k_select<true, SEL_E>), dim3(blocks), dim3(SEL_THREADS), lds, st, se);
+    } else {
+        if (sel_e > SEL_E) hipLaunchKernelGGL((k_select<false, SEL_E_BIG>), dim3(blocks), dim3(SEL_THREADS), lds, st, se);
+        else hipLaunchKernelGGL((k_select<false, SEL_E>), dim3(blocks), dim3(SEL_THREADS), lds, st, se);
+    }
+    HIP_TRY(hipGetLastError());
+    return PIVOT_OK;
 }
 
 template <typename T, int D>
@@ -2353,6 +2505,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
         uint32_t *cand = (uint32_t *)take(pl.b_cand);
         uint32_t *fbl = (uint32_t *)take(pl.b_fbl);
         uint32_t *bigl = (uint32_t *)take(pl.b_big);
+        uint32_t *gsc = (uint32_t *)take(pl.b_gsc);
 
         ScanParams sp{};
         if (pl.dense) {
@@ -2434,7 +2587,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             se.big_list = bigl;
             se.big_count = fb_count + 1;
             se.rows = rows;
-            const size_t lds = sel_lds_bytes(0);
+            se.buf_cap = pl.buf_cap;
             StageTimer tm(ST_SELECT, st);
             // the wavefront sort stages at most 2112 entries: top_k up to
             // 2048 leaves the boundary bucket its slack
@@ -2445,16 +2598,12 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
                                    dim3(64 * SW_WAVES), wlds, st, se);
                 HIP_TRY(hipGetLastError());
                 se.list = 1;
-                hipLaunchKernelGGL(k_select<true>, dim3((unsigned)std::min<int64_t>(rows, 2048)), dim3(SEL_THREADS), lds,
-                                   st, se);
+                int rc = launch_select(se, true, pl.sel_e, (unsigned)std::min<int64_t>(rows, 2048), st);
+                if (rc) return rc;
             } else {
-                if (sorted_out)
-                    hipLaunchKernelGGL(k_select<true>, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, se);
-                else
-                    hipLaunchKernelGGL(k_select<false>, dim3((unsigned)rows), dim3(SEL_THREADS), sel_cand_lds_bytes(),
-                                       st, se);
+                int rc = launch_select(se, sorted_out != 0, pl.sel_e, (unsigned)rows, st);
+                if (rc) return rc;
             }
-            HIP_TRY(hipGetLastError());
         }
         {
             FbParams fp{};
@@ -2476,8 +2625,10 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             fp.sorted_out = sorted_out;
             fp.o = ro;
             fp.D = pl.D;
-            const size_t lds = sel_lds_bytes(pl.D);
+            fp.buf_cap = pl.buf_cap;
+            const size_t lds = sel_lds_bytes(pl.D, pl.buf_cap);
             StageTimer tm(ST_FALLBACK, st);
+            HIP_TRY(set_lds((const void *)k_fallback<T>, lds));
             hipLaunchKernelGGL((k_fallback<T>), dim3(FB_BLOCKS), dim3(SEL_THREADS), lds, st, fp);
             HIP_TRY(hipGetLastError());
         }
@@ -2495,19 +2646,14 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             rp.S = pl.S;
             rp.decode = 0;
             rp.offs = nullptr;
-            const RefLayout lay = refine_layout(pl.K, pl.top_k, pl.g);
-            rp.nqw = lay.nqw;
-            rp.nqb = (pl.g + rp.nqw - 1) / rp.nqw;
             rp.top_k = pl.top_k;
-            rp.reg_bytes = lay.reg_bytes;
-            rp.ref_cap = lay.cap;
             rp.pad_first = pl.literal ? 1 : 0;
             rp.out_idx = out_idx;
             rp.out_score = out_score;
-            const size_t lds = lay.lds;
-            const int nblocks = (int)(rows * rp.nqb);
+            rp.gsc = gsc;
+            rp.gstride = pl.gstride;
             StageTimer tm(ST_REFINE, st);
-            int rc = dispatch_refine<T>(pl.D, rp, nblocks, lds, st);
+            int rc = dispatch_refine<T>(pl.D, rp, rows, pl.top_k, st);
             if (rc) return rc;
         }
     }
@@ -2521,7 +2667,9 @@ struct DecPlan {
     Sampling sm;
     int sshift;
     int64_t chunks;
-    size_t o_offs, o_P, o_dense, o_tau, o_cnt, o_surv, o_fbl, o_big, o_cand, bytes;
+    int sel_e, buf_cap;
+    int64_t gstride;
+    size_t o_offs, o_P, o_dense, o_tau, o_cnt, o_surv, o_fbl, o_big, o_cand, o_gsc, bytes;
 };
 
 int make_dec_plan(DecPlan &dp, int B, const int64_t *ctx, int g, int H, int D, int top_k,
@@ -2553,7 +2701,10 @@ int make_dec_plan(DecPlan &dp, int B, const int64_t *ctx, int g, int H, int D, i
     dp.total = total;
     dp.max_ctx = mx;
     dp.esz = dtype == PIVOT_BF16 ? 2 : 4;
-    dp.sm = sampling(dp.Ksel, mx);
+    dp.sel_e = dp.Ksel > SORT_MP * SEL_THREADS ? SEL_E_BIG : SEL_E;
+    dp.buf_cap = (int)std::max<int64_t>(SORT_MP * SEL_THREADS, dp.Ksel);
+    dp.gstride = mode == PIVOT_REFINE && K > REF_MAXK ? ((K + 15) & ~(int64_t)15) + 64 : 0;
+    dp.sm = sampling(dp.Ksel, mx, dp.sel_e);
     dp.sshift = 0;
     while (((int64_t)1 << dp.sshift) < dp.sm.stride) ++dp.sshift;
     dp.chunks = (mx + DF_KEYS - 1) / DF_KEYS;
@@ -2578,6 +2729,8 @@ int make_dec_plan(DecPlan &dp, int B, const int64_t *ctx, int g, int H, int D, i
     off += align256(rows * 4);
     dp.o_cand = off;
     off += mode == PIVOT_REFINE ? align256((size_t)H * B * K * 4) : 0;
+    dp.o_gsc = off;
+    off += align256((size_t)H * B * (size_t)g * (size_t)dp.gstride * 4);
     dp.bytes = off;
     return PIVOT_OK;
 }
@@ -2671,7 +2824,7 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
         se.big_count = ctr + 1;
         se.rows = rows;
         se.offs = offs;
-        const size_t lds = sel_lds_bytes(0);
+        se.buf_cap = dp.buf_cap;
         if (sorted_out && dp.Ksel <= 2048) {
             const size_t wlds = (size_t)SW_WAVES * SW_REG;
             HIP_TRY(set_lds((const void *)k_select_wave, wlds));
@@ -2679,16 +2832,12 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
                                dim3(64 * SW_WAVES), wlds, st, se);
             HIP_TRY(hipGetLastError());
             se.list = 1;
-            hipLaunchKernelGGL(k_select<true>, dim3((unsigned)std::min<int64_t>(rows, 2048)), dim3(SEL_THREADS), lds, st,
-                               se);
+            int rc = launch_select(se, true, dp.sel_e, (unsigned)std::min<int64_t>(rows, 2048), st);
+            if (rc) return rc;
         } else {
-            if (sorted_out)
-                hipLaunchKernelGGL(k_select<true>, dim3((unsigned)rows), dim3(SEL_THREADS), lds, st, se);
-            else
-                hipLaunchKernelGGL(k_select<false>, dim3((unsigned)rows), dim3(SEL_THREADS), sel_cand_lds_bytes(), st,
-                                   se);
+            int rc = launch_select(se, sorted_out != 0, dp.sel_e, (unsigned)rows, st);
+            if (rc) return rc;
         }
-        HIP_TRY(hipGetLastError());
     }
     {
         FbParams fp{};
@@ -2703,8 +2852,10 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
         fp.sorted_out = sorted_out;
         fp.o = ro;
         fp.D = dp.D;
-        const size_t lds = sel_lds_bytes(dp.D);
+        fp.buf_cap = dp.buf_cap;
+        const size_t lds = sel_lds_bytes(dp.D, dp.buf_cap);
         StageTimer tm(ST_FALLBACK, st);
+        HIP_TRY(set_lds((const void *)k_fallback<T>, lds));
         hipLaunchKernelGGL((k_fallback<T>), dim3((unsigned)std::min<int64_t>(rows, FB_BLOCKS)), dim3(SEL_THREADS),
                            lds, st, fp);
         HIP_TRY(hipGetLastError());
@@ -2723,18 +2874,13 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
         rp.S = (int64_t)dp.B * dp.g;
         rp.decode = 1;
         rp.offs = offs;
-        const RefLayout lay = refine_layout(dp.K, dp.top_k, dp.g);
-        rp.nqw = lay.nqw;
-        rp.nqb = (dp.g + rp.nqw - 1) / rp.nqw;
         rp.top_k = dp.top_k;
-        rp.reg_bytes = lay.reg_bytes;
-        rp.ref_cap = lay.cap;
         rp.out_idx = out_idx;
         rp.out_score = out_score;
-        const size_t lds = lay.lds;
-        const int nblocks = dp.B * dp.H * rp.nqb;
+        rp.gsc = (uint32_t *)(ws + dp.o_gsc);
+        rp.gstride = dp.gstride;
         StageTimer tm(ST_REFINE, st);
-        int rc = dispatch_refine<T>(dp.D, rp, nblocks, lds, st);
+        int rc = dispatch_refine<T>(dp.D, rp, (int64_t)dp.B * dp.H, dp.top_k, st);
         if (rc) return rc;
     }
     return PIVOT_OK;
