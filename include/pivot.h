@@ -155,6 +155,26 @@ int pivot_index_decode(const void *q, const void *k_cache, int32_t dtype,
                        float *out_score, void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/* pivot_index_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments, results and errors as
+ * pivot_index_decode, without the workspace. The scratch is the library's
+ * own static device array of 256 MiB (one copy per GPU, held until the
+ * process ends; the 64-sequence decode step with contexts up to 131072, H =
+ * 8, D = 128, top_k = 2048, K = 4096 needs 222 MiB of it). A call whose
+ * pivot_decode_workspace_bytes exceeds 256 MiB returns PIVOT_EWORKSPACE
+ * before anything is enqueued. The call allocates nothing and records no
+ * stage-timing events. Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other threads) race and
+ * must be serialised by the caller. The first call on a device looks the
+ * array's address up (hipGetSymbolAddress) with that device current. */
+int pivot_index_decode_noalloc(const void *q, const void *k_cache,
+                               int32_t dtype, const int64_t *ctx_lens_host,
+                               int32_t B, int32_t g, int32_t H, int32_t D,
+                               int32_t top_k, double candidate_ratio,
+                               int32_t mode, int32_t *out_idx,
+                               float *out_score, void *stream);
+
 /* Workspace for dense_index (all heads in one pass; H = 1 gives the
  * minimum). Returns 0 for invalid arguments. */
 size_t dense_index_workspace_bytes(int64_t S, int32_t H, int32_t D,

@@ -35,7 +35,7 @@ EXPORTED = (
     "pivot_status_string", "pivot_candidate_count", "pivot_prefill_workspace_bytes",
     "pivot_index_prefill", "pivot_decode_workspace_bytes", "pivot_index_decode",
     "dense_index_workspace_bytes", "dense_index", "pivot_profile_enable", "pivot_profile_read",
-    "pivot_sparse_attention",
+    "pivot_sparse_attention", "pivot_index_decode_noalloc",
 )
 
 #: kernel stages reported by the stage timer (include/pivot.h)
@@ -62,6 +62,9 @@ lib.pivot_decode_workspace_bytes.restype = _sz
 lib.pivot_index_decode.argtypes = [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f64, _i32,
                                    _vp, _vp, _vp, _sz, _vp]
 lib.pivot_index_decode.restype = ctypes.c_int
+lib.pivot_index_decode_noalloc.argtypes = [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f64, _i32,
+                                           _vp, _vp, _vp]
+lib.pivot_index_decode_noalloc.restype = ctypes.c_int
 lib.dense_index_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, _i32]
 lib.dense_index_workspace_bytes.restype = _sz
 lib.dense_index.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
@@ -246,6 +249,28 @@ def index_decode(q, k_cache, ctx_lens, g, top_k=2048, candidate_ratio=2.0, mode=
     _check(lib.pivot_index_decode(_ptr(q), _ptr(k_cache), code, cp, B, g, H, D, top_k, candidate_ratio,
                                   _MODES[mode], _ptr(out), _ptr(sc), _ptr(ws), ws.numel(), _stream(q.device)),
            "pivot_index_decode")
+    return (out, sc) if return_scores else out
+
+
+def index_decode_noalloc(q, k_cache, ctx_lens, g, top_k=2048, candidate_ratio=2.0, mode="refine",
+                         return_scores=False, out=None, out_scores=None):
+    """index_decode without a workspace: the library's static device scratch
+    (256 MiB per GPU) holds the intermediate arrays, and the C call
+    allocates nothing (pass `out` / `out_scores` to allocate nothing here
+    either). Calls that overlap on one GPU race on that scratch."""
+    _dev(q, "q")
+    _dev(k_cache, "k_cache")
+    ctx = torch.as_tensor(ctx_lens, dtype=torch.int64).cpu().contiguous()
+    B = ctx.numel()
+    rows, H, D = q.shape
+    if rows != B * g or k_cache.dim() != 3 or k_cache.shape[1:] != (H, D) or k_cache.dtype != q.dtype:
+        raise ValueError("decode shapes: q (B*g, H, D), k_cache (sum ctx, H, D), one dtype")
+    if k_cache.shape[0] != int(ctx.sum()):
+        raise ValueError("k_cache rows must equal the sum of ctx_lens")
+    out, sc = _outputs((rows, H, top_k), q.device, return_scores, out, out_scores)
+    _check(lib.pivot_index_decode_noalloc(_ptr(q), _ptr(k_cache), _dtype_code(q), ctypes.c_void_p(ctx.data_ptr()),
+                                          B, g, H, D, top_k, candidate_ratio, _MODES[mode], _ptr(out), _ptr(sc),
+                                          _stream(q.device)), "pivot_index_decode_noalloc")
     return (out, sc) if return_scores else out
 
 

@@ -35,12 +35,20 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/pivot.h"
 #include "pivot_device.hpp"
 
 using namespace pivot;
+
+// Scratch of pivot_index_decode_noalloc: device memory the library owns, one
+// copy per GPU, held until the process ends. Host code never uses this name
+// as an address (on the host it is a stand-in): it takes the device address
+// from hipGetSymbolAddress, once per device.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)256 << 20;
+static __device__ __align__(256) unsigned char scratch[STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -2173,6 +2181,7 @@ struct ProfRec {
     hipEvent_t a, b;
 };
 bool g_prof_on = false;
+thread_local bool t_prof_off = false;  // set while a call must record no events
 int g_prof_used = 0;     // records filled since the last read
 int g_prof_created = 0;  // records whose events exist
 ProfRec g_prof[PROF_MAX];
@@ -2182,7 +2191,7 @@ struct StageTimer {
     int slot = -1;
     hipStream_t st;
     StageTimer(int stage, hipStream_t s) : st(s) {
-        if (!g_prof_on || g_prof_used >= PROF_MAX) return;
+        if (!g_prof_on || t_prof_off || g_prof_used >= PROF_MAX) return;
         ProfRec &r = g_prof[g_prof_used];
         if (g_prof_used >= g_prof_created) {
             if (hipEventCreate(&r.a) != hipSuccess) return;
@@ -2886,6 +2895,25 @@ int run_decode(const DecPlan &dp, const int64_t *ctx, const T *q, const T *kc, i
     return PIVOT_OK;
 }
 
+// Device address of `scratch` on the current device, looked up on the
+// first call on that device (with the device current) and kept.
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES];
+
+int static_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return PIVOT_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PIVOT_EHIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return PIVOT_OK;
+}
+
 }  // namespace
 
 // =================================================================== C ABI
@@ -3004,6 +3032,31 @@ int pivot_index_decode(const void *q, const void *k_cache, int32_t dtype, const 
                                   out_score, (unsigned char *)workspace, st);
     return run_decode<float>(dp, ctx_lens_host, (const float *)q, (const float *)k_cache, out_idx, out_score,
                              (unsigned char *)workspace, st);
+}
+
+int pivot_index_decode_noalloc(const void *q, const void *k_cache, int32_t dtype, const int64_t *ctx_lens_host,
+                               int32_t B, int32_t g, int32_t H, int32_t D, int32_t top_k, double candidate_ratio,
+                               int32_t mode, int32_t *out_idx, float *out_score, void *stream) {
+    DecPlan dp;
+    int rc = make_dec_plan(dp, B, ctx_lens_host, g, H, D, top_k, candidate_ratio, mode, dtype);
+    if (rc) return rc;
+    if (!q || !k_cache || !out_idx) return PIVOT_EINVAL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned4(out_idx) || (out_score && !aligned4(out_score)))
+        return PIVOT_EINVAL;
+    if (dp.bytes > STATIC_SCRATCH_BYTES) return PIVOT_EWORKSPACE;
+    void *ws = nullptr;
+    rc = static_scratch(&ws);
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    t_prof_off = true;  // no event records: nothing is created during this call
+    if (dtype == PIVOT_BF16)
+        rc = run_decode<bf16_t>(dp, ctx_lens_host, (const bf16_t *)q, (const bf16_t *)k_cache, out_idx, out_score,
+                                (unsigned char *)ws, st);
+    else
+        rc = run_decode<float>(dp, ctx_lens_host, (const float *)q, (const float *)k_cache, out_idx, out_score,
+                               (unsigned char *)ws, st);
+    t_prof_off = false;
+    return rc;
 }
 
 int pivot_profile_enable(int on) {
