@@ -75,6 +75,36 @@ def counted_traffic(stage: str, S: int, H: int, g: int):
         return None
 
 
+def recall_rows(a, b, skip_first_rows: int = 0, H: int = 1):
+    """Recall@top_k of index rows a against reference rows b (device int32
+    (S*H, top_k), -1 padding): mean over rows of |a & b| / |b|, leaving out
+    the first skip_first_rows positions (position 0 has a single key)."""
+    import torch
+    k = b.shape[1]
+    tot, n = 0.0, 0
+    for r0 in range(skip_first_rows * H, b.shape[0], 1 << 16):
+        bb, aa = b[r0:r0 + (1 << 16)].long(), a[r0:r0 + (1 << 16)].long()
+        bs, _ = torch.sort(torch.where(bb >= 0, bb, 1 << 40), dim=1)
+        pos = torch.searchsorted(bs, aa).clamp(max=k - 1)
+        hit = ((torch.gather(bs, 1, pos) == aa) & (aa >= 0)).sum(1)
+        nb = (bb >= 0).sum(1)
+        ok = nb > 0
+        tot += float((hit[ok].double() / nb[ok].double()).sum())
+        n += int(ok.sum())
+    return tot / max(n, 1)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def time_calls(fn, steps: int, warmup: int, pv):
     import torch
     for _ in range(warmup):
@@ -258,8 +288,16 @@ def main():
         t = stages[dom] / 1e3 / max(1, launches.get(dom, 1))
         achieved = amount / max(1, launches.get(dom, 1)) / t
         scale = 1e12 if unit == "TFLOP/s" else 1e9
+        traffic = counted_traffic(dom, S, H, g)
         roof = {"bound": bound, "kernel": dom, "achieved": achieved / scale, "peak": peak / scale,
-                "unit": unit, "frac": achieved / peak, "traffic": counted_traffic(dom, S, H, g)}
+                "unit": unit, "frac": achieved / peak, "traffic": traffic,
+                "achieved_basis": "algorithmic work per launch / launch time"}
+        if traffic is not None and bound == "hbm":
+            # the bytes the counters saw leave or reach the L2 (a part of the
+            # gathered rows hits in L2): the HBM-side rate beside the
+            # algorithmic one
+            roof["traffic_GBps"] = traffic / t / 1e9
+            roof["traffic_frac"] = traffic / t / peak
     scan_t = stages.get("scan", 0.0) / 1e3
     scan_roof = {"bound": "mfma", "achieved": scan_flops / scan_t / 1e12 if scan_t else None,
                  "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
@@ -353,12 +391,13 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
+        from oracle.pool import OraclePool, workers_default
         rng = np.random.default_rng(11)
         G = (S + g - 1) // g
         done_rows = 0
         t0 = time.perf_counter()
         ngroups = 0
-        log(f"timing the oracle for about {args.cpu_seconds:.0f} s")
+        log(f"timing the oracle on one core for about {args.cpu_seconds:.0f} s")
         while time.perf_counter() - t0 < args.cpu_seconds:
             hh = rng.integers(0, H, 1).astype(np.int32)
             jj = rng.integers(0, G, 1)
@@ -366,10 +405,28 @@ def main():
             done_rows += int(min(g, S - jj[0] * g))
             ngroups += 1
         el = time.perf_counter() - t0
-        cpu = {"value": done_rows / el, "unit": "queries/s", "cores": 1, "kind": "oracle",
-               "sample": f"{ngroups} PIVOT-Refine groups (all {g} members each) drawn uniformly over "
-                         f"(head, group) of this workload, seed 11, single-threaded C oracle, {el:.1f} s"}
-        log(f"oracle {cpu['value']:.2f} queries/s")
+        single = {"value": done_rows / el, "unit": "queries/s", "cores": 1, "groups": ngroups, "seconds": el}
+        log(f"oracle, one core: {single['value']:.2f} queries/s")
+        nw = workers_default()
+        log(f"timing the oracle on {nw} cores (one single-threaded process each) for about {args.cpu_seconds:.0f} s")
+        with OraclePool(workers=nw, need_bytes=qh.nbytes + kh.nbytes) as pool:
+            qr, kr = pool.put(qh), pool.put(kh)
+            w0 = time.perf_counter()
+            res = pool.map([("timed_groups", dict(q=qr, k=kr, seconds=args.cpu_seconds, seed=11 + 1000 * (w + 1),
+                                                  top_k=top_k, g=g, candidate_ratio=ratio, mode="refine"))
+                            for w in range(nw)])
+            wall = time.perf_counter() - w0
+        rows_all = sum(r[0] for r in res)
+        rate = sum(r[0] / r[2] for r in res)
+        cpu = {"value": rate, "unit": "queries/s", "cores": nw, "kind": "oracle",
+               "sample": f"PIVOT-Refine groups (all {g} members each) drawn uniformly over (head, group) of this "
+                         f"workload: {nw} single-threaded C oracle processes for {args.cpu_seconds:.0f} s each "
+                         f"({sum(r[1] for r in res)} groups), value = sum of the per-process rates; "
+                         f"one core alone: {single['value']:.1f} queries/s ({ngroups} groups, seed 11)",
+               "single_core": single,
+               "all_core_wall": {"rows": rows_all, "seconds": wall, "queries_per_s": rows_all / wall},
+               "cpu_model": cpu_model(), "nproc": os.cpu_count()}
+        log(f"oracle, {nw} cores: {rate:.2f} queries/s")
     del ws, out, q, k, cfg
     torch.cuda.empty_cache()
 
@@ -409,7 +466,7 @@ def main():
                 return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
             return torch.from_numpy(a).to(dev)
 
-        def prefill_config(name, qd, kd, tk, gg, modes, dense_too, ksteps):
+        def prefill_config(name, qd, kd, tk, gg, modes, dense_too, ksteps, all_rows_recall=False):
             Sx, Hx, Dx = qd.shape
             Kx = pv.candidate_count(tk, 2.0)
             wsx = torch.empty(max(pv.prefill_workspace_bytes(Sx, Hx, Dx, tk, gg, 2.0, m, qd.dtype)
@@ -431,15 +488,28 @@ def main():
                 cms, _, cst, _ = time_calls(dcall, ksteps, args.warmup, pv)
                 res["dense"] = {"ms_per_step": cms, "queries_per_s": Sx * Hx / (cms / 1e3), "stage_ms": cst}
                 log(f"{name} dense: {cms:.3f} ms/step")
+            if all_rows_recall:
+                # recall@top_k of every row (positions >= 1) against the dense
+                # indexer (the GPU's: bit-exact to the oracle on integer
+                # inputs, tie-tolerant on Gaussian ones)
+                dref = pv.dense_index(qd, kd, tk, max_workspace_bytes=48 << 30).view(Sx * Hx, tk)
+                rec = {}
+                for mode in modes:
+                    rows = pv.index_prefill(qd, kd, tk, gg, 2.0, mode, workspace=wsx).view(Sx * Hx, tk)
+                    rec[mode] = recall_rows(rows, dref, skip_first_rows=1, H=Hx)
+                rec.update({"rows": (Sx - 1) * Hx, "against": "dense indexer (GPU), every row with i >= 1"})
+                res["recall"] = rec
+                log(f"{name} recall@{tk}: {rec}")
+                del dref
             del wsx, outx
             return res
 
         tc = syn.tiny_prefill()
         configs["tiny"] = prefill_config("tiny S=1024 H=8 D=64 fp32", host(tc["q"]), host(tc["k"]), 64, 8,
-                                         ("refine", "reuse"), True, args.steps * 4)
+                                         ("refine", "reuse"), True, args.steps * 4, all_rows_recall=True)
         ic = syn.int_prefill()
         configs["int16k"] = prefill_config("S=16384 H=16 integer bf16", host(ic["q"]), host(ic["k"]), 512, 8,
-                                           ("refine", "reuse"), False, args.steps * 2)
+                                           ("refine", "reuse"), False, args.steps * 2, all_rows_recall=True)
         del tc, ic
         log("drawing the long prefill S=131072 H=32 g=16 on the device")
         lc = syn.long_prefill_device(dev, S=131072, H=32, g=16, seed=1004)
@@ -516,7 +586,7 @@ def main():
             "literal_refine": literal,
             "sparse_attention": attention,
             "configs": configs,
-            "host": {"cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count(),
+            "host": {"cpu": cpu_model(), "nproc": os.cpu_count(),
                      "gpu": torch.cuda.get_device_name(dev)},
         },
     }

@@ -1,4 +1,8 @@
-"""Runs oracle calls over the host's cores (test infrastructure).
+"""Runs oracle calls over the host's cores.
+
+TEST INFRASTRUCTURE, like the rest of this package: used by the tests and by
+the CPU-baseline leg of the benchmark only. It holds no arithmetic of the
+method; it only distributes calls of ``oracle`` functions over processes.
 
 The oracle is single-threaded C; full-size parity runs many independent
 calls (one per head, or per group, or per sequence) in worker processes.
@@ -71,7 +75,28 @@ def decode_sequence(q, kc, ctx, g, top_k, candidate_ratio, mode):
     return idx[:, 0], sc[:, 0], oracle.proxy(q, g, 0, 0), cand
 
 
-_TASKS = {"prefill_groups_of_head": prefill_groups_of_head, "decode_sequence": decode_sequence}
+def timed_groups(q, k, seconds, seed, top_k, g, candidate_ratio, mode):
+    """Whole groups drawn uniformly over (head, group) and run one after the
+    other until `seconds` have passed; returns (rows, groups, seconds)."""
+    import time
+
+    import oracle
+    S, H = q.shape[0], q.shape[1]
+    G = (S + g - 1) // g
+    rng = np.random.default_rng(seed)
+    rows = groups = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        hh = rng.integers(0, H, 1).astype(np.int32)
+        jj = rng.integers(0, G, 1)
+        oracle.prefill_groups(q, k, hh, jj, top_k, g, candidate_ratio, mode)
+        rows += int(min(g, S - jj[0] * g))
+        groups += 1
+    return rows, groups, time.perf_counter() - t0
+
+
+_TASKS = {"prefill_groups_of_head": prefill_groups_of_head, "decode_sequence": decode_sequence,
+          "timed_groups": timed_groups}
 
 
 def _run(task):

@@ -362,7 +362,7 @@ LARGE_TOPK = [
 def test_large_top_k_bit_exact_integer_inputs(pv, mode, S, H, D, top_k, ratio, g, dtype):
     """top_k above 2048 and K up to 8192 against the oracle, bit for bit on
     integer inputs (index-only and with scores)."""
-    from tests.oracle_pool import OraclePool
+    from oracle.pool import OraclePool
     print(f"\n[large top_k] S={S} H={H} D={D} k={top_k} r={ratio} g={g} {dtype} {mode}", flush=True)
     a = 8 if dtype == "f32" else 4
     q = syn.integers((S, H, D), 7600 + top_k, a, dtype)

@@ -1,6 +1,6 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 bench times (index-only rows, the wavefront selectors), against the oracle
-run over the host's cores (tests/oracle_pool.py).
+run over the host's cores (oracle/pool.py).
 
   * S=16384, H=16, D=128 bf16 integers in [-4, 4], top_k=512, g=8, K=1024:
     every float32 score is exact, so every row of every head is compared
@@ -21,7 +21,7 @@ import pytest
 
 import synthetic as syn
 from tests import parity
-from tests.oracle_pool import OraclePool
+from oracle.pool import OraclePool
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
