@@ -338,14 +338,23 @@ def main():
         attention = {}
         for mode in ("refine", "reuse"):
             pv.index_prefill(q, k, top_k, g, ratio, mode, workspace=ws, out=out)
-            ams, _, _, _ = time_calls(lambda: pv.sparse_attention(q, k, v, out, out=aout), max(1, args.steps // 2),
-                                      1, pv)
+            # Reuse rows are shared by the members of a group: the grouped
+            # attention gathers each group's rows once
+            gg = g if mode == "reuse" else None
+            ams, _, _, _ = time_calls(lambda: pv.sparse_attention(q, k, v, out, out=aout, g=gg),
+                                      max(1, args.steps // 2), 1, pv)
             # algorithmic bytes: every valid entry's key and value row, plus
             # the query, index row and output row of every (position, head)
             nvalid = float((out >= 0).sum().item())
-            abytes = nvalid * D * 2 * 2 + S * H * (D * 2 + top_k * 4 + D * 4)
+            # algorithmic bytes: the key and value rows of every valid entry
+            # (of every group's row when rows are shared), the queries, the
+            # index rows read and the output
+            nrows_read = S * H if gg is None else ((S + g - 1) // g) * H
+            ngath = nvalid if gg is None else nvalid / g
+            abytes = ngath * D * 2 * 2 + S * H * (D * 2 + D * 4) + nrows_read * top_k * 4
             attention[mode] = {"ms": ams, "queries_per_s": S * H / (ams / 1e3), "valid_entries": nvalid,
-                               "gathered_bytes": nvalid * D * 2 * 2, "algorithmic_GBps": abytes / (ams / 1e3) / 1e9}
+                               "grouped": gg is not None, "gathered_bytes": ngath * D * 2 * 2,
+                               "algorithmic_GBps": abytes / (ams / 1e3) / 1e9}
             log(f"sparse attention on {mode} rows: {ams:.2f} ms ({abytes / (ams / 1e3) / 1e9:.0f} GB/s of row reads)")
         del v, aout
         torch.cuda.empty_cache()

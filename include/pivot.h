@@ -100,6 +100,19 @@ int pivot_sparse_attention(const void *q, const void *k, const void *v,
                            const int32_t *idx, int32_t top_k, float scale,
                            float *out, void *stream);
 
+/* The same attention for rows shared by groups of g consecutive positions
+ * (the rows PIVOT-Reuse returns: every member of a group has the row of its
+ * first position): positions j*g .. min(j*g + g, S) - 1 all attend over the
+ * index row of position j*g, which is read once per group; the other rows of
+ * idx are not read. Each group's key and value rows are gathered once for
+ * all of its members. Arguments and errors as for pivot_sparse_attention,
+ * plus g >= 1; the output is the attention above for every position. */
+int pivot_sparse_attention_grouped(const void *q, const void *k, const void *v,
+                                   int32_t dtype, int64_t S, int32_t H,
+                                   int32_t D, const int32_t *idx,
+                                   int32_t top_k, int32_t g, float scale,
+                                   float *out, void *stream);
+
 /* Human-readable text of a status code (static storage). */
 const char *pivot_status_string(int status);
 

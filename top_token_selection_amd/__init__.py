@@ -35,7 +35,7 @@ EXPORTED = (
     "pivot_status_string", "pivot_candidate_count", "pivot_prefill_workspace_bytes",
     "pivot_index_prefill", "pivot_decode_workspace_bytes", "pivot_index_decode",
     "dense_index_workspace_bytes", "dense_index", "pivot_profile_enable", "pivot_profile_read",
-    "pivot_sparse_attention", "pivot_index_decode_noalloc",
+    "pivot_sparse_attention", "pivot_index_decode_noalloc", "pivot_sparse_attention_grouped",
 )
 
 #: kernel stages reported by the stage timer (include/pivot.h)
@@ -75,6 +75,9 @@ lib.pivot_profile_read.argtypes = [_vp, _vp, ctypes.c_int]
 lib.pivot_profile_read.restype = ctypes.c_int
 lib.pivot_sparse_attention.argtypes = [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp, _i32, ctypes.c_float, _vp, _vp]
 lib.pivot_sparse_attention.restype = ctypes.c_int
+lib.pivot_sparse_attention_grouped.argtypes = [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp, _i32, _i32, ctypes.c_float,
+                                               _vp, _vp]
+lib.pivot_sparse_attention_grouped.restype = ctypes.c_int
 
 
 class PivotError(RuntimeError):
@@ -274,10 +277,12 @@ def index_decode_noalloc(q, k_cache, ctx_lens, g, top_k=2048, candidate_ratio=2.
     return (out, sc) if return_scores else out
 
 
-def sparse_attention(q, k, v, idx, scale=None, out=None):
+def sparse_attention(q, k, v, idx, scale=None, out=None, g=None):
     """Downstream sparse attention over indexer rows: float32 (S, H, D).
     softmax(scale q_i . k_c) over the entries c of idx[i, h] in [0, S) (-1 is
-    padding), applied to v_c; scale defaults to D**-0.5."""
+    padding), applied to v_c; scale defaults to D**-0.5. With g, positions
+    j*g .. j*g+g-1 all attend over the row of position j*g (Reuse rows), and
+    each group's rows are gathered once."""
     for name, t in (("q", q), ("k", k), ("v", v), ("idx", idx)):
         _dev(t, name)
     if q.shape != k.shape or q.shape != v.shape or q.dim() != 3 or len({q.dtype, k.dtype, v.dtype}) != 1:
@@ -290,6 +295,13 @@ def sparse_attention(q, k, v, idx, scale=None, out=None):
     elif out.dtype != torch.float32 or tuple(out.shape) != (S, H, D) or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 (S, H, D) tensor")
     sc = float(D) ** -0.5 if scale is None else float(scale)
+    if g is not None:
+        # rows shared by groups of g positions (Reuse rows): the row of each
+        # group's first position serves all of its members
+        _check(lib.pivot_sparse_attention_grouped(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), S, H, D, _ptr(idx),
+                                                  idx.shape[2], int(g), sc, _ptr(out), _stream(q.device)),
+               "pivot_sparse_attention_grouped")
+        return out
     _check(lib.pivot_sparse_attention(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), S, H, D, _ptr(idx), idx.shape[2],
                                       sc, _ptr(out), _stream(q.device)), "pivot_sparse_attention")
     return out

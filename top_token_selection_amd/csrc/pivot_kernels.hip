@@ -2169,6 +2169,214 @@ __global__ void __launch_bounds__(256) k_sparse_attn(AttnParams p) {
     }
 }
 
+// ------------------------------------------- sparse attention, shared rows
+
+constexpr int AG_NQ = 8;         // member queries per block
+constexpr int AG_CH = 64;        // index-row entries per chunk
+constexpr int AG_THREADS = 256;  // 4 wavefronts
+
+struct AttnGroupParams {
+    const void *q, *k, *v;   // (S, H, D)
+    const int32_t *idx;      // (S, H, top_k); the row of position j*g serves group j
+    int64_t S;
+    int H, top_k, g;
+    int64_t G;               // groups per head
+    int nmb;                 // blocks per group (AG_NQ members each)
+    float scale_log2;        // scale * log2(e)
+    float *out;              // (S, H, D) float32
+};
+
+// Sparse attention for groups of g consecutive positions that share one
+// index row (PIVOT-Reuse rows are the same for every member of a group):
+// one block per (head, group, AG_NQ members) walks the row in chunks of
+// AG_CH entries. The chunk's key and value rows are gathered once for all
+// members into LDS (values as float32); scores come from MFMA 16x16 tiles
+// (16 entries x 16 query columns, members in the first columns) and leave
+// as base-2 logits; the softmax runs online per member (chunk maxima and
+// sums through LDS); the weighted sum runs on the VALU, one thread per
+// (member, D/32 dimensions). The next chunk's rows are loaded while the
+// current one is reduced.
+template <typename T, int D>
+__global__ void __launch_bounds__(AG_THREADS) k_attn_group(AttnGroupParams p) {
+    constexpr bool F32 = std::is_same<T, float>::value;
+    constexpr int RB = D * (int)sizeof(T);       // bytes of a key row
+    constexpr int RBP = RB + 16;                 // LDS stride of a key row (spreads the banks)
+    constexpr int PER = RB / 4 / 16;             // 16-byte pieces per thread per row (4 threads a row)
+    constexpr int DS = D / 32;                   // dimensions per thread in the weighted sum
+    constexpr int VS = D + 4;                    // LDS stride (floats) of a value row (spreads the banks)
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char *kt = smem;                                   // AG_CH key rows
+    float *vt = (float *)(smem + AG_CH * RBP);                  // AG_CH value rows, float32
+    float *ps = vt + AG_CH * VS;                                // [AG_NQ][AG_CH] probabilities
+    float *wst = ps + AG_NQ * AG_CH;                            // [4][AG_NQ] wave maxima, [4][AG_NQ] sums
+
+    const int nblk = (int)(p.G * p.H) * p.nmb;
+    const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)nblk);
+    const int mb = (int)(L % p.nmb);
+    const int64_t grp = L / p.nmb;
+    const int h = (int)(grp / p.G);
+    const int64_t j = grp % p.G;
+    const int64_t i0 = j * p.g + (int64_t)mb * AG_NQ;           // first member of this block
+    const int m = (int)min((int64_t)AG_NQ, min(j * p.g + p.g, p.S) - i0);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int qcol = l & 15, lq = l >> 4;
+    const int pq = tid >> 5, sl = tid & 31;                     // weighted sum: member, dimension slice
+    const T *Q = (const T *)p.q;
+    const unsigned char *K = (const unsigned char *)p.k;
+    const unsigned char *V = (const unsigned char *)p.v;
+    const int64_t rstride = (int64_t)p.H * RB;                  // bytes between positions
+    const int32_t *row = p.idx + ((j * p.g) * p.H + h) * (int64_t)p.top_k;
+
+    // member queries as MFMA B fragments (column qcol), zero past m
+    typedef typename std::conditional<F32, f32x4_t, bf16x8_t>::type frag_t;
+    constexpr int NKS = F32 ? D / 16 : D / 32;
+    frag_t bq[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        if (qcol < m) {
+            const int dofs = F32 ? 16 * ks + 4 * lq : 32 * ks + 8 * lq;
+            bq[ks] = *(const frag_t *)(Q + ((i0 + qcol) * p.H + h) * (int64_t)D + dofs);
+        } else {
+            bq[ks] = frag_t{};
+        }
+    }
+
+    // chunk loads: thread t takes entry r = t / 4 of the chunk, quarter t % 4
+    // of its key and value rows; two chunks are in flight (register sets A
+    // and B, the chunk's parity)
+    const int lr = tid >> 2, lp = tid & 3;
+    struct ChunkRegs {
+        u32x4_t k[PER], v[PER];
+        bool valid;
+    };
+    auto load_chunk = [&](int c0, ChunkRegs &cr) {
+        const int e = c0 + lr;
+        const int32_t c = e < p.top_k ? row[e] : -1;
+        cr.valid = c >= 0 && (int64_t)c < p.S;
+        const int64_t off = (cr.valid ? (int64_t)c : 0) * rstride + (int64_t)h * RB + lp * (RB / 4);
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+            cr.k[t] = *(const u32x4_t *)(K + off + 16 * t);
+            cr.v[t] = *(const u32x4_t *)(V + off + 16 * t);
+        }
+    };
+    // mrun / lrun / o: member pq's running maximum (base-2 logits), sum of
+    // weights and weighted sum; mcol: member qcol's running maximum
+    float mrun = -INFINITY, lrun = 0.f, mcol = -INFINITY, o[DS];
+#pragma unroll
+    for (int d = 0; d < DS; ++d) o[d] = 0.f;
+    uint32_t *cvalid = (uint32_t *)(wst + 8 * AG_NQ);           // [AG_CH] entry valid flags
+    ChunkRegs ra, rb;
+    load_chunk(0, ra);
+    if (AG_CH < p.top_k) load_chunk(AG_CH, rb);
+    auto chunk = [&](int c0, ChunkRegs &cr) {
+        // chunk into LDS
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+            *(u32x4_t *)(kt + lr * RBP + lp * (RB / 4) + 16 * t) = cr.k[t];
+            float *vd = vt + lr * VS + lp * (D / 4) + (16 / (int)sizeof(T)) * t;
+            if constexpr (F32) {
+                *(u32x4_t *)vd = cr.v[t];
+            } else {
+                const u32x4_t x = cr.v[t];
+                *(float4 *)vd = make_float4(__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xFFFF0000u),
+                                            __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xFFFF0000u));
+                *(float4 *)(vd + 4) = make_float4(__uint_as_float(x[2] << 16), __uint_as_float(x[2] & 0xFFFF0000u),
+                                                  __uint_as_float(x[3] << 16), __uint_as_float(x[3] & 0xFFFF0000u));
+            }
+        }
+        if (lp == 0) cvalid[lr] = cr.valid ? 1u : 0u;
+        __syncthreads();
+        // the chunk after next into the registers just emptied
+        if (c0 + 2 * AG_CH < p.top_k) load_chunk(c0 + 2 * AG_CH, cr);
+        // scores of entries 16 w .. 16 w + 15 for the member columns
+        f32x4_t acc = f32x4_t{};
+        {
+            const unsigned char *kr = kt + (16 * w + qcol) * RBP;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                if constexpr (F32) {
+                    const f32x4_t a = *(const f32x4_t *)(kr + (16 * ks + 4 * lq) * 4);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[v], bq[ks][v], acc, 0, 0, 0);
+                } else {
+                    const bf16x8_t a = *(const bf16x8_t *)(kr + (32 * ks + 8 * lq) * 2);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[ks], acc, 0, 0, 0);
+                }
+            }
+        }
+        // lane (qcol, lq) holds entries 16 w + 4 lq + i of member qcol
+        float sc[4], cm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 16 * w + 4 * lq + i;
+            sc[i] = cvalid[e] ? acc[i] * p.scale_log2 : -INFINITY;
+            cm = fmaxf(cm, sc[i]);
+        }
+        cm = fmaxf(cm, __shfl_xor(cm, 16));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        if (lq == 0 && qcol < AG_NQ) wst[w * AG_NQ + qcol] = cm;
+        __syncthreads();
+        // every thread keeps the running maximum of its own member (score
+        // lanes: column qcol; weighted-sum threads: member pq) from the
+        // chunk maxima of the four wavefronts
+        auto chunk_max = [&](int q) {
+            return fmaxf(fmaxf(wst[q], wst[AG_NQ + q]), fmaxf(wst[2 * AG_NQ + q], wst[3 * AG_NQ + q]));
+        };
+        const int qq = qcol < AG_NQ ? qcol : 0;
+        mcol = fmaxf(mcol, chunk_max(qq));
+        const float mnew = fmaxf(mrun, chunk_max(pq));
+        {
+            const float ref = mcol == -INFINITY ? 0.f : mcol;  // no valid entry yet: every p is 0
+            float psum = 0.f, pv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pv[i] = exp2f(sc[i] - ref);
+                psum += pv[i];
+            }
+            if (qcol < AG_NQ)
+                *(float4 *)(ps + qcol * AG_CH + 16 * w + 4 * lq) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+            psum += __shfl_xor(psum, 16);
+            psum += __shfl_xor(psum, 32);
+            if (lq == 0 && qcol < AG_NQ) wst[4 * AG_NQ + w * AG_NQ + qcol] = psum;
+        }
+        __syncthreads();
+        // weighted sum for member pq, dimensions DS * sl .. DS * sl + DS - 1
+        {
+            const float a = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
+            lrun = lrun * a + ((wst[4 * AG_NQ + pq] + wst[5 * AG_NQ + pq]) + (wst[6 * AG_NQ + pq] + wst[7 * AG_NQ + pq]));
+            mrun = mnew;
+#pragma unroll
+            for (int d = 0; d < DS; ++d) o[d] *= a;
+            const float *pr = ps + pq * AG_CH;
+            const float *vr = vt + DS * sl;
+#pragma unroll 4
+            for (int e = 0; e < AG_CH; e += 4) {
+                const float4 p4 = *(const float4 *)(pr + e);
+                const float pe[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float *vv = vr + (e + u) * VS;
+#pragma unroll
+                    for (int d = 0; d < DS; ++d) o[d] = fmaf(pe[u], vv[d], o[d]);
+                }
+            }
+        }
+        __syncthreads();
+    };
+    for (int c0 = 0; c0 < p.top_k; c0 += 2 * AG_CH) {
+        chunk(c0, ra);
+        if (c0 + AG_CH < p.top_k) chunk(c0 + AG_CH, rb);
+    }
+    if (pq < m) {
+        float *dst = p.out + ((i0 + pq) * p.H + h) * (int64_t)D + DS * sl;
+        const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
+#pragma unroll
+        for (int d = 0; d < DS; ++d) dst[d] = lrun > 0.f ? o[d] * inv : 0.f;
+    }
+}
+
 // ==================================================================== host
 
 enum Stage { ST_PROXY = 0, ST_SAMPLE, ST_TAU, ST_SCAN, ST_SELECT, ST_FALLBACK, ST_REFINE,
@@ -2940,6 +3148,54 @@ int pivot_sparse_attention(const void *q, const void *k, const void *v, int32_t 
         else hipLaunchKernelGGL((k_sparse_attn<float, 128>), dim3((unsigned)nblocks), dim3(256), 0, st, ap);
     }
     return hipGetLastError() == hipSuccess ? PIVOT_OK : PIVOT_EHIP;
+}
+
+int pivot_sparse_attention_grouped(const void *q, const void *k, const void *v, int32_t dtype, int64_t S, int32_t H,
+                                   int32_t D, const int32_t *idx, int32_t top_k, int32_t g, float scale, float *out,
+                                   void *stream) {
+    if (!q || !k || !v || !idx || !out) return PIVOT_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(idx) || !aligned4(out)) return PIVOT_EINVAL;
+    if (S < 1 || H < 1 || top_k < 1 || g < 1 || !std::isfinite(scale)) return PIVOT_EINVAL;
+    if (dtype != PIVOT_F32 && dtype != PIVOT_BF16) return PIVOT_EINVAL;
+    if (S > (int64_t)INT32_MAX) return PIVOT_EINVAL;
+    if (D != 64 && D != 128) return PIVOT_EUNSUPPORTED;
+    AttnGroupParams ap{};
+    ap.q = q;
+    ap.k = k;
+    ap.v = v;
+    ap.idx = idx;
+    ap.S = S;
+    ap.H = H;
+    ap.top_k = top_k;
+    ap.g = g;
+    ap.G = (S + g - 1) / g;
+    ap.nmb = (g + AG_NQ - 1) / AG_NQ;
+    ap.scale_log2 = scale * 1.4426950408889634f;
+    ap.out = out;
+    const int64_t nblocks = ap.G * H * ap.nmb;
+    if (nblocks > (int64_t)INT32_MAX) return PIVOT_EUNSUPPORTED;
+    const size_t esz = dtype == PIVOT_BF16 ? 2 : 4;
+    const size_t lds = (size_t)AG_CH * (D * esz + 16) + (size_t)AG_CH * (D + 4) * 4 + (size_t)AG_NQ * AG_CH * 4 +
+                       8 * AG_NQ * 4 + (size_t)AG_CH * 4;
+    hipStream_t st = (hipStream_t)stream;
+    auto go = [&](const void *fn, auto launch) -> int {
+        HIP_TRY(set_lds(fn, lds));
+        launch();
+        return hipGetLastError() == hipSuccess ? PIVOT_OK : PIVOT_EHIP;
+    };
+    const dim3 grid((unsigned)nblocks), blk(AG_THREADS);
+    if (dtype == PIVOT_BF16) {
+        if (D == 64)
+            return go((const void *)k_attn_group<bf16_t, 64>,
+                      [&] { hipLaunchKernelGGL((k_attn_group<bf16_t, 64>), grid, blk, lds, st, ap); });
+        return go((const void *)k_attn_group<bf16_t, 128>,
+                  [&] { hipLaunchKernelGGL((k_attn_group<bf16_t, 128>), grid, blk, lds, st, ap); });
+    }
+    if (D == 64)
+        return go((const void *)k_attn_group<float, 64>,
+                  [&] { hipLaunchKernelGGL((k_attn_group<float, 64>), grid, blk, lds, st, ap); });
+    return go((const void *)k_attn_group<float, 128>,
+              [&] { hipLaunchKernelGGL((k_attn_group<float, 128>), grid, blk, lds, st, ap); });
 }
 
 const char *pivot_status_string(int status) {
