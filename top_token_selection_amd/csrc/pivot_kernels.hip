@@ -1551,10 +1551,11 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
                 emit((const uint32_t *)buf);
                 return true;
             }
+            // staged entries u = l, l + 64, ...: every lane takes a share
+            // whatever the staged count
             auto fend = [&](uint32_t f) { return (h2[f >> 1] >> ((f & 1u) << 4)) & 0xFFFFu; };
-            for (uint32_t t = 0; t < (uint32_t)NSL; ++t) {
-                const uint32_t u = s0 + t;
-                if (u < nsc) {
+            for (uint32_t u = (uint32_t)l; u < nsc; u += 64u) {
+                {
                     const uint32_t w = buf[u];
                     const uint32_t f = tag[u];
                     const uint32_t end = fend(f);
@@ -1562,11 +1563,22 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
                     const uint32_t lw = w >> POSB;
                     const uint32_t myidx = idx_of(w & PM);
                     uint32_t rank = 0;
-                    for (uint32_t x = beg; x < end; ++x) {
-                        const uint32_t en = buf[x];
-                        const uint32_t le = en >> POSB;
-                        if (le > lw) ++rank;
-                        else if (le == lw && x != u) rank += idx_of(en & PM) < myidx ? 1u : 0u;
+                    // four bucket companions per iteration: their LDS reads
+                    // are in flight together (slots past the bucket are
+                    // read inside the staging area and not counted)
+                    for (uint32_t x = beg; x < end; x += 4u) {
+                        uint32_t en[4], ix[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) en[i] = buf[min(x + (uint32_t)i, end - 1u)];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ix[i] = idx_of(en[i] & PM);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t xi = x + (uint32_t)i;
+                            const uint32_t le = en[i] >> POSB;
+                            const bool in = xi < end && xi != u;
+                            rank += (in && (le > lw || (le == lw && ix[i] < myidx))) ? 1u : 0u;
+                        }
                     }
                     if (beg + rank < msel) put(beg + rank, myidx);
                 }
