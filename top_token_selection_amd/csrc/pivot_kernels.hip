@@ -182,7 +182,7 @@ struct ScanParams {
     const float *tau;       // per-row threshold, nullptr = keep all
     uint32_t *out;          // survivors [(row*2+half)*stride + slot]: (float bits, key) pairs
     int cap_half;           // more than this many in a half = overflow
-    int stride;             // slots per (row, half): cap_half + 32
+    int stride;             // slots per (row, half): cap_half + 32, a multiple of 8
     int *cnt;               // survivors per (row, half); > cap_half = overflow
     int64_t min_n;          // rows with prefix <= min_n are skipped
     int n_tiles, Hc;
@@ -222,11 +222,10 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     constexpr int NSTREAM = 2 * SCAN_THREADS;  // (row, half) streams per block
     extern __shared__ __align__(16) unsigned char smem[];
     // survivor rings (static LDS, so that addresses fold into offsets):
-    // score bits [RING][NSTREAM], then key indices likewise; the key tiles
-    // are the dynamic LDS
-    __shared__ __align__(16) uint32_t ringS[2 * RING * NSTREAM];
-    constexpr uint32_t RROW = NSTREAM * 4;         // bytes per ring row
-    constexpr uint32_t RKEYS = RING * NSTREAM;     // words from scores to keys
+    // (score bits, key index) entries [RING][NSTREAM]; the key tiles are
+    // the dynamic LDS
+    __shared__ __align__(16) uint2 ringS[RING * NSTREAM];
+    constexpr uint32_t RROW = NSTREAM * 8;         // bytes per ring row
     static_assert((RING & (RING - 1)) == 0 && (RROW & (RROW - 1)) == 0, "ring sizes are powers of two");
     static_assert(FLUSH == 8, "a chunk is four lanes' 16-byte stores");
 
@@ -359,52 +358,67 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
         }
     };
 
-    // Every stream of column block gb with FLUSH or more staged survivors
-    // sends its FLUSH oldest (entries fl .. fl+7, ring rows fl % RING ..)
-    // as one 64-byte chunk. The streams are ranked; the r-th one passes its
-    // chunk's byte offset in the survivor array and its lane with the
-    // chunk's first ring row to lane 4r (forward permute, no LDS memory)
-    // and over its quad (DPP), and lane 4r + q stores entries fl + 2q,
-    // fl + 2q + 1: an instruction writes 16 whole chunks. At most cap_half
-    // + 16 are ever kept, inside the stream's stride. Wavefront-uniform
-    // control flow.
+    // Every stream with FLUSH or more staged survivors sends its FLUSH
+    // oldest (entries fl .. fl+7, ring rows fl % RING ..) as one 64-byte
+    // chunk. The streams of each column block are ranked; the r-th one
+    // passes one word -- its chunk's index in the survivor array (64-byte
+    // units) above its lane and the chunk's first ring row -- to lane 4r
+    // (forward permute, no LDS memory) and over its quad (DPP), and lane
+    // 4r + q stores entries fl + 2q, fl + 2q + 1 (one LDS read of two ring
+    // rows): an instruction writes 16 whole chunks. Both column blocks'
+    // passes run side by side, so their LDS round trips overlap. At most
+    // cap_half + 16 are ever kept, inside the stream's stride.
+    // Wavefront-uniform control flow.
     static_assert(RING % FLUSH == 0, "a chunk's ring rows do not wrap");
-    auto flush = [&](int gb) {
-        const bool need = cs[gb] / RROW - fl[gb] >= (uint32_t)FLUSH;
-        const uint64_t M = __ballot(need);
-        if (M == 0) return;
-        const uint32_t rank =
-            __builtin_amdgcn_mbcnt_hi((uint32_t)(M >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)M, 0u));
-        const int nf = __popcll(M);
-        const uint32_t mydst = soff0[gb] + fl[gb] * 8u;
-        const uint32_t mysrc = (uint32_t)l | ((fl[gb] % RING) << 6);
-        for (int r0 = 0; r0 < nf; r0 += 16) {
-            // senders target lane 4 (rank - r0); the others an odd lane
-            const bool mine = need && rank - (uint32_t)r0 < 16u;
-            const int to = mine ? (int)(rank - (uint32_t)r0) * 16 : (l | 1) * 4;
-            const uint32_t sdst = dpp_u32<0x00>(0u, (uint32_t)__builtin_amdgcn_ds_permute(to, (int)mydst));
-            const uint32_t ssrc = dpp_u32<0x00>(0u, (uint32_t)__builtin_amdgcn_ds_permute(to, (int)mysrc));
-            if ((l >> 2) < nf - r0) {
-                const uint32_t q2 = 2u * (uint32_t)(l & 3);
-                const uint32_t *src = ringS + gb * SCAN_THREADS + w * 64 + (int)(ssrc & 63u);
-                const uint32_t ia = ((ssrc >> 6) + q2) * NSTREAM, ib = ia + NSTREAM;
-                const uint2 a = make_uint2(src[ia], src[ia + RKEYS]);
-                const uint2 b = make_uint2(src[ib], src[ib + RKEYS]);
-                *(uint4 *)(sb + (sdst + 8u * q2)) = make_uint4(a.x, a.y, b.x, b.y);
+    auto flush = [&]() {
+        bool need[2];
+        uint64_t M[2];
+        uint32_t rank[2], pk[2];
+        int nf[2];
+#pragma unroll
+        for (int gb = 0; gb < 2; ++gb) {
+            need[gb] = cs[gb] / RROW - fl[gb] >= (uint32_t)FLUSH;
+            M[gb] = __ballot(need[gb]);
+            nf[gb] = __popcll(M[gb]);
+            rank[gb] = __builtin_amdgcn_mbcnt_hi((uint32_t)(M[gb] >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)M[gb], 0u));
+            pk[gb] = ((soff0[gb] / 64u + fl[gb] / 8u) << 10) | ((fl[gb] % RING) << 6) | (uint32_t)l;
+        }
+        if ((M[0] | M[1]) == 0) return;
+        const int nmax = max(nf[0], nf[1]);
+        for (int r0 = 0; r0 < nmax; r0 += 16) {
+            uint32_t got[2];
+#pragma unroll
+            for (int gb = 0; gb < 2; ++gb) {
+                // senders target lane 4 (rank - r0); the others an odd lane
+                const bool mine = need[gb] && rank[gb] - (uint32_t)r0 < 16u;
+                const int to = mine ? (int)(rank[gb] - (uint32_t)r0) * 16 : (l | 1) * 4;
+                got[gb] = dpp_u32<0x00>(0u, (uint32_t)__builtin_amdgcn_ds_permute(to, (int)pk[gb]));
+            }
+#pragma unroll
+            for (int gb = 0; gb < 2; ++gb) {
+                if ((l >> 2) < nf[gb] - r0) {
+                    const uint32_t q2 = 2u * (uint32_t)(l & 3);
+                    const uint2 *e = ringS + (((got[gb] >> 6) & (RING - 1)) + q2) * NSTREAM + gb * SCAN_THREADS +
+                                     w * 64 + (int)(got[gb] & 63u);
+                    const uint2 a = e[0], b = e[NSTREAM];
+                    *(uint4 *)(sb + (got[gb] >> 10) * 64u + 8u * q2) = make_uint4(a.x, a.y, b.x, b.y);
+                }
             }
         }
-        fl[gb] += need ? (uint32_t)FLUSH : 0u;
+#pragma unroll
+        for (int gb = 0; gb < 2; ++gb) fl[gb] += need[gb] ? (uint32_t)FLUSH : 0u;
     };
 
     // keep the scores of tile kt that reach the row's threshold; at most 16
     // per stream and tile. Tiles below every row's prefix end skip the causal
-    // test. A flush check after every 8 scores keeps the ring from filling.
-    // Per score: one compare (two on causal tiles), the count update, the
-    // ring row address from the count (one and-or), and one LDS instruction
-    // storing score bits and key index; the 16 key indices of the tile are
-    // shared by both column blocks. A slot is written whether kept or not
-    // (row cnt % RING is free: fewer than RING entries wait); only kept ones
-    // are counted.
+    // test. A flush check after every 8 scores of each column block keeps
+    // the ring from filling. Per score: one compare (two on causal tiles),
+    // the count update, the ring slot address from the count (one and-or),
+    // and one LDS instruction storing score bits and key index; the 16 key
+    // indices of the tile are shared by both column blocks. A slot is
+    // written whether kept or not (row cnt % RING is free: fewer than RING
+    // entries wait); only kept ones are counted.
     auto filter = [&](int kt, const acc_t &acc) {
 #pragma unroll
         for (int gb = 0; gb < 2; ++gb)
@@ -415,23 +429,25 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
         for (int v = 0; v < 16; ++v) kv[v] = tkey + kstr * (uint32_t)(8 * (v >> 2) + (v & 3));
         auto run = [&](auto causal) {
 #pragma unroll
-            for (int gb = 0; gb < 2; ++gb) {
-                // byte offset of this stream's column in a ring row
-                const uint32_t col = (uint32_t)(gb * SCAN_THREADS + stream0) * 4u;
-                // rows' key bound relative to this lane's first key of the tile
-                const int lim = vcount[gb] - (kt * SCAN_KEYS + 4 * half);
+            for (int hv = 0; hv < 2; ++hv) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int vo = 8 * (v >> 2) + (v & 3);
-                    const float sc = acc[gb][v];
-                    bool keep = sc >= tau[gb];
-                    if constexpr (decltype(causal)::value) keep = keep && (vo < lim);
-                    uint32_t *slot = (uint32_t *)((unsigned char *)ringS + ((cs[gb] & ((RING - 1) * RROW)) | col));
-                    slot[0] = __float_as_uint(sc);
-                    slot[RKEYS] = kv[v];
-                    cs[gb] += keep ? RROW : 0u;
-                    if ((v & 7) == 7) flush(gb);
+                for (int gb = 0; gb < 2; ++gb) {
+                    // byte offset of this stream's column in a ring row
+                    const uint32_t col = (uint32_t)(gb * SCAN_THREADS + stream0) * 8u;
+                    // rows' key bound relative to this lane's first key of the tile
+                    const int lim = vcount[gb] - (kt * SCAN_KEYS + 4 * half);
+#pragma unroll
+                    for (int v = 8 * hv; v < 8 * hv + 8; ++v) {
+                        const int vo = 8 * (v >> 2) + (v & 3);
+                        const float sc = acc[gb][v];
+                        bool keep = sc >= tau[gb];
+                        if constexpr (decltype(causal)::value) keep = keep && (vo < lim);
+                        uint2 *slot = (uint2 *)((unsigned char *)ringS + ((cs[gb] & ((RING - 1) * RROW)) | col));
+                        *slot = make_uint2(__float_as_uint(sc), kv[v]);
+                        cs[gb] += keep ? RROW : 0u;
+                    }
                 }
+                flush();
             }
         };
         if ((int64_t)(kt + 1) * SCAN_KEYS <= vfull) run(std::false_type{});
@@ -481,10 +497,9 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
 
     // the rest of each ring (fewer than FLUSH entries) one by one
     for (int gb = 0; gb < 2; ++gb) {
-        const uint32_t *rs = ringS + gb * SCAN_THREADS + stream0;
+        const uint2 *rs = ringS + gb * SCAN_THREADS + stream0;
         const uint32_t cnt = cs[gb] / RROW;
-        for (uint32_t e = fl[gb]; e < cnt; ++e)
-            *(uint2 *)(sb + soff0[gb] + e * 8u) = make_uint2(rs[(e % RING) * NSTREAM], rs[(e % RING) * NSTREAM + RKEYS]);
+        for (uint32_t e = fl[gb]; e < cnt; ++e) *(uint2 *)(sb + soff0[gb] + e * 8u) = rs[(e % RING) * NSTREAM];
         const int64_t j = j0 + 64 * w + 32 * gb + (l & 31);
         if (j < p.G) p.cnt[((int64_t)hl * p.G + j) * 2 + half] = (int)cnt;
     }
@@ -2547,7 +2562,9 @@ int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio,
     pl.cap_half = sm.cap_half;
     pl.keep_all_n = sm.keep_all_n;
     const int64_t vmax = (pl.n_max + s - 1) / s;
-    pl.samp_half = (int)((vmax + 1) / 2 + 8);
+    // a multiple of 8: every stream of the sample pass starts on a 64-byte
+    // chunk, as the scan's flush addresses streams in chunks
+    pl.samp_half = (int)(((vmax + 1) / 2 + 8 + 7) & ~(int64_t)7);
     pl.n_tiles = (int)((pl.G + SCAN_ROWS - 1) / SCAN_ROWS);
     const size_t rows = (size_t)pl.G;
     pl.b_P = dense ? 0 : align256(rows * D * pl.esz);
