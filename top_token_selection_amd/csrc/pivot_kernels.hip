@@ -55,8 +55,9 @@ namespace {
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 
-constexpr int SCAN_THREADS = 256;  // 4 wavefronts
-constexpr int SCAN_ROWS = 256;     // groups per scan block (64 per wave)
+constexpr int SCAN_THREADS = 512;  // 8 wavefronts
+constexpr int SCAN_GB = 1;         // 32-group column blocks per wavefront
+constexpr int SCAN_ROWS = SCAN_THREADS / 64 * 32 * SCAN_GB;  // groups per scan block
 constexpr int SCAN_KEYS = 32;      // keys per k-tile
 constexpr int RING = 16;           // staged survivors per (row, half) stream
 constexpr int FLUSH = 8;           // survivors written per flush (64 bytes)
@@ -188,11 +189,12 @@ struct ScanParams {
     int n_tiles, Hc;
 };
 
-// One block: 256 consecutive groups of one head against every key of their
-// prefixes, 32 keys per step. MFMA 32x32x16 with keys as the A operand (rows)
-// and proxies as B (columns): lane l holds column l%32 of each 32x32 tile,
-// i.e. one group, for 16 keys -- its threshold and running survivor count
-// stay in registers. Two blocks share a CU.
+// One block: SCAN_ROWS consecutive groups of one head against every key of
+// their prefixes, 32 keys per step; each wavefront takes SCAN_GB column
+// blocks of 32 groups. MFMA 32x32x16 with keys as the A operand (rows) and
+// proxies as B (columns): lane l holds column l%32 of each 32x32 tile, i.e.
+// one group, for 16 keys -- its threshold and running survivor count stay
+// in registers. Two blocks share a CU (four wavefronts per SIMD).
 //
 // Key tiles are loaded into registers two steps ahead (the keys of a head
 // are shared by the blocks of its groups, which are not in step: many loads
@@ -213,13 +215,16 @@ struct ScanParams {
 // 16 whole chunks of different streams. A stream that passes cap_half
 // survivors stops keeping (its row takes the exact fallback).
 template <typename T, int D>
-__global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
+__global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2 : 4) k_scan(ScanParams p) {
+    constexpr int GB = SCAN_GB;
     constexpr int RB = D * (int)sizeof(T);     // bytes per key row
     constexpr int NCK = RB / 16;               // 16-byte chunks per key row
     constexpr int SWZ = (NCK < 16 ? NCK : 16) - 1;
     constexpr int TILE = SCAN_KEYS * RB;       // bytes per LDS tile
-    constexpr int NLD = SCAN_KEYS * NCK / SCAN_THREADS;  // loads per thread per tile
-    constexpr int NSTREAM = 2 * SCAN_THREADS;  // (row, half) streams per block
+    constexpr int PIECES = SCAN_KEYS * NCK;    // 16-byte pieces per tile
+    constexpr int NLD = (PIECES + SCAN_THREADS - 1) / SCAN_THREADS;  // loads per thread per tile
+    constexpr int NSTREAM = 2 * SCAN_ROWS;     // (row, half) streams per block
+    static_assert(NSTREAM == GB * SCAN_THREADS, "one stream per lane and column block");
     extern __shared__ __align__(16) unsigned char smem[];
     // survivor rings (static LDS, so that addresses fold into offsets):
     // (score bits, key index) entries [RING][NSTREAM]; the key tiles are
@@ -253,8 +258,8 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     // takes the causal test)
     int64_t vfull = 0;
     {
-        const int64_t jw = j0 + 64 * w;
-        if (jw + 63 < p.G && prefix_len(jw, p.g) > p.min_n)
+        const int64_t jw = j0 + 32 * GB * w;
+        if (jw + 32 * GB - 1 < p.G && prefix_len(jw, p.g) > p.min_n)
             vfull = virt_count(prefix_len(jw, p.g), p.kstride, p.koff);
     }
     const float never = __builtin_nanf("");  // s >= NaN is false for every s
@@ -264,11 +269,13 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     // fl[gb] of them already written to the stream's buffer at byte offset
     // soff0[gb] from the block's part of the survivor array
     unsigned char *sb = (unsigned char *)p.out + ((int64_t)hl * p.G + j0) * 2 * (int64_t)p.stride * 8;
-    uint32_t soff0[2], cs[2] = {0u, 0u}, fl[2] = {0u, 0u};
-    int vcount[2];
-    float tau[2];
-    for (int gb = 0; gb < 2; ++gb) {
-        const int jl = 64 * w + 32 * gb + (l & 31);
+    uint32_t soff0[GB], cs[GB], fl[GB];
+    int vcount[GB];
+    float tau[GB];
+    for (int gb = 0; gb < GB; ++gb) {
+        cs[gb] = 0u;
+        fl[gb] = 0u;
+        const int jl = 32 * GB * w + 32 * gb + (l & 31);
         const int64_t j = j0 + jl;
         soff0[gb] = (uint32_t)((jl * 2 + half) * p.stride) * 8u;
         int64_t vc = 0;
@@ -285,10 +292,10 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     // proxies as resident B fragments
     typedef typename std::conditional<std::is_same<T, float>::value, f32x4_t, bf16x8_t>::type frag_t;
     constexpr int NKS = std::is_same<T, float>::value ? D / 8 : D / 16;
-    frag_t bq[2][NKS];
+    frag_t bq[GB][NKS];
     const T *Pb = (const T *)p.P + (int64_t)hl * p.p_head;
-    for (int gb = 0; gb < 2; ++gb) {
-        const int64_t j = j0 + 64 * w + 32 * gb + (l & 31);
+    for (int gb = 0; gb < GB; ++gb) {
+        const int64_t j = j0 + 32 * GB * w + 32 * gb + (l & 31);
         for (int ks = 0; ks < NKS; ++ks) {
             frag_t f;
             if (j < p.G) {
@@ -317,7 +324,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     auto load_tile = [&](int kt, piece_t &pr) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            const int q = (i * (SCAN_THREADS / 64) + w) * 64 + l;
+            const int q = min((i * (SCAN_THREADS / 64) + w) * 64 + l, PIECES - 1);
             const int r = q / NCK, c = q % NCK;
             const int64_t v = min((int64_t)kt * SCAN_KEYS + r, vmax - 1);
             const int64_t key = p.koff + (int64_t)p.kstride * v;
@@ -329,15 +336,18 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
         for (int i = 0; i < NLD; ++i) {
             const int q = (i * (SCAN_THREADS / 64) + w) * 64 + l;
             const int r = q / NCK, c = q % NCK;
-            *(u32x4_t *)(smem + (kt & 1) * TILE + (r * NCK + (c ^ (r & SWZ))) * 16) = pr[i];
+            // threads past the tile's pieces (a tile smaller than one
+            // piece per thread) store nothing
+            if (PIECES % SCAN_THREADS == 0 || q < PIECES)
+                *(u32x4_t *)(smem + (kt & 1) * TILE + (r * NCK + (c ^ (r & SWZ))) * 16) = pr[i];
         }
     };
 
-    typedef f32x16_t acc_t[2];
+    typedef f32x16_t acc_t[GB];
     auto matrix = [&](int kt, acc_t &acc) {
         const unsigned char *cur = smem + (kt & 1) * TILE;
-        acc[0] = f32x16_t{};
-        acc[1] = f32x16_t{};
+#pragma unroll
+        for (int gb = 0; gb < GB; ++gb) acc[gb] = f32x16_t{};
         const int r = l & 31;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -345,14 +355,14 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
             if constexpr (std::is_same<T, float>::value) {
                 const f32x4_t a = *(const f32x4_t *)ap;
 #pragma unroll
-                for (int gb = 0; gb < 2; ++gb)
+                for (int gb = 0; gb < GB; ++gb)
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
                         acc[gb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[v], bq[gb][ks][v], acc[gb], 0, 0, 0);
             } else {
                 const bf16x8_t a = *(const bf16x8_t *)ap;
 #pragma unroll
-                for (int gb = 0; gb < 2; ++gb)
+                for (int gb = 0; gb < GB; ++gb)
                     acc[gb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[gb][ks], acc[gb], 0, 0, 0);
             }
         }
@@ -371,32 +381,35 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     // Wavefront-uniform control flow.
     static_assert(RING % FLUSH == 0, "a chunk's ring rows do not wrap");
     auto flush = [&]() {
-        bool need[2];
-        uint64_t M[2];
-        uint32_t rank[2], pk[2];
-        int nf[2];
+        bool need[GB];
+        uint64_t M[GB];
+        uint32_t rank[GB], pk[GB];
+        int nf[GB];
+        uint64_t any = 0;
+        int nmax = 0;
 #pragma unroll
-        for (int gb = 0; gb < 2; ++gb) {
+        for (int gb = 0; gb < GB; ++gb) {
             need[gb] = cs[gb] / RROW - fl[gb] >= (uint32_t)FLUSH;
             M[gb] = __ballot(need[gb]);
             nf[gb] = __popcll(M[gb]);
             rank[gb] = __builtin_amdgcn_mbcnt_hi((uint32_t)(M[gb] >> 32),
                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)M[gb], 0u));
             pk[gb] = ((soff0[gb] / 64u + fl[gb] / 8u) << 10) | ((fl[gb] % RING) << 6) | (uint32_t)l;
+            any |= M[gb];
+            nmax = max(nmax, nf[gb]);
         }
-        if ((M[0] | M[1]) == 0) return;
-        const int nmax = max(nf[0], nf[1]);
+        if (any == 0) return;
         for (int r0 = 0; r0 < nmax; r0 += 16) {
-            uint32_t got[2];
+            uint32_t got[GB];
 #pragma unroll
-            for (int gb = 0; gb < 2; ++gb) {
+            for (int gb = 0; gb < GB; ++gb) {
                 // senders target lane 4 (rank - r0); the others an odd lane
                 const bool mine = need[gb] && rank[gb] - (uint32_t)r0 < 16u;
                 const int to = mine ? (int)(rank[gb] - (uint32_t)r0) * 16 : (l | 1) * 4;
                 got[gb] = dpp_u32<0x00>(0u, (uint32_t)__builtin_amdgcn_ds_permute(to, (int)pk[gb]));
             }
 #pragma unroll
-            for (int gb = 0; gb < 2; ++gb) {
+            for (int gb = 0; gb < GB; ++gb) {
                 if ((l >> 2) < nf[gb] - r0) {
                     const uint32_t q2 = 2u * (uint32_t)(l & 3);
                     const uint2 *e = ringS + (((got[gb] >> 6) & (RING - 1)) + q2) * NSTREAM + gb * SCAN_THREADS +
@@ -407,7 +420,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
             }
         }
 #pragma unroll
-        for (int gb = 0; gb < 2; ++gb) fl[gb] += need[gb] ? (uint32_t)FLUSH : 0u;
+        for (int gb = 0; gb < GB; ++gb) fl[gb] += need[gb] ? (uint32_t)FLUSH : 0u;
     };
 
     // keep the scores of tile kt that reach the row's threshold; at most 16
@@ -421,17 +434,14 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     // entries wait); only kept ones are counted.
     auto filter = [&](int kt, const acc_t &acc) {
 #pragma unroll
-        for (int gb = 0; gb < 2; ++gb)
+        for (int gb = 0; gb < GB; ++gb)
             if (cs[gb] > (uint32_t)p.cap_half * RROW) tau[gb] = never;
         const uint32_t tkey = kstr * (uint32_t)(kt * SCAN_KEYS) + lane_key;
-        uint32_t kv[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) kv[v] = tkey + kstr * (uint32_t)(8 * (v >> 2) + (v & 3));
         auto run = [&](auto causal) {
 #pragma unroll
             for (int hv = 0; hv < 2; ++hv) {
 #pragma unroll
-                for (int gb = 0; gb < 2; ++gb) {
+                for (int gb = 0; gb < GB; ++gb) {
                     // byte offset of this stream's column in a ring row
                     const uint32_t col = (uint32_t)(gb * SCAN_THREADS + stream0) * 8u;
                     // rows' key bound relative to this lane's first key of the tile
@@ -443,7 +453,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
                         bool keep = sc >= tau[gb];
                         if constexpr (decltype(causal)::value) keep = keep && (vo < lim);
                         uint2 *slot = (uint2 *)((unsigned char *)ringS + ((cs[gb] & ((RING - 1) * RROW)) | col));
-                        *slot = make_uint2(__float_as_uint(sc), kv[v]);
+                        *slot = make_uint2(__float_as_uint(sc), tkey + kstr * (uint32_t)vo);
                         cs[gb] += keep ? RROW : 0u;
                     }
                 }
@@ -496,11 +506,11 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) k_scan(ScanParams p) {
     }
 
     // the rest of each ring (fewer than FLUSH entries) one by one
-    for (int gb = 0; gb < 2; ++gb) {
+    for (int gb = 0; gb < GB; ++gb) {
         const uint2 *rs = ringS + gb * SCAN_THREADS + stream0;
         const uint32_t cnt = cs[gb] / RROW;
         for (uint32_t e = fl[gb]; e < cnt; ++e) *(uint2 *)(sb + soff0[gb] + e * 8u) = rs[(e % RING) * NSTREAM];
-        const int64_t j = j0 + 64 * w + 32 * gb + (l & 31);
+        const int64_t j = j0 + 32 * GB * w + 32 * gb + (l & 31);
         if (j < p.G) p.cnt[((int64_t)hl * p.G + j) * 2 + half] = (int)cnt;
     }
 }
