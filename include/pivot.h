@@ -49,7 +49,9 @@
  * optional stage-timing records below). Work is
  * enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
  * call returns once it is enqueued. Calls are reentrant for distinct
- * workspaces. The workspace is scratch device memory of at least the size
+ * workspaces, except while stage timing is enabled (pivot_profile_enable):
+ * the timing records are process-wide, so calls from several threads must
+ * then be serialised. The workspace is scratch device memory of at least the size
  * the matching *_workspace_bytes function returns; a smaller workspace that
  * still holds one head's share is used in several passes over the heads.
  *
