@@ -1764,7 +1764,18 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     uint32_t *cl = (uint32_t *)smem;                    // candidate list (Kc)
     unsigned char *regs = smem + ((p.Kc * 4 + 15) & ~15);
     const uint32_t *src = p.cand + grp * p.Kc;
-    for (int i = tid; i < nc; i += nthreads) cl[i] = src[i];
+    // eight loads a thread in flight before the first LDS store (a plain
+    // copy loop waits for each load in turn)
+    for (int i0 = tid; i0 < nc; i0 += 8 * nthreads) {
+        uint32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[min(i0 + u * nthreads, nc - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * nthreads;
+            if (i < nc) cl[i] = v[u];
+        }
+    }
 
     typedef typename std::conditional<std::is_same<T, float>::value, f32x4_t, bf16x8_t>::type frag_t;
     constexpr bool F32 = std::is_same<T, float>::value;
