@@ -1324,10 +1324,15 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
     // -- 2. fine buckets per coarse bin: n = the power of two nearest to
     //    0.9 * count * 2048 / nt (rounded down instead when that
     //    overshoots 2048 in all), at least 2^(sh1 - 20) so that a key's
-    //    bits inside its fine bucket fit LOWB bits, at most 2^sh1. Table
-    //    word = fine base | (sh1 - log2(n)) << 12 | (fine base + n - 1)
-    //    << 18, the last fine bucket of the bin (an empty bin at or above
-    //    b1: the running base | 1 << 17).
+    //    bits inside its fine bucket fit LOWB bits, at most 2^sh1. The
+    //    table has one 8-byte entry per bin at or above b1, r = bin - b1,
+    //    at index r + r / 16 (a lane writes 16 consecutive bins: the gap
+    //    spreads the lanes' stores over the banks): x = last fine bucket of
+    //    the bin + (r << log2(n)),
+    //    y = sub | fine base << 5, sub = sh1 - log2(n). A key k with
+    //    rel = k - kb (kb = the lower end of bin b1) then has its fine
+    //    bucket at x - (rel >> sub) and its bits inside it in the low sub
+    //    bits of rel (an empty bin: sub 0, the running base).
     const uint32_t lgmin = sh1 > LOWB ? (uint32_t)(sh1 - LOWB) : 0u;
     const float scl = (float)(REF_NB * 9 / 10) / (float)nt;
     for (int round_down = 0; round_down < 2; ++round_down) {
@@ -1352,53 +1357,68 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
         if (total > (uint32_t)REF_NB && !round_down) continue;
         uint32_t run = wave_incl_scan(loc) - loc;
         wave_lds_sync();
+        uint2 *tab = (uint2 *)h1;
+        static_assert(8 * (NC + NC / 16) <= 4 * (NC + 64 + REF_NB / 2 + 64), "the table ends before vars");
 #pragma unroll
         for (int i = CPL - 1; i >= 0; --i) {
             const uint32_t lg = lgs[i];
             const uint32_t bin = NC - CPL * (l + 1) + i;
             // empty bins at or above b1 take no bucket but keep the base
             // running, so bases never increase with the bin
-            mine[i] = lg != 0xFFu ? (run | (((uint32_t)sh1 - lg) << 12) | ((run + (1u << lg) - 1u) << 18))
-                                  : (bin >= b1 ? (run | (1u << 17)) : 0xFFFFFFFFu);
+            if (bin >= b1) {
+                const uint32_t r = bin - b1;
+                tab[r + (r >> 4)] = lg != 0xFFu
+                                        ? make_uint2(run + (1u << lg) - 1u + (r << lg), ((uint32_t)sh1 - lg) | (run << 5))
+                                        : make_uint2(0u, run << 5);
+            }
             if (lg != 0xFFu) run += 1u << lg;
         }
         if (l == 63) vars[2] = run;  // fine buckets in use
         break;
     }
     wave_lds_sync();
+    const uint32_t kb = klo + (b1 << sh1);  // lower end of bin b1
+    const uint2 *tab = (const uint2 *)h1;
     // a packed word's coarse bin is the lowest bin at or above b1 whose
     // table base is <= its fine bucket (bases fall as bins rise)
     auto unpack = [&](uint32_t w) -> uint32_t {
         if (w == 0xFFFFFFFFu) return 0u;
         const uint32_t fb = w >> 20;
-        uint32_t lo = b1, hi = NC - 1;
+        uint32_t lo = 0, hi = NC - 1 - b1;
         while (lo < hi) {
             const uint32_t mid = (lo + hi) >> 1;
-            if ((h1[mid] & 0xFFFu) <= fb) hi = mid;
+            if ((tab[mid + (mid >> 4)].y >> 5) <= fb) hi = mid;
             else lo = mid + 1;
         }
-        const uint32_t t = h1[lo];
-        const uint32_t sub = (t >> 12) & 31u;
+        const uint32_t t = tab[lo + (lo >> 4)].y;
+        const uint32_t sub = t & 31u;
         const uint32_t lg = (uint32_t)sh1 - sub;
-        const uint32_t top = (1u << lg) - 1u - (fb - (t & 0xFFFu));
+        const uint32_t top = (1u << lg) - 1u - (fb - (t >> 5));
         const uint32_t low = (top << sub) | (w & ((1u << sub) - 1u));
-        return klo + (lo << sh1) + low;
+        return kb + (lo << sh1) + low;
     };
-    if (vars[2] <= (uint32_t)REF_NB) {
+    // the 32-bit fine counters (and 64 trash counters) take the staging
+    // area, free until the scatter
+    if (vars[2] <= (uint32_t)REF_NB && cap >= (uint32_t)REF_NB) {
         // packed word of a key: fine bucket << 20 | its bits inside the
         // fine bucket (0 = best bucket); 0xFFFFFFFF when not wanted
         // (below the range, below b1, or an empty slot). f = the counter
         // the key goes to: its fine bucket, or the lane's trash counter.
-        const uint32_t trash_f = (uint32_t)(REF_NB + 2 * l);
-        auto packed = [&](uint32_t k, uint32_t &f) -> uint32_t {
-            const uint32_t rel = k - klo;
-            const uint32_t bin = rel >> sh1;
-            const uint32_t t = h1[min(bin, (uint32_t)(NC - 1))];
-            const uint32_t sub = (t >> 12) & 31u;
-            const uint32_t low = rel & ((1u << sh1) - 1u);
-            const uint32_t fb = (t >> 18) - (low >> sub);
-            const uint32_t w = (fb << 20) | (low & ((1u << sub) - 1u));
-            const bool ok = k >= klo && bin >= b1;
+        const uint32_t trash_f = (uint32_t)(REF_NB + l);
+        // every wanted key has kb <= k <= mx: one unsigned compare of
+        // k - kb (keys below kb wrap past mx - kb)
+        const uint32_t span = mx - kb;
+        const uint32_t rmax = (uint32_t)(NC - 1) - b1;
+        uint32_t *fc = buf;
+        for (int i = l; i < (REF_NB + 64) / 4; i += 64) ((uint4 *)fc)[i] = make_uint4(0u, 0u, 0u, 0u);
+        wave_lds_sync();
+        // packed word of a key from rel = k - kb and its table entry t
+        auto packed = [&](uint32_t rel, uint2 t, uint32_t &f) -> uint32_t {
+            // sub = the low 5 bits of t.y, which is all the shift and the
+            // bit-field extract read of it
+            const uint32_t fb = t.x - (rel >> (t.y & 31u));
+            const uint32_t w = (fb << 20) | __builtin_amdgcn_ubfe(rel, 0u, t.y);
+            const bool ok = rel <= span;
             f = ok ? fb : trash_f;
             return ok ? w : 0xFFFFFFFFu;
         };
@@ -1407,51 +1427,71 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
         //    register holds its packed word (every slot, so empty ones
         //    read as "not wanted" in all passes); unpack() gives the key
         //    back to the general path.
+        //    Eight keys at a time: their eight table reads are issued
+        //    before any of them is used, so that the batch waits for one
+        //    LDS round trip, not eight.
+        static_assert(E % 8 == 0, "keys go in batches of eight");
 #pragma unroll
-        for (int e = 0; e < E / 4; ++e) {
-            if (e < e4) {
+        for (int e0 = 0; e0 < E / 4; e0 += 2) {
+            if (e0 < e4) {
+                uint32_t rel[8];
+                uint2 t[8];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    uint32_t f;
-                    key[4 * e + v] = packed(key[4 * e + v], f);
-                    atomicAdd(&h2[f >> 1], 1u << ((f & 1u) << 4));
+                for (int i = 0; i < 8; ++i) rel[i] = key[4 * e0 + i] - kb;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t r = min(rel[i] >> sh1, rmax);
+                    t[i] = tab[r + (r >> 4)];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    if (e0 + i / 4 < e4) {
+                        uint32_t f;
+                        key[4 * e0 + i] = packed(rel[i], t[i], f);
+                        atomicAdd(&fc[f], 1u);
+                    } else {
+                        key[4 * e0 + i] = 0xFFFFFFFFu;
+                    }
                 }
             } else {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) key[4 * e + v] = 0xFFFFFFFFu;
+                for (int i = 0; i < 8; ++i) key[4 * e0 + i] = 0xFFFFFFFFu;
             }
             __builtin_amdgcn_sched_barrier(0);  // bound the loads in flight
         }
         wave_lds_sync();
+        // lane l: fine buckets 32 l .. 32 l + 31; their output offsets,
+        // two 16-bit ones a word, stay in registers until the scatter
+        // path is taken (they go to h2, over the table)
+        constexpr int OW = REF_NB / 128;
+        uint32_t ow[OW];
         {
-            uint32_t *fw = h2 + (REF_NB / 128) * l;  // lane l: fine buckets 32 l .. 32 l + 31
+            const uint4 *fw = (const uint4 *)(fc + (REF_NB / 64) * l);
+            uint32_t cnt[REF_NB / 64];
             uint32_t loc = 0;
             cmax = 0u;
 #pragma unroll
-            for (int i = 0; i < REF_NB / 512; ++i) {
-                const uint4 c4 = *(const uint4 *)(fw + 4 * i);
-                loc += (c4.x & 0xFFFFu) + (c4.x >> 16) + (c4.y & 0xFFFFu) + (c4.y >> 16) +
-                       (c4.z & 0xFFFFu) + (c4.z >> 16) + (c4.w & 0xFFFFu) + (c4.w >> 16);
+            for (int i = 0; i < REF_NB / 256; ++i) {
+                const uint4 c4 = fw[i];
+                cnt[4 * i + 0] = c4.x;
+                cnt[4 * i + 1] = c4.y;
+                cnt[4 * i + 2] = c4.z;
+                cnt[4 * i + 3] = c4.w;
+                loc += c4.x + c4.y + c4.z + c4.w;
             }
             uint32_t run = wave_incl_scan(loc) - loc;
 #pragma unroll
-            for (int i = 0; i < REF_NB / 512; ++i) {
-                const uint4 c4 = *(const uint4 *)(fw + 4 * i);
-                const uint32_t w4[4] = {c4.x, c4.y, c4.z, c4.w};
-                uint32_t o4[4];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const uint32_t c = (w4[t >> 1] >> ((t & 1) << 4)) & 0xFFFFu;
-                    if (run < msel) cmax = max(cmax, c);  // buckets 0 .. fstar only
-                    if (t & 1) o4[t >> 1] |= run << 16;
-                    else o4[t >> 1] = run;
-                    if (run < msel && msel <= run + c) {
-                        vars[3] = (uint32_t)(32 * l + 8 * i + t);
-                        vars[4] = run + c;
-                    }
-                    run += c;
+            for (int t = 0; t < REF_NB / 64; ++t) {
+                const uint32_t c = cnt[t];
+                if (run < msel) cmax = max(cmax, c);  // buckets 0 .. fstar only
+                if (t & 1) ow[t >> 1] |= run << 16;
+                else ow[t >> 1] = run;
+                if (run < msel && msel <= run + c) {
+                    vars[3] = (uint32_t)((REF_NB / 64) * l + t);
+                    vars[4] = run + c;
                 }
-                *(uint4 *)(fw + 4 * i) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+                run += c;
             }
         }
         wave_lds_sync();
@@ -1466,6 +1506,9 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
         constexpr int NSL = 36;                                     // staged slots per lane
         static_assert(NSL % 4 == 0 && 64 * NSL >= (int)TAGS, "every staged slot has a lane");
         if (nsc <= cap && nsc <= TAGS && msel <= STG && cap + 64u >= 64u * (uint32_t)NSL) {
+#pragma unroll
+            for (int i = 0; i < OW / 4; ++i)
+                *(uint4 *)(h2 + OW * l + 4 * i) = make_uint4(ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]);
             wave_lds_sync();
             uint16_t *tag = (uint16_t *)h1;
             const uint32_t trashf = (uint32_t)(REF_NB + 2 * l);
