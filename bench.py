@@ -189,7 +189,7 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip timing the other workloads (tiny, S=16384 integer, S=131072 long)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
-    ap.add_argument("--recall-rows", type=int, default=256)
+    ap.add_argument("--recall-rows", type=int, default=4096)
     ap.add_argument("--long", action="store_true", help="S=131072, H=32, g=16 instead")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: recall@top_k against the dense indexer and time per call "
@@ -313,22 +313,38 @@ def main():
         qh = syn.bf16_tensor_to_bits(q)
         kh = syn.bf16_tensor_to_bits(k)
     if args.recall_rows > 0:
-        import oracle
-        log(f"dense oracle on {args.recall_rows} sampled rows")
+        from oracle.pool import OraclePool
+        # the dense oracle's rows, and the group-prefix dense rows (the
+        # query's own top_k over its group's prefix [0, n_j), which leaves
+        # out the keys of [g_start, i): the oracle's Refine with a candidate
+        # set covering every prefix), in single-threaded processes over the
+        # host's cores
         t0 = time.perf_counter()
-        dense_rows, _ = oracle.dense_rows(qh, kh, ri, rh, top_k)
+        with OraclePool(need_bytes=qh.nbytes + kh.nbytes) as pool:
+            log(f"dense and group-prefix dense oracle on {args.recall_rows} sampled rows "
+                f"({pool.workers} processes)")
+            qr, kr = pool.put(qh), pool.put(kh)
+            chunks = [c for c in np.array_split(np.arange(len(ri)), 4 * pool.workers) if len(c)]
+            tasks = [("dense_rows", dict(q=qr, k=kr, rows_i=ri[c], rows_h=rh[c], top_k=top_k)) for c in chunks]
+            tasks += [("prefill_rows", dict(q=qr, k=kr, rows_i=ri[c], rows_h=rh[c], top_k=top_k, g=g,
+                                            candidate_ratio=S / top_k, mode="refine")) for c in chunks]
+            res = pool.map(tasks)
+        dense_rows = np.concatenate([r[0] for r in res[:len(chunks)]])
+        gp_rows = np.concatenate([r[0] for r in res[len(chunks):]])
         dense_s = time.perf_counter() - t0
         pv.index_prefill(q, k, top_k, g, ratio, "reuse", workspace=ws, out=out)
         reu_rows = out[ri_d, rh_d].cpu().numpy()
 
-        def rec(rows):
+        def rec(rows, ref):
             vals = []
-            for a, b in zip(rows, dense_rows):
+            for a, b in zip(rows, ref):
                 bs = set(b[b >= 0].tolist())
                 vals.append(len(set(a[a >= 0].tolist()) & bs) / len(bs))
             return float(np.mean(vals))
-        recall = {"refine": rec(ref_rows), "reuse": rec(reu_rows), "rows": int(args.recall_rows),
-                  "sample": "positions uniform in [g, S), heads uniform, seed 7", "oracle_s": dense_s}
+        recall = {"refine": rec(ref_rows, dense_rows), "reuse": rec(reu_rows, dense_rows),
+                  "rows": int(args.recall_rows),
+                  "sample": "positions uniform in [g, S), heads uniform, seed 7", "oracle_s": dense_s,
+                  "vs_group_prefix_dense": {"refine": rec(ref_rows, gp_rows), "reuse": rec(reu_rows, gp_rows)}}
         log(f"recall@{top_k}: {recall}")
 
     # ------------------------------------ downstream sparse attention
@@ -526,34 +542,50 @@ def main():
         lc = syn.long_prefill_device(dev, S=131072, H=32, g=16, seed=1004)
         lres = prefill_config("long S=131072 H=32 g=16", lc["q"], lc["k"], 2048, 16, ("refine", "reuse"),
                               False, max(2, args.steps // 2))
-        # recall@2048 on a 4096-row sample against the dense indexer (GPU;
-        # bit-exact to the oracle on integer inputs, tie-tolerant on these)
+        # recall@2048 on a 4096-row sample against the dense oracle and the
+        # group-prefix dense oracle rows (single-threaded processes over the
+        # host's cores)
         if args.recall_rows > 0:
-            Sl, Hl = 131072, 32
+            from oracle.pool import OraclePool
+            Sl, Hl, gl = 131072, 32, 16
             rng = np.random.default_rng(13)
-            li = torch.from_numpy(rng.integers(16, Sl, 4096)).to(dev)
-            lh = torch.from_numpy(rng.integers(0, Hl, 4096)).to(dev)
-            lws = torch.empty(pv.prefill_workspace_bytes(Sl, Hl, 128, 2048, 16, 2.0, "refine", torch.bfloat16),
+            li_h = rng.integers(16, Sl, 4096)
+            lh_h = rng.integers(0, Hl, 4096).astype(np.int32)
+            li, lh = torch.from_numpy(li_h).to(dev), torch.from_numpy(lh_h.astype(np.int64)).to(dev)
+            lws = torch.empty(pv.prefill_workspace_bytes(Sl, Hl, 128, 2048, gl, 2.0, "refine", torch.bfloat16),
                               dtype=torch.uint8, device=dev)
             lout = torch.empty((Sl, Hl, 2048), dtype=torch.int32, device=dev)
             rows = {}
             for mode in ("refine", "reuse"):
-                pv.index_prefill(lc["q"], lc["k"], 2048, 16, 2.0, mode, workspace=lws, out=lout)
+                pv.index_prefill(lc["q"], lc["k"], 2048, gl, 2.0, mode, workspace=lws, out=lout)
                 rows[mode] = lout[li, lh].cpu().numpy()
-            del lws
-            pv.dense_index(lc["q"], lc["k"], 2048, out=lout, max_workspace_bytes=48 << 30)
-            drows = lout[li, lh].cpu().numpy()
-            del lout
+            del lws, lout
+            lqh, lkh = syn.bf16_tensor_to_bits(lc["q"]), syn.bf16_tensor_to_bits(lc["k"])
+            t0 = time.perf_counter()
+            with OraclePool(need_bytes=lqh.nbytes + lkh.nbytes) as pool:
+                qr, kr = pool.put(lqh), pool.put(lkh)
+                chunks = [c for c in np.array_split(np.arange(4096), 4 * pool.workers) if len(c)]
+                tasks = [("dense_rows", dict(q=qr, k=kr, rows_i=li_h[c], rows_h=lh_h[c], top_k=2048))
+                         for c in chunks]
+                tasks += [("prefill_rows", dict(q=qr, k=kr, rows_i=li_h[c], rows_h=lh_h[c], top_k=2048, g=gl,
+                                                candidate_ratio=Sl / 2048, mode="refine")) for c in chunks]
+                res = pool.map(tasks)
+            del lqh, lkh
+            drows = np.concatenate([r[0] for r in res[:len(chunks)]])
+            gprows = np.concatenate([r[0] for r in res[len(chunks):]])
 
-            def rec2(a_rows):
+            def rec2(a_rows, ref):
                 vals = []
-                for a, b in zip(a_rows, drows):
+                for a, b in zip(a_rows, ref):
                     bs = set(b[b >= 0].tolist())
                     vals.append(len(set(a[a >= 0].tolist()) & bs) / len(bs))
                 return float(np.mean(vals))
-            lres["recall"] = {"refine": rec2(rows["refine"]), "reuse": rec2(rows["reuse"]), "rows": 4096,
-                              "against": "dense indexer (GPU)",
-                              "sample": "positions uniform in [16, S), heads uniform, seed 13"}
+            lres["recall"] = {"refine": rec2(rows["refine"], drows), "reuse": rec2(rows["reuse"], drows),
+                              "rows": 4096, "against": "dense oracle",
+                              "sample": "positions uniform in [16, S), heads uniform, seed 13",
+                              "oracle_s": time.perf_counter() - t0,
+                              "vs_group_prefix_dense": {"refine": rec2(rows["refine"], gprows),
+                                                        "reuse": rec2(rows["reuse"], gprows)}}
             log(f"long recall@2048: {lres['recall']}")
         configs["long131k"] = lres
         del lc
