@@ -1200,15 +1200,15 @@ struct RefParams {
 //    count (2048 fine buckets in all, numbered from the best down), so a
 //    fine bucket holds one or two keys on average whatever the shape of
 //    the score distribution.
-// 3. A fine histogram (16-bit counters, two per word); its scan finds
-//    the fine bucket holding the msel-th key and gives every fine bucket
-//    its output offset.
+// 3. A fine histogram (32-bit counters in the staging area, free until
+//    the scatter); its scan finds the fine bucket holding the msel-th key
+//    and gives every fine bucket its output offset (16-bit, two a word).
 // 4. Fine buckets up to that one are scattered as packed words (key bits
 //    inside the bucket, position), tagged with their bucket.
 // 5. Each lane takes a run of consecutive staged slots and ranks every
 //    entry against its bucket companions (score desc, index asc).
-// Out-of-range keys use per-lane trash bins / slots: no branches, no
-// single hot address.
+// Out-of-range keys go to per-lane trash bins / slots: no branches, no
+// single hot address (masking them off the LDS atomics measured slower).
 // `my` is the wavefront's LDS region (REF_HDR bytes of header, then cap + 64
 // staged words); positions take POSB bits of a staged word, key bits inside
 // a fine bucket the other LOWB.
