@@ -1282,8 +1282,8 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
     for (int att = 0; att < 2; ++att) {
         const int bw1 = bit_width(mx - klo);
         sh1 = bw1 > REF_LOG2C ? bw1 - REF_LOG2C : 0;
-        for (int i = l; i < (NC + 64 + REF_NB / 2 + 64) / 4; i += 64)
-            ((uint4 *)h1)[i] = make_uint4(0u, 0u, 0u, 0u);
+        // the coarse counts and trash bins (h2 is written before it is read)
+        for (int i = l; i < (NC + 64) / 4; i += 64) ((uint4 *)h1)[i] = make_uint4(0u, 0u, 0u, 0u);
         if (l == 0) vars[0] = 0xFFFFFFFFu;
         wave_lds_sync();
 #pragma unroll
