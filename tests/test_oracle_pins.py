@@ -196,6 +196,48 @@ def test_refine_rows_are_subsets_of_candidates():
             assert set(r[r >= 0].tolist()) <= cs
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_candidates_match_exact_bruteforce(dtype):
+    """C_j (in total order, with proxy scores) of every group equals the
+    exact top-K of the exactly rounded proxy over the prefix [0, max(j g, 1)),
+    ragged last group included ("How It Works": candidate set of size K)."""
+    S, H, D, top_k, g, ratio = 27, 2, 4, 3, 4, 2.0
+    q = syn.integers((S, H, D), 71, 3, dtype)
+    k = syn.integers((S, H, D), 72, 3, dtype)
+    K = oracle.candidate_count(top_k, ratio)
+    qv, kv = exact_ref.values(q), exact_ref.values(k)
+    for h in range(H):
+        for j in range((S + g - 1) // g):
+            i0 = j * g
+            m = min(g, S - i0)
+            p = exact_ref.proxy_exact(qv, i0, m, h, dtype == "bf16")
+            want = exact_ref.topk_exact([(exact_ref.dot_f32(p, kv, c, h), c) for c in range(max(i0, 1))], K)
+            cand, sc = oracle.prefill_candidates(q, k, h, j, top_k, g, ratio)
+            assert cand.tolist() == [c for _, c in want], (h, j)
+            assert sc.astype(np.float64).tolist() == [s for s, _ in want], (h, j)
+
+
+def test_decode_candidates_equal_last_prefill_group():
+    """The decode candidate set of sequence b equals that of group L / g of
+    a prefill of length L + g whose last g queries are the MTP queries."""
+    g, H, D, top_k = 4, 2, 16, 6
+    ctx = np.array([40, 8, 64], np.int64)
+    B = len(ctx)
+    kc = syn.gaussian((int(ctx.sum()), H, D), 131, "bf16")
+    qd = syn.gaussian((B * g, H, D), 132, "bf16")
+    off = 0
+    for b in range(B):
+        L = int(ctx[b])
+        keys = np.concatenate([kc[off:off + L], syn.gaussian((g, H, D), 133 + b, "bf16")])
+        qs = np.concatenate([syn.gaussian((L, H, D), 134 + b, "bf16"), qd[b * g:(b + 1) * g]])
+        for h in range(H):
+            dc, ds = oracle.decode_candidates(qd, kc, ctx, g, h, b, top_k, 2.0)
+            pc, ps = oracle.prefill_candidates(qs, keys, h, L // g, top_k, g, 2.0)
+            np.testing.assert_array_equal(dc, pc)
+            np.testing.assert_array_equal(ds, ps)
+        off += L
+
+
 # -------------------------------------------------------- special cases
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
