@@ -1217,7 +1217,7 @@ struct RefParams {
 // went through put(rank, index) (ranks >= msel are not passed) and then
 // emit(nullptr). Returns false when the general path must run; key[] then
 // hold the keys again.
-template <int E, int POSB, class IDX, class PUT, class EMIT>
+template <int E, int POSB, bool SMALLW, class IDX, class PUT, class EMIT>
 __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, const int nc, const uint32_t msel,
                                              const uint32_t smp, unsigned char *my, const uint32_t cap, IDX idx_of,
                                              PUT put, EMIT emit) {
@@ -1542,19 +1542,26 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
             wave_lds_sync();
             // -- 5. rank inside the bucket. Slots run in bucket order, so
             //    ordering every bucket puts the row in place. Lane l
-            //    holds the staged slots [NSL l, NSL (l + 1)) and X more
-            //    on either side as 64-bit words (bucket + 1) << 52 |
+            //    holds the staged slots [W l, W (l + 1)) and X more on
+            //    either side as 64-bit words (bucket + 1) << 52 |
             //    (inverted key bits in the bucket) << 32 | key index and
             //    runs odd-even transposition rounds until none swaps:
             //    the words of a bucket then stand in final order (score
             //    desc, index asc), and every bucket that touches the
             //    lane's own slots is whole in its window unless it
-            //    reaches past an edge of the window. In that rare case
-            //    every entry is ranked by a counted loop over its bucket
-            //    instead and stored straight to the output row.
-            constexpr int X = 8;
-            constexpr int NW = NSL + 2 * X;
-            const uint32_t s0 = (uint32_t)(NSL * l);
+            //    reaches past an edge of the window. In that case every
+            //    entry is ranked by a counted loop over its bucket
+            //    instead and stored straight to the output row. Lists of
+            //    at most 1024 keys (SMALLW) take W = 16, X = 16: their
+            //    buckets of equal keys (integer-valued scores) run long,
+            //    and the wider margins keep them inside the window; the
+            //    others take W = NSL, X = 8.
+            constexpr int W = SMALLW ? 16 : NSL;
+            constexpr int X = SMALLW ? 16 : 8;
+            // lane 1's left margin starts at slot 0 or later
+            static_assert(W % 4 == 0 && X % 4 == 0 && X <= W, "margins in whole 16-byte pieces");
+            constexpr int NW = W + 2 * X;
+            const uint32_t s0 = (uint32_t)(W * l);
             const bool own = s0 < nsc;
             // window entries below lim hold slots before nsc
             const int lim = own ? (int)(nsc - s0) + X : 0;
@@ -1563,7 +1570,7 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
                 const uint4 *bp = (const uint4 *)(buf + s0);
                 const uint2 *tp = (const uint2 *)(tag + s0);
 #pragma unroll
-                for (int i = -X / 4; i < NSL / 4 + X / 4; ++i) {
+                for (int i = -X / 4; i < W / 4 + X / 4; ++i) {
                     uint4 x = make_uint4(0u, 0u, 0u, 0u);
                     uint2 y = make_uint2(0u, 0u);
                     if (own && (i >= 0 || l > 0)) {
@@ -1586,10 +1593,12 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
             }
             // a bucket reaching from an own slot past the window
             const uint32_t tl = (uint32_t)(A[0] >> (32 + LOWB)), tf = (uint32_t)(A[X] >> (32 + LOWB));
-            const uint32_t tb = (uint32_t)(A[X + NSL - 1] >> (32 + LOWB));
+            const uint32_t tb = (uint32_t)(A[X + W - 1] >> (32 + LOWB));
             const uint32_t tr = (uint32_t)(A[NW - 1] >> (32 + LOWB));
             const bool edge = own && ((tl != 0u && tl == tf) || (tb <= (uint32_t)REF_NB && tb == tr));
-            if (__ballot(edge) == 0ull) {
+            // every staged slot has a lane (always so with SMALLW: nc <= 1024)
+            const bool covered = !SMALLW || nsc <= 64u * (uint32_t)W;
+            if (covered && __ballot(edge) == 0ull) {
                 // entries only move inside their bucket, and odd-even
                 // transposition orders m entries in m phases: ceil(bmax / 2)
                 // rounds of both parities order every bucket (no test
@@ -1612,7 +1621,7 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
                 //    run: slots past nsc are never read), then out with
                 //    whole-line stores
 #pragma unroll
-                for (int t = 0; t < NSL; t += 4)
+                for (int t = 0; t < W; t += 4)
                     *(uint4 *)(buf + s0 + t) = make_uint4((uint32_t)A[X + t], (uint32_t)A[X + t + 1],
                                                           (uint32_t)A[X + t + 2], (uint32_t)A[X + t + 3]);
                 wave_lds_sync();
@@ -1736,7 +1745,7 @@ __global__ void __launch_bounds__(64 * SW_WAVES) k_select_wave(SelParams p) {
     const int m = (int)min((int64_t)p.g, p.o.S - i0);
     const int64_t rstride = (int64_t)p.o.H * p.o.top_k;
     int32_t *dst0 = p.o.out_idx + (i0 * p.o.H + p.o.h0 + hl) * (int64_t)p.o.top_k;
-    const bool done = fused_select<SW_E, 13>(
+    const bool done = fused_select<SW_E, 13, false>(
         key, e4, ns, msel, smp, smem + w * SW_REG, (uint32_t)SW_CAP, idx_of,
         [&](uint32_t fin, uint32_t idx) {
             for (int t = 0; t < m; ++t) dst0[t * rstride + fin] = (int32_t)idx;
@@ -1765,7 +1774,7 @@ __global__ void __launch_bounds__(64 * SW_WAVES) k_select_wave(SelParams p) {
 // the MFMA layout in registers (bf16 blocks of several queries); otherwise
 // the loads take the MFMA layout directly. GOUT: the scores go to global
 // rows (p.gsc) and the kernel ends after the gather.
-template <typename T, int D, bool LINES, bool GOUT>
+template <typename T, int D, bool LINES, bool GOUT, bool SMALLW>
 __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int nblk = (int)(p.NG * p.Hc) * p.nqb;
@@ -1985,7 +1994,7 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
     const int64_t obase = ((qrow0 + q0 + w) * p.H + h) * (int64_t)p.top_k;
 
     if (!p.out_score &&
-        fused_select<REF_E, 12>(
+        fused_select<REF_E, 12, SMALLW>(
             key, e4, nc, msel, smp, my, (uint32_t)p.ref_cap, [&](uint32_t pos) { return cl[pos]; },
             [&](uint32_t fin, uint32_t idx) { p.out_idx[obase + fin] = (int32_t)idx; },
             [&](const uint32_t *row) {
@@ -2705,15 +2714,15 @@ RefLayout refine_layout(int64_t K, int top_k, int g) {
     return L;
 }
 
-template <typename T, int D, bool GOUT>
+template <typename T, int D, bool GOUT, bool SMALLW = false>
 int launch_refine(const RefParams &rp, int nblocks, size_t lds, hipStream_t st) {
     if (sizeof(T) == 2 && rp.nqw > 1) {
         constexpr bool LINES = sizeof(T) == 2;
-        HIP_TRY(set_lds((const void *)k_refine<T, D, LINES, GOUT>, lds));
-        hipLaunchKernelGGL((k_refine<T, D, LINES, GOUT>), dim3(nblocks), dim3(64 * rp.nqw), lds, st, rp);
+        HIP_TRY(set_lds((const void *)k_refine<T, D, LINES, GOUT, SMALLW>, lds));
+        hipLaunchKernelGGL((k_refine<T, D, LINES, GOUT, SMALLW>), dim3(nblocks), dim3(64 * rp.nqw), lds, st, rp);
     } else {
-        HIP_TRY(set_lds((const void *)k_refine<T, D, false, GOUT>, lds));
-        hipLaunchKernelGGL((k_refine<T, D, false, GOUT>), dim3(nblocks), dim3(64 * rp.nqw), lds, st, rp);
+        HIP_TRY(set_lds((const void *)k_refine<T, D, false, GOUT, SMALLW>, lds));
+        hipLaunchKernelGGL((k_refine<T, D, false, GOUT, SMALLW>), dim3(nblocks), dim3(64 * rp.nqw), lds, st, rp);
     }
     HIP_TRY(hipGetLastError());
     return PIVOT_OK;
@@ -2732,6 +2741,11 @@ int dispatch_refine(int D, RefParams rp, int64_t groups, int top_k, hipStream_t 
         rp.reg_bytes = lay.reg_bytes;
         rp.ref_cap = lay.cap;
         const int nblocks = (int)(groups * rp.nqb);
+        // lists of at most 1024 keys: the select's ranking window for
+        // long runs of equal keys
+        if (rp.Kc <= 1024)
+            return D == 64 ? launch_refine<T, 64, false, true>(rp, nblocks, lay.lds, st)
+                           : launch_refine<T, 128, false, true>(rp, nblocks, lay.lds, st);
         return D == 64 ? launch_refine<T, 64, false>(rp, nblocks, lay.lds, st)
                        : launch_refine<T, 128, false>(rp, nblocks, lay.lds, st);
     }
