@@ -1426,11 +1426,35 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
         // -- 3. fine histogram, crossing, offsets. From here on each key
         //    register holds its packed word (every slot, so empty ones
         //    read as "not wanted" in all passes); unpack() gives the key
-        //    back to the general path.
+        //    back to the general path. With SLOTS, the counter's old value
+        //    is the key's slot inside its fine bucket: sub[k / 4] keeps it,
+        //    four 8-bit ones a word, for the scatter (rows whose staged
+        //    buckets reach 256 keys take the general path); without, the
+        //    scatter claims slots with atomics of its own (96 keys a lane
+        //    leave no registers for the slots; lists of at most 1024 keys
+        //    measured faster with the claims).
         //    Eight keys at a time: their eight table reads are issued
         //    before any of them is used, so that the batch waits for one
-        //    LDS round trip, not eight.
+        //    LDS round trip, not eight; a batch's slots are taken into sub
+        //    after the next batch's table reads have returned (LDS
+        //    operations of a wavefront complete in order), so that they
+        //    cost no wait of their own.
         static_assert(E % 8 == 0, "keys go in batches of eight");
+        constexpr bool SLOTS = E <= 64 && !SMALLW;
+        uint32_t sub[SLOTS ? E / 4 : 1];
+        uint32_t got[8] = {};
+        // the low bytes of four counts (a count of a bucket that is not
+        // staged may pass 255: only its own byte may hold garbage)
+        auto keep_slots = [&](int b) {
+            if constexpr (SLOTS) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const uint32_t lo = __builtin_amdgcn_perm(got[4 * i + 1], got[4 * i], 0x0c0c0400u);
+                    const uint32_t hi = __builtin_amdgcn_perm(got[4 * i + 3], got[4 * i + 2], 0x0c0c0400u);
+                    sub[2 * b + i] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                }
+            }
+        };
 #pragma unroll
         for (int e0 = 0; e0 < E / 4; e0 += 2) {
             if (e0 < e4) {
@@ -1444,22 +1468,26 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
                     t[i] = tab[r + (r >> 4)];
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                if (e0 >= 2) keep_slots(e0 / 2 - 1);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     if (e0 + i / 4 < e4) {
                         uint32_t f;
                         key[4 * e0 + i] = packed(rel[i], t[i], f);
-                        atomicAdd(&fc[f], 1u);
+                        if constexpr (SLOTS) got[i] = atomicAdd(&fc[f], 1u);
+                        else atomicAdd(&fc[f], 1u);
                     } else {
                         key[4 * e0 + i] = 0xFFFFFFFFu;
                     }
                 }
             } else {
+                if (e0 >= 2) keep_slots(e0 / 2 - 1);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) key[4 * e0 + i] = 0xFFFFFFFFu;
             }
             __builtin_amdgcn_sched_barrier(0);  // bound the loads in flight
         }
+        keep_slots(E / 8 - 1);
         wave_lds_sync();
         // lane l: fine buckets 32 l .. 32 l + 31; their output offsets,
         // two 16-bit ones a word, stay in registers until the scatter
@@ -1499,46 +1527,73 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
         const uint32_t nsc = vars[4];
         const uint32_t bmax = wave_max(cmax);  // the largest staged bucket
         // h1 (the table, dead once every key is packed) then holds a 16-bit
-        // bucket tag per staged entry; h1..h2 (dead once every rank is
-        // known) then hold the finished row.
+        // bucket tag per staged entry; h2 the buckets' 16-bit start
+        // offsets.
         constexpr uint32_t STG = (uint32_t)(NC + 64 + REF_NB / 2 + 64);
         constexpr uint32_t TAGS = 2u * (uint32_t)(NC + 64) - 64u;  // + 64 trash tags
         constexpr int NSL = 36;                                     // staged slots per lane
         static_assert(NSL % 4 == 0 && 64 * NSL >= (int)TAGS, "every staged slot has a lane");
-        if (nsc <= cap && nsc <= TAGS && msel <= STG && cap + 64u >= 64u * (uint32_t)NSL) {
+        if (nsc <= cap && nsc <= TAGS && msel <= STG && cap + 64u >= 64u * (uint32_t)NSL && (!SLOTS || bmax <= 255u)) {
 #pragma unroll
             for (int i = 0; i < OW / 4; ++i)
                 *(uint4 *)(h2 + OW * l + 4 * i) = make_uint4(ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]);
             wave_lds_sync();
             uint16_t *tag = (uint16_t *)h1;
-            const uint32_t trashf = (uint32_t)(REF_NB + 2 * l);
+            // bucket starts; without SLOTS the scatter's atomics advance
+            // them to the bucket ends
+            const uint16_t *start = (const uint16_t *)h2;
             // -- 4. scatter fine buckets 0 .. fstar as (key bits in the
-            //    bucket << 12 | position) with the bucket as a tag (slots
-            //    of 8 keys claimed before any is stored, so the atomics
-            //    overlap; keys not taken go to per-lane trash slots)
+            //    bucket << 12 | position) with the bucket as a tag, each
+            //    to its bucket's start + its slot in the bucket (the eight
+            //    start reads, or slot claims, of a batch are in flight
+            //    together; keys not taken go to per-lane trash slots)
+            if constexpr (!SLOTS) {
+                const uint32_t trashf = (uint32_t)(REF_NB + 2 * l);
 #pragma clang loop unroll(full)
-            for (int e0 = 0; e0 < E / 4; e0 += 2)
-                if (e0 < e4) {
-                    uint32_t got[8], fb[8];
+                for (int e0 = 0; e0 < E / 4; e0 += 2)
+                    if (e0 < e4) {
+                        uint32_t cl8[8], fb[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        // a word of a key not wanted (all ones) has bucket
-                        // 4095, past every fine bucket
-                        const uint32_t w = key[4 * e0 + i];
-                        fb[i] = (w >> 20) > fstar ? trashf : (w >> 20);
-                        got[i] = atomicAdd(&h2[fb[i] >> 1], 1u << ((fb[i] & 1u) << 4));
-                    }
+                        for (int i = 0; i < 8; ++i) {
+                            const uint32_t w = key[4 * e0 + i];
+                            fb[i] = (w >> 20) > fstar ? trashf : (w >> 20);
+                            cl8[i] = atomicAdd(&h2[fb[i] >> 1], 1u << ((fb[i] & 1u) << 4));
+                        }
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int e = e0 + i / 4, v = i % 4;
-                        const bool take = fb[i] < (uint32_t)REF_NB && e < e4;
-                        const uint32_t slot = (got[i] >> ((fb[i] & 1u) << 4)) & 0xFFFFu;
-                        buf[take ? slot : cap + l] =
-                            ((key[4 * e0 + i] & LM) << POSB) | (256u * (uint32_t)e + (uint32_t)(4 * l + v));
-                        tag[take ? slot : TAGS + l] = (uint16_t)fb[i];
+                        for (int i = 0; i < 8; ++i) {
+                            const int e = e0 + i / 4, v = i % 4;
+                            const bool take = fb[i] < (uint32_t)REF_NB && e < e4;
+                            const uint32_t slot = (cl8[i] >> ((fb[i] & 1u) << 4)) & 0xFFFFu;
+                            buf[take ? slot : cap + l] =
+                                ((key[4 * e0 + i] & LM) << POSB) | (256u * (uint32_t)e + (uint32_t)(4 * l + v));
+                            tag[take ? slot : TAGS + l] = (uint16_t)fb[i];
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+            } else {
+#pragma clang loop unroll(full)
+                for (int e0 = 0; e0 < E / 4; e0 += 2)
+                    if (e0 < e4) {
+                        uint32_t fb[8], st[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            // a word of a key not wanted (all ones) has bucket
+                            // 4095, past every fine bucket
+                            fb[i] = key[4 * e0 + i] >> 20;
+                            st[i] = start[min(fb[i], fstar)];
+                        }
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const int k = 4 * e0 + i, e = e0 + i / 4, v = i % 4;
+                            const bool take = fb[i] <= fstar && e < e4;
+                            const uint32_t slot = st[i] + ((sub[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+                            buf[take ? slot : cap + l] =
+                                ((key[k] & LM) << POSB) | (256u * (uint32_t)e + (uint32_t)(4 * l + v));
+                            tag[take ? slot : TAGS + l] = (uint16_t)fb[i];
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+            }
             wave_lds_sync();
             // -- 5. rank inside the bucket. Slots run in bucket order, so
             //    ordering every bucket puts the row in place. Lane l
@@ -1630,13 +1685,19 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
             }
             // staged entries u = l, l + 64, ...: every lane takes a share
             // whatever the staged count
-            auto fend = [&](uint32_t f) { return (h2[f >> 1] >> ((f & 1u) << 4)) & 0xFFFFu; };
             for (uint32_t u = (uint32_t)l; u < nsc; u += 64u) {
                 {
                     const uint32_t w = buf[u];
                     const uint32_t f = tag[u];
-                    const uint32_t end = fend(f);
-                    const uint32_t beg = f == 0u ? 0u : fend(f - 1u);
+                    uint32_t beg, end;
+                    if constexpr (SLOTS) {
+                        beg = start[f];
+                        end = f < fstar ? (uint32_t)start[f + 1u] : nsc;
+                    } else {
+                        auto fend = [&](uint32_t b) { return (h2[b >> 1] >> ((b & 1u) << 4)) & 0xFFFFu; };
+                        end = fend(f);
+                        beg = f == 0u ? 0u : fend(f - 1u);
+                    }
                     const uint32_t lw = w >> POSB;
                     const uint32_t myidx = idx_of(w & PM);
                     uint32_t rank = 0;
