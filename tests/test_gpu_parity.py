@@ -140,6 +140,34 @@ def test_heavy_ties_at_the_boundary(pv, mode):
     np.testing.assert_array_equal(parity.to_host(only), oi)
 
 
+def test_refine_large_tie_group_among_staged_keys(pv):
+    """One key vector repeated at every 13th position scores far above the
+    others for every query (queries in [0, 3], the repeated key all 3s,
+    the rest in [-3, 3]), so each query's best fine bucket holds every copy
+    in its prefix: fewer than 256 copies in early rows (the staged-slot
+    scatter with one long bucket), up to 315 in late ones (past the 8-bit
+    slots: the exact general path). K = 2048, top_k = 1024; bit-exact."""
+    print("\n[large tie group] refine", flush=True)
+    S, H, D, top_k, g = 4104, 1, 64, 1024, 8
+    rng = np.random.default_rng(4242)
+    q = rng.integers(0, 4, (S, H, D)).astype(np.float32)
+    k = rng.integers(-3, 4, (S, H, D)).astype(np.float32)
+    hot = np.arange(5, S, 13)
+    k[hot] = 3.0
+    q, k = syn.to_bf16_bits(q), syn.to_bf16_bits(k)
+    oi, os_ = oracle.prefill(q, k, top_k, g, 2.0, "refine")
+    # the design holds: late rows start with every copy in the prefix
+    last = oi[S - 1, 0]
+    n_hot = int(np.sum(hot < (S - 1) // g * g))
+    assert n_hot >= 256 and np.array_equal(last[:n_hot], hot[:n_hot])
+    gi, gs = run_prefill(pv, q, k, top_k, g, 2.0, "refine")
+    np.testing.assert_array_equal(gi, oi)
+    np.testing.assert_array_equal(gs, os_)
+    only = pv.index_prefill(dev_tensor(q), dev_tensor(k), top_k=top_k, g=g, mode="refine")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(parity.to_host(only), oi)
+
+
 @pytest.mark.parametrize("S,H,D,top_k,dtype", [(1024, 8, 64, 64, "f32"), (700, 3, 128, 32, "bf16")])
 def test_dense_bit_exact_integer_inputs(pv, S, H, D, top_k, dtype):
     print(f"\n[dense exact] S={S} H={H} D={D} k={top_k} {dtype}", flush=True)
