@@ -62,7 +62,8 @@ __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
 // Cross-lane steps use DPP (data-parallel primitives of the VALU): row_shr:n
 // (row_shl:n) gives lane l the value of lane l - n (l + n) of its row of 16
-// lanes, row_bcast:15 / row_bcast:31 carry lane
+// lanes, wave_shr:1 (wave_shl:1) that of lane l - 1 (l + 1) of the whole
+// wavefront, row_bcast:15 / row_bcast:31 carry lane
 // 15 of a row into the next row / lane 31 into rows 2 and 3. A lane with no
 // source (or in a row left out by the row mask) gets `old`.
 template <int CTRL, int ROW_MASK = 0xF>
@@ -77,6 +78,7 @@ __device__ __forceinline__ uint32_t dpp_zero(uint32_t v) {
 }
 constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
 constexpr int DPP_ROW_SHL4 = 0x104;
+constexpr int DPP_WAVE_SHL1 = 0x130, DPP_WAVE_SHR1 = 0x138;
 constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
 
 // op over lanes 0..l for every lane l (inclusive scan); lane 63 ends with

@@ -1625,10 +1625,10 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
                 const uint4 *bp = (const uint4 *)(buf + s0);
                 const uint2 *tp = (const uint2 *)(tag + s0);
 #pragma unroll
-                for (int i = -X / 4; i < W / 4 + X / 4; ++i) {
+                for (int i = 0; i < W / 4; ++i) {
                     uint4 x = make_uint4(0u, 0u, 0u, 0u);
                     uint2 y = make_uint2(0u, 0u);
-                    if (own && (i >= 0 || l > 0)) {
+                    if (own) {
                         x = bp[i];
                         y = tp[i];
                     }
@@ -1639,11 +1639,23 @@ __device__ __forceinline__ bool fused_select(uint32_t (&key)[E], const int e4, c
                     for (int q = 0; q < 4; ++q) {
                         // window entry j + q is slot s0 - X + j + q; the list
                         // read stays inside LDS whatever the word holds
-                        const bool ok = j + q < X ? l > 0 : j + q < lim;
                         const uint32_t idx = idx_of(wd[q] & PM);
                         const uint32_t kv = ((tg[q] + 1u) << LOWB) | (LM - (wd[q] >> POSB));
-                        A[j + q] = ok ? (((uint64_t)kv << 32) | idx) : (j + q < X ? 0ull : ~0ull);
+                        A[j + q] = j + q < lim ? (((uint64_t)kv << 32) | idx) : ~0ull;
                     }
+                }
+                // the margins are the neighbours' own slots: the last X of
+                // lane l - 1 (none left of lane 0: 0) and the first X of lane
+                // l + 1 (none right of lane 63: all ones), across lanes by DPP
+#pragma unroll
+                for (int q = 0; q < X; ++q) {
+                    const uint64_t a = A[W + q], b = A[X + q];
+                    const uint32_t alo = dpp_zero<DPP_WAVE_SHR1>((uint32_t)a);
+                    const uint32_t ahi = dpp_zero<DPP_WAVE_SHR1>((uint32_t)(a >> 32));
+                    const uint32_t blo = dpp_u32<DPP_WAVE_SHL1>(~0u, (uint32_t)b);
+                    const uint32_t bhi = dpp_u32<DPP_WAVE_SHL1>(~0u, (uint32_t)(b >> 32));
+                    A[q] = ((uint64_t)ahi << 32) | alo;
+                    A[X + W + q] = ((uint64_t)bhi << 32) | blo;
                 }
             }
             // a bucket reaching from an own slot past the window
@@ -2041,12 +2053,20 @@ __global__ void __launch_bounds__(512) k_refine(RefParams p) {
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (e < e4) v = *(const uint4 *)(my + (e * 64 + l) * 16);
         // position 256 e + 4 l + v; the bound is taken against a uniform
-        // value so that no per-position register outlives the load
+        // value so that no per-position register outlives the load (whole
+        // chunks of 256 take no per-key test)
         const int rem = nc - 256 * e;
-        key[4 * e + 0] = 4 * l + 0 < rem ? v.x : 0u;
-        key[4 * e + 1] = 4 * l + 1 < rem ? v.y : 0u;
-        key[4 * e + 2] = 4 * l + 2 < rem ? v.z : 0u;
-        key[4 * e + 3] = 4 * l + 3 < rem ? v.w : 0u;
+        if (rem >= 256) {
+            key[4 * e + 0] = v.x;
+            key[4 * e + 1] = v.y;
+            key[4 * e + 2] = v.z;
+            key[4 * e + 3] = v.w;
+        } else {
+            key[4 * e + 0] = 4 * l + 0 < rem ? v.x : 0u;
+            key[4 * e + 1] = 4 * l + 1 < rem ? v.y : 0u;
+            key[4 * e + 2] = 4 * l + 2 < rem ? v.z : 0u;
+            key[4 * e + 3] = 4 * l + 3 < rem ? v.w : 0u;
+        }
     }
     // one key of every 64th part of the list, for the coarse range below
     const uint32_t smp = nc >= 64 ? ((const uint32_t *)my)[((uint32_t)l * (uint32_t)nc) >> 6] : 0u;
