@@ -214,7 +214,7 @@ struct ScanParams {
 // entries, four lanes to a chunk, so that one store instruction writes up to
 // 16 whole chunks of different streams. A stream that passes cap_half
 // survivors stops keeping (its row takes the exact fallback).
-template <typename T, int D>
+template <typename T, int D, bool UNIT>
 __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2 : 4) k_scan(ScanParams p) {
     constexpr int GB = SCAN_GB;
     constexpr int RB = D * (int)sizeof(T);     // bytes per key row
@@ -232,6 +232,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
     __shared__ __align__(16) uint2 ringS[RING * NSTREAM];
     constexpr uint32_t RROW = NSTREAM * 8;         // bytes per ring row
     static_assert((RING & (RING - 1)) == 0 && (RROW & (RROW - 1)) == 0, "ring sizes are powers of two");
+    static_assert(RROW == 0x1000, "the filter's count step is written as 0x1000");
     static_assert(FLUSH == 8, "a chunk is four lanes' 16-byte stores");
 
     // Heads go to XCDs in groups of ceil(Hc / 8) (each XCD's contiguous range
@@ -264,12 +265,16 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
     }
     const float never = __builtin_nanf("");  // s >= NaN is false for every s
 
-    // this lane's two streams: survivors kept so far (cs[gb], counted in
-    // units of RROW so that it is the ring row's byte offset once masked),
-    // fl[gb] of them already written to the stream's buffer at byte offset
-    // soff0[gb] from the block's part of the survivor array
+    // this lane's two streams: survivors kept so far (cs[gb]) and already
+    // written (fl[gb]), both counted in units of RROW so that a count masked
+    // to the ring is the ring row's byte offset; the stream's buffer sits at
+    // byte offset soff0[gb] from the block's part of the survivor array.
+    // pk[gb] describes the stream's next chunk for the flush: bits 13.. its
+    // index in 64-byte units from the wavefront's part of the survivor
+    // array, bits 0..12 the LDS byte offset / 8 of its first ring entry.
     unsigned char *sb = (unsigned char *)p.out + ((int64_t)hl * p.G + j0) * 2 * (int64_t)p.stride * 8;
-    uint32_t soff0[GB], cs[GB], fl[GB];
+    unsigned char *sbw = sb + (int64_t)(32 * GB * w) * 2 * (int64_t)p.stride * 8;
+    uint32_t soff0[GB], cs[GB], fl[GB], pk[GB];
     int vcount[GB];
     float tau[GB];
     for (int gb = 0; gb < GB; ++gb) {
@@ -278,6 +283,8 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
         const int jl = 32 * GB * w + 32 * gb + (l & 31);
         const int64_t j = j0 + jl;
         soff0[gb] = (uint32_t)((jl * 2 + half) * p.stride) * 8u;
+        pk[gb] = ((uint32_t)(((32 * gb + (l & 31)) * 2 + half) * p.stride) / 8u << 13) |
+                 (uint32_t)(gb * SCAN_THREADS + w * 64 + l);
         int64_t vc = 0;
         tau[gb] = never;  // rows past the end never keep
         if (j < p.G) {
@@ -311,7 +318,9 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
     const int ntiles_k = (int)((vmax + SCAN_KEYS - 1) / SCAN_KEYS);
     const unsigned char *Kb = (const unsigned char *)((const T *)p.K + p.k_head0 + (int64_t)hl * p.k_head);
     const int64_t krow_bytes = p.k_row * (int64_t)sizeof(T);
-    const uint32_t kstr = (uint32_t)p.kstride;
+    // UNIT: every key (kstride 1), so that a score's key index is the tile's
+    // plus a constant
+    const uint32_t kstr = UNIT ? 1u : (uint32_t)p.kstride;
     const uint32_t lane_key = (uint32_t)p.koff + kstr * (uint32_t)(4 * half);
 
     // tile kt, staged through registers: piece i of a thread is 16-byte
@@ -321,14 +330,40 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
     // chunk pos ^ swz(r). Keys past the last row's prefix repeat the last
     // key: their scores are never kept (that tile takes the causal test).
     typedef u32x4_t piece_t[NLD];
-    auto load_tile = [&](int kt, piece_t &pr) {
+    // A tile's rows are read through a buffer resource whose base is the
+    // tile's first key (scalar registers) and whose range ends after the
+    // row of virtual key vmax - 1: this thread's piece sits at a fixed
+    // offset from the base, and rows past the range read as zero (their
+    // scores are never kept). Offsets past 32 bits take the clamped loads.
+    const uint32_t rstep = kstr * (uint32_t)krow_bytes;  // bytes between consecutive virtual keys
+    const bool bufok = (uint64_t)kstr * (uint64_t)krow_bytes * SCAN_KEYS + RB < (1ull << 32);
+    const int64_t kend = vmax > 0 ? (p.koff + (int64_t)p.kstride * (vmax - 1)) * krow_bytes + RB : 0;
+    uint32_t loff[NLD];
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int q = min((i * (SCAN_THREADS / 64) + w) * 64 + l, PIECES - 1);
-            const int r = q / NCK, c = q % NCK;
-            const int64_t v = min((int64_t)kt * SCAN_KEYS + r, vmax - 1);
-            const int64_t key = p.koff + (int64_t)p.kstride * v;
-            pr[i] = *(const u32x4_t *)(Kb + key * krow_bytes + c * 16);
+    for (int i = 0; i < NLD; ++i) {
+        const int q = min((i * (SCAN_THREADS / 64) + w) * 64 + l, PIECES - 1);
+        loff[i] = (uint32_t)(q / NCK) * rstep + (uint32_t)(q % NCK) * 16u;
+    }
+    auto load_tile = [&](int kt, piece_t &pr, auto buf) {
+        const int64_t v0 = (int64_t)kt * SCAN_KEYS;
+        if constexpr (decltype(buf)::value) {
+            const int64_t b0 = (p.koff + (int64_t)p.kstride * v0) * krow_bytes;
+            const int64_t left = kend - b0;
+            const uint32_t nrec = left <= 0 ? 0u : (left >= (int64_t)0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)left);
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(Kb + b0), (short)0, (int)nrec, 0x00020000);
+#pragma unroll
+            for (int i = 0; i < NLD; ++i)
+                pr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)loff[i], 0, 0));
+        } else {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int q = min((i * (SCAN_THREADS / 64) + w) * 64 + l, PIECES - 1);
+                const int r = q / NCK, c = q % NCK;
+                const int64_t v = min(v0 + r, vmax - 1);
+                const int64_t key = p.koff + (int64_t)p.kstride * v;
+                pr[i] = *(const u32x4_t *)(Kb + key * krow_bytes + c * 16);
+            }
         }
     };
     auto store_tile = [&](int kt, const piece_t &pr) {
@@ -344,57 +379,71 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
     };
 
     typedef f32x16_t acc_t[GB];
+    // fragment of k-step ks: chunk (2 ks + half) ^ (r & SWZ) of tile row r,
+    // i.e. LDS address A0 ^ (ks << 5) with A0 that of k-step 0 (the chunk
+    // bits lie below the row's); A0 is renewed opaquely every tile so that
+    // the eight addresses are formed in the loop instead of held in
+    // registers
+    const uint32_t A0 = (uint32_t)(uintptr_t)smem + (uint32_t)((l & 31) * RB) +
+                        ((uint32_t)(half ^ ((l & 31) & SWZ)) << 4);
+    typedef __attribute__((address_space(3))) const unsigned char *lds_cptr;
+    // All NKS fragments of a tile are read before its matrix work (the
+    // scheduler would otherwise interleave one read and one MFMA at a time,
+    // exposing the LDS latency eight times a step).
     auto matrix = [&](int kt, acc_t &acc) {
-        const unsigned char *cur = smem + (kt & 1) * TILE;
+        uint32_t a0;
+        asm volatile("" : "=v"(a0) : "0"(A0));
 #pragma unroll
         for (int gb = 0; gb < GB; ++gb) acc[gb] = f32x16_t{};
-        const int r = l & 31;
+        frag_t fa[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            fa[ks] = *(__attribute__((address_space(3))) const frag_t *)((lds_cptr)(uintptr_t)(a0 ^ (uint32_t)(ks << 5)) +
+                                                                       (kt & 1) * TILE);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            const unsigned char *ap = cur + r * RB + (((2 * ks + half) ^ (r & SWZ)) * 16);
-            if constexpr (std::is_same<T, float>::value) {
-                const f32x4_t a = *(const f32x4_t *)ap;
 #pragma unroll
-                for (int gb = 0; gb < GB; ++gb)
+            for (int gb = 0; gb < GB; ++gb) {
+                if constexpr (std::is_same<T, float>::value) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
-                        acc[gb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[v], bq[gb][ks][v], acc[gb], 0, 0, 0);
-            } else {
-                const bf16x8_t a = *(const bf16x8_t *)ap;
-#pragma unroll
-                for (int gb = 0; gb < GB; ++gb)
-                    acc[gb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[gb][ks], acc[gb], 0, 0, 0);
+                        acc[gb] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[ks][v], bq[gb][ks][v], acc[gb], 0, 0, 0);
+                } else {
+                    acc[gb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks], bq[gb][ks], acc[gb], 0, 0, 0);
+                }
             }
         }
     };
 
     // Every stream with FLUSH or more staged survivors sends its FLUSH
-    // oldest (entries fl .. fl+7, ring rows fl % RING ..) as one 64-byte
-    // chunk. The streams of each column block are ranked; the r-th one
-    // passes one word -- its chunk's index in the survivor array (64-byte
-    // units) above its lane and the chunk's first ring row -- to lane 4r
-    // (forward permute, no LDS memory) and over its quad (DPP), and lane
-    // 4r + q stores entries fl + 2q, fl + 2q + 1 (one LDS read of two ring
-    // rows): an instruction writes 16 whole chunks. Both column blocks'
-    // passes run side by side, so their LDS round trips overlap. At most
-    // cap_half + 16 are ever kept, inside the stream's stride.
-    // Wavefront-uniform control flow.
-    static_assert(RING % FLUSH == 0, "a chunk's ring rows do not wrap");
+    // oldest (ring rows fl % RING ..) as one 64-byte chunk. The streams of
+    // each column block are ranked; the r-th one passes pk (its chunk's
+    // index and first ring entry) to lane 4r (forward permute, no LDS
+    // memory) and over its quad (DPP), and lane 4r + q stores entries
+    // 2q, 2q + 1 of the chunk (one LDS read of two ring rows): an
+    // instruction writes 16 whole chunks. Both column blocks' passes run
+    // side by side, so their LDS round trips overlap. At most cap_half + 16
+    // are ever kept, inside the stream's stride. Wavefront-uniform control
+    // flow.
+    static_assert(RING == 2 * FLUSH, "a chunk starts at ring row 0 or FLUSH");
+    static_assert(NSTREAM <= 1024, "ring entry offsets / 8 fit 13 bits");
+    const uint32_t lds_q = 2u * (uint32_t)(l & 3) * RROW;  // ring rows 2q, 2q+1 of a chunk
+    unsigned char *sbq = sbw + 16u * (uint32_t)(l & 3);    // entries 2q, 2q+1 of a chunk
     auto flush = [&]() {
         bool need[GB];
         uint64_t M[GB];
-        uint32_t rank[GB], pk[GB];
+        uint32_t rank[GB];
         int nf[GB];
         uint64_t any = 0;
         int nmax = 0;
 #pragma unroll
         for (int gb = 0; gb < GB; ++gb) {
-            need[gb] = cs[gb] / RROW - fl[gb] >= (uint32_t)FLUSH;
+            need[gb] = cs[gb] - fl[gb] >= (uint32_t)FLUSH * RROW;
             M[gb] = __ballot(need[gb]);
             nf[gb] = __popcll(M[gb]);
             rank[gb] = __builtin_amdgcn_mbcnt_hi((uint32_t)(M[gb] >> 32),
                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)M[gb], 0u));
-            pk[gb] = ((soff0[gb] / 64u + fl[gb] / 8u) << 10) | ((fl[gb] % RING) << 6) | (uint32_t)l;
             any |= M[gb];
             nmax = max(nmax, nf[gb]);
         }
@@ -411,16 +460,18 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
 #pragma unroll
             for (int gb = 0; gb < GB; ++gb) {
                 if ((l >> 2) < nf[gb] - r0) {
-                    const uint32_t q2 = 2u * (uint32_t)(l & 3);
-                    const uint2 *e = ringS + (((got[gb] >> 6) & (RING - 1)) + q2) * NSTREAM + gb * SCAN_THREADS +
-                                     w * 64 + (int)(got[gb] & 63u);
+                    const uint2 *e = (const uint2 *)((unsigned char *)ringS + (((got[gb] & 0x1FFFu) << 3) | lds_q));
                     const uint2 a = e[0], b = e[NSTREAM];
-                    *(uint4 *)(sb + (got[gb] >> 10) * 64u + 8u * q2) = make_uint4(a.x, a.y, b.x, b.y);
+                    *(uint4 *)(sbq + (got[gb] >> 13) * 64u) = make_uint4(a.x, a.y, b.x, b.y);
                 }
             }
         }
 #pragma unroll
-        for (int gb = 0; gb < GB; ++gb) fl[gb] += need[gb] ? (uint32_t)FLUSH : 0u;
+        for (int gb = 0; gb < GB; ++gb) {
+            // next chunk: one further in the array, the other half of the ring
+            fl[gb] += need[gb] ? (uint32_t)FLUSH * RROW : 0u;
+            pk[gb] = need[gb] ? (pk[gb] + (1u << 13)) ^ (FLUSH * RROW / 8u) : pk[gb];
+        }
     };
 
     // keep the scores of tile kt that reach the row's threshold; at most 16
@@ -428,10 +479,11 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
     // test. A flush check after every 8 scores of each column block keeps
     // the ring from filling. Per score: one compare (two on causal tiles),
     // the count update, the ring slot address from the count (one and-or),
-    // and one LDS instruction storing score bits and key index; the 16 key
-    // indices of the tile are shared by both column blocks. A slot is
-    // written whether kept or not (row cnt % RING is free: fewer than RING
-    // entries wait); only kept ones are counted.
+    // the key index, and one LDS instruction storing score bits and key
+    // index from their own registers; the 16 key indices of the tile are
+    // shared by both column blocks. A slot is written whether kept or not
+    // (row cnt % RING is free: fewer than RING entries wait); only kept ones
+    // are counted.
     auto filter = [&](int kt, const acc_t &acc) {
 #pragma unroll
         for (int gb = 0; gb < GB; ++gb)
@@ -452,9 +504,20 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
                         const float sc = acc[gb][v];
                         bool keep = sc >= tau[gb];
                         if constexpr (decltype(causal)::value) keep = keep && (vo < lim);
-                        uint2 *slot = (uint2 *)((unsigned char *)ringS + ((cs[gb] & ((RING - 1) * RROW)) | col));
-                        *slot = make_uint2(__float_as_uint(sc), tkey + kstr * (uint32_t)vo);
-                        cs[gb] += keep ? RROW : 0u;
+                        // only the lanes that keep write (exec = their ballot,
+                        // restored at once: no branch); they also count
+                        const uint32_t slot = (uint32_t)(uintptr_t)ringS + ((cs[gb] & ((RING - 1) * RROW)) | col);
+                        const uint64_t km = __builtin_amdgcn_ballot_w64(keep);
+                        uint64_t sv;
+                        asm volatile(
+                            "s_and_saveexec_b64 %[sv], %[km]\n\t"
+                            "ds_write2_b32 %[a], %[x], %[y] offset1:1\n\t"
+                            "v_add_u32_e32 %[c], 0x1000, %[c]\n\t"
+                            "s_mov_b64 exec, %[sv]"
+                            : [sv] "=&s"(sv), [c] "+v"(cs[gb])
+                            : [km] "s"(km), [a] "v"(slot), [x] "v"(__float_as_uint(sc)),
+                              [y] "v"(tkey + kstr * (uint32_t)vo)
+                            : "memory");
                     }
                 }
                 flush();
@@ -464,52 +527,59 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
         else run(std::true_type{});
     };
 
-    // Two tiles are in flight in registers while a third is in LDS. Step
-    // kt: the barrier (after this wavefront's LDS writes are done) makes
-    // tile kt, written by every wavefront in the previous step, readable,
-    // and frees the buffer of tile kt-1; tile kt+1 (loaded two steps ago)
-    // goes there, and its registers take the loads of tile kt+3. The
-    // compiler waits for exactly those loads before the LDS writes, so
-    // survivor stores issued since are never waited for.
-    auto step = [&](int kt, const acc_t &prev, acc_t &cur, piece_t &nxt) {
+    // Four tiles are in flight in registers while one is in LDS. Step kt:
+    // the barrier (after this wavefront's LDS writes are done) makes tile
+    // kt, written by every wavefront in the previous step, readable, and
+    // frees the buffer of tile kt-1; tile kt+1 (loaded four steps ago) goes
+    // there, and its registers take the loads of tile kt+5; then tile kt's
+    // scores are computed and filtered. The compiler's wait before the LDS
+    // writes counts the three later tile loads, so survivor stores of the
+    // last steps need not have completed.
+    auto step = [&](int kt, acc_t &acc, piece_t &nxt, auto buf) {
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
-        // unconditional (tiles past the last repeat its last key), so that
-        // the compiler's count of loads in flight is exact
+        // unconditional (tiles past the last read zeros or repeat its last
+        // key), so that the compiler's count of loads in flight is exact
         store_tile(kt + 1, nxt);
-        load_tile(kt + 3, nxt);
-        matrix(kt, cur);
-        if (kt > 0) filter(kt - 1, prev);
+        load_tile(kt + 5, nxt, buf);
+        matrix(kt, acc);
+        filter(kt, acc);
     };
-    // every proxy fragment has arrived before the loop. Even tiles
-    // accumulate in accA and stage in pA, odd ones in accB and pB (two
-    // steps per iteration keep the names static).
+    // every proxy fragment has arrived before the loop. Tile t stages in
+    // P[t % 4] (four steps per iteration keep the names static). One copy
+    // of the loop per kind of tile load, so that each has a single load
+    // instruction.
     __builtin_amdgcn_s_waitcnt(0);
-    acc_t accA, accB;
-    piece_t pA, pB;
-    if (ntiles_k > 0) {
-        load_tile(0, pA);
-        load_tile(1, pB);
-        store_tile(0, pA);
-        load_tile(2, pA);
-    }
-    int kt = 0;
-    for (; kt + 2 <= ntiles_k; kt += 2) {
-        step(kt, accB, accA, pB);
-        step(kt + 1, accA, accB, pA);
-    }
-    if (kt < ntiles_k) {
-        step(kt, accB, accA, pB);
-        filter(kt, accA);
-    } else if (ntiles_k > 0) {
-        filter(ntiles_k - 1, accB);
-    }
+    auto mainloop = [&](auto buf) {
+        acc_t acc;
+        piece_t P0, P1, P2, P3;
+        if (ntiles_k > 0) {
+            load_tile(0, P0, buf);
+            load_tile(1, P1, buf);
+            load_tile(2, P2, buf);
+            load_tile(3, P3, buf);
+            store_tile(0, P0);
+            load_tile(4, P0, buf);
+        }
+        int kt = 0;
+        for (; kt + 4 <= ntiles_k; kt += 4) {
+            step(kt, acc, P1, buf);
+            step(kt + 1, acc, P2, buf);
+            step(kt + 2, acc, P3, buf);
+            step(kt + 3, acc, P0, buf);
+        }
+        if (kt < ntiles_k) step(kt, acc, P1, buf);
+        if (kt + 1 < ntiles_k) step(kt + 1, acc, P2, buf);
+        if (kt + 2 < ntiles_k) step(kt + 2, acc, P3, buf);
+    };
+    if (bufok) mainloop(std::true_type{});
+    else mainloop(std::false_type{});
 
     // the rest of each ring (fewer than FLUSH entries) one by one
     for (int gb = 0; gb < GB; ++gb) {
         const uint2 *rs = ringS + gb * SCAN_THREADS + stream0;
         const uint32_t cnt = cs[gb] / RROW;
-        for (uint32_t e = fl[gb]; e < cnt; ++e) *(uint2 *)(sb + soff0[gb] + e * 8u) = rs[(e % RING) * NSTREAM];
+        for (uint32_t e = fl[gb] / RROW; e < cnt; ++e) *(uint2 *)(sb + soff0[gb] + e * 8u) = rs[(e % RING) * NSTREAM];
         const int64_t j = j0 + 32 * GB * w + 32 * gb + (l & 31);
         if (j < p.G) p.cnt[((int64_t)hl * p.G + j) * 2 + half] = (int)cnt;
     }
@@ -2866,19 +2936,20 @@ int launch_select(const SelParams &se, bool sorted, int sel_e, unsigned blocks, 
     return PIVOT_OK;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool UNIT>
 int launch_scan(const ScanParams &sp, hipStream_t st) {
     // dynamic LDS: the two key tiles (the survivor rings are static)
     const size_t lds = 2 * SCAN_KEYS * (size_t)D * sizeof(T);
-    HIP_TRY(set_lds((const void *)k_scan<T, D>, lds));
-    hipLaunchKernelGGL((k_scan<T, D>), dim3(sp.Hc * sp.n_tiles), dim3(SCAN_THREADS), lds, st, sp);
+    HIP_TRY(set_lds((const void *)k_scan<T, D, UNIT>, lds));
+    hipLaunchKernelGGL((k_scan<T, D, UNIT>), dim3(sp.Hc * sp.n_tiles), dim3(SCAN_THREADS), lds, st, sp);
     HIP_TRY(hipGetLastError());
     return PIVOT_OK;
 }
 
 template <typename T>
 int dispatch_scan(int D, const ScanParams &sp, hipStream_t st) {
-    return D == 64 ? launch_scan<T, 64>(sp, st) : launch_scan<T, 128>(sp, st);
+    if (sp.kstride == 1) return D == 64 ? launch_scan<T, 64, true>(sp, st) : launch_scan<T, 128, true>(sp, st);
+    return D == 64 ? launch_scan<T, 64, false>(sp, st) : launch_scan<T, 128, false>(sp, st);
 }
 
 template <typename T>
