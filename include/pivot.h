@@ -137,6 +137,10 @@ size_t pivot_prefill_workspace_bytes(int64_t S, int32_t H, int32_t D,
  *   K = floor(top_k * candidate_ratio) with top_k <= K <= 8192 (the
  *   resource limit of the selection kernels; larger -> PIVOT_EUNSUPPORTED),
  *   mode      PIVOT_REFINE, PIVOT_REUSE or PIVOT_REFINE_LITERAL
+ *   The scan reads 32 sampled key rows at 32-bit offsets from the first:
+ *   inputs where 32 * s * H * D * element size reaches 4 GiB (s, the
+ *   sampling stride, is about S / 4080 for long sequences) return
+ *   PIVOT_EUNSUPPORTED; no input that fits one GPU's memory comes near. 
  *   out_idx   device (S, H, top_k) int32, written completely
  *   out_score device (S, H, top_k) float32 or NULL
  *   workspace device scratch, workspace_bytes as described above

@@ -81,6 +81,11 @@ def test_workspace_sizes(pv):
     assert f(64, 1, 64, 2048, 8, 4.0, 0, 1) > f(64, 1, 64, 2048, 8, 2.0, 0, 1) > 0
     assert f(64, 1, 64, 8192, 8, 1.0, 1, 1) > 0
     assert pv.lib.dense_index_workspace_bytes(1024, 8, 64, 64, 0) > 0
+    # the scan's key tiles span 32 sampled rows through 32-bit offsets: at
+    # S = 2^31 - 2 the sampling stride (2^20 keys) of 128-byte rows passes
+    # 4 GiB and the call is refused; at S = 2^28 (stride 2^17) it is not
+    assert f((1 << 31) - 2, 1, 64, 64, 8, 2.0, 0, 1) == 0
+    assert f(1 << 28, 1, 64, 64, 8, 2.0, 0, 1) > 0
     ctx = (ctypes.c_int64 * 3)(5, 9, 100)
     assert pv.lib.pivot_decode_workspace_bytes(3, ctx, 2, 8, 128, 64, 2.0, 0, 1) > 0
     bad = (ctypes.c_int64 * 2)(5, 0)

@@ -333,10 +333,10 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
     // A tile's rows are read through a buffer resource whose base is the
     // tile's first key (scalar registers) and whose range ends after the
     // row of virtual key vmax - 1: this thread's piece sits at a fixed
-    // offset from the base, and rows past the range read as zero (their
-    // scores are never kept). Offsets past 32 bits take the clamped loads.
+    // offset from the base (below 2^32: the host refuses key strides that
+    // would pass it), and rows past the range read as zero (their scores
+    // are never kept).
     const uint32_t rstep = kstr * (uint32_t)krow_bytes;  // bytes between consecutive virtual keys
-    const bool bufok = (uint64_t)kstr * (uint64_t)krow_bytes * SCAN_KEYS + RB < (1ull << 32);
     const int64_t kend = vmax > 0 ? (p.koff + (int64_t)p.kstride * (vmax - 1)) * krow_bytes + RB : 0;
     uint32_t loff[NLD];
 #pragma unroll
@@ -344,27 +344,15 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
         const int q = min((i * (SCAN_THREADS / 64) + w) * 64 + l, PIECES - 1);
         loff[i] = (uint32_t)(q / NCK) * rstep + (uint32_t)(q % NCK) * 16u;
     }
-    auto load_tile = [&](int kt, piece_t &pr, auto buf) {
-        const int64_t v0 = (int64_t)kt * SCAN_KEYS;
-        if constexpr (decltype(buf)::value) {
-            const int64_t b0 = (p.koff + (int64_t)p.kstride * v0) * krow_bytes;
-            const int64_t left = kend - b0;
-            const uint32_t nrec = left <= 0 ? 0u : (left >= (int64_t)0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)left);
-            const __amdgpu_buffer_rsrc_t rs =
-                __builtin_amdgcn_make_buffer_rsrc((void *)(Kb + b0), (short)0, (int)nrec, 0x00020000);
+    auto load_tile = [&](int kt, piece_t &pr) {
+        const int64_t b0 = (p.koff + (int64_t)p.kstride * kt * SCAN_KEYS) * krow_bytes;
+        const int64_t left = kend - b0;
+        const uint32_t nrec = left <= 0 ? 0u : (left >= (int64_t)0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)left);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(Kb + b0), (short)0, (int)nrec, 0x00020000);
 #pragma unroll
-            for (int i = 0; i < NLD; ++i)
-                pr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)loff[i], 0, 0));
-        } else {
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                const int q = min((i * (SCAN_THREADS / 64) + w) * 64 + l, PIECES - 1);
-                const int r = q / NCK, c = q % NCK;
-                const int64_t v = min(v0 + r, vmax - 1);
-                const int64_t key = p.koff + (int64_t)p.kstride * v;
-                pr[i] = *(const u32x4_t *)(Kb + key * krow_bytes + c * 16);
-            }
-        }
+        for (int i = 0; i < NLD; ++i)
+            pr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)loff[i], 0, 0));
     };
     auto store_tile = [&](int kt, const piece_t &pr) {
 #pragma unroll
@@ -535,45 +523,41 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
     // scores are computed and filtered. The compiler's wait before the LDS
     // writes counts the three later tile loads, so survivor stores of the
     // last steps need not have completed.
-    auto step = [&](int kt, acc_t &acc, piece_t &nxt, auto buf) {
+    auto step = [&](int kt, acc_t &acc, piece_t &nxt) {
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
-        // unconditional (tiles past the last read zeros or repeat its last
-        // key), so that the compiler's count of loads in flight is exact
+        // unconditional (tiles past the last read zeros), so that the
+        // compiler's count of loads in flight is exact
         store_tile(kt + 1, nxt);
-        load_tile(kt + 5, nxt, buf);
+        load_tile(kt + 5, nxt);
         matrix(kt, acc);
         filter(kt, acc);
     };
     // every proxy fragment has arrived before the loop. Tile t stages in
-    // P[t % 4] (four steps per iteration keep the names static). One copy
-    // of the loop per kind of tile load, so that each has a single load
-    // instruction.
+    // P[t % 4] (four steps per iteration keep the names static).
     __builtin_amdgcn_s_waitcnt(0);
-    auto mainloop = [&](auto buf) {
+    {
         acc_t acc;
         piece_t P0, P1, P2, P3;
         if (ntiles_k > 0) {
-            load_tile(0, P0, buf);
-            load_tile(1, P1, buf);
-            load_tile(2, P2, buf);
-            load_tile(3, P3, buf);
+            load_tile(0, P0);
+            load_tile(1, P1);
+            load_tile(2, P2);
+            load_tile(3, P3);
             store_tile(0, P0);
-            load_tile(4, P0, buf);
+            load_tile(4, P0);
         }
         int kt = 0;
         for (; kt + 4 <= ntiles_k; kt += 4) {
-            step(kt, acc, P1, buf);
-            step(kt + 1, acc, P2, buf);
-            step(kt + 2, acc, P3, buf);
-            step(kt + 3, acc, P0, buf);
+            step(kt, acc, P1);
+            step(kt + 1, acc, P2);
+            step(kt + 2, acc, P3);
+            step(kt + 3, acc, P0);
         }
-        if (kt < ntiles_k) step(kt, acc, P1, buf);
-        if (kt + 1 < ntiles_k) step(kt + 1, acc, P2, buf);
-        if (kt + 2 < ntiles_k) step(kt + 2, acc, P3, buf);
-    };
-    if (bufok) mainloop(std::true_type{});
-    else mainloop(std::false_type{});
+        if (kt < ntiles_k) step(kt, acc, P1);
+        if (kt + 1 < ntiles_k) step(kt + 1, acc, P2);
+        if (kt + 2 < ntiles_k) step(kt + 2, acc, P3);
+    }
 
     // the rest of each ring (fewer than FLUSH entries) one by one
     for (int gb = 0; gb < GB; ++gb) {
@@ -2785,6 +2769,11 @@ int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio,
     pl.rsel = sm.rsel;
     pl.cap_half = sm.cap_half;
     pl.keep_all_n = sm.keep_all_n;
+    // the scan addresses a key tile's rows by 32-bit offsets from the
+    // tile's first key: SCAN_KEYS strided rows must span less than 4 GiB
+    // (far beyond any input that fits one GPU's memory)
+    if ((uint64_t)s * (uint64_t)H * (uint64_t)D * (uint64_t)pl.esz * SCAN_KEYS + (uint64_t)D * pl.esz >= (1ull << 32))
+        return PIVOT_EUNSUPPORTED;
     const int64_t vmax = (pl.n_max + s - 1) / s;
     // a multiple of 8: every stream of the sample pass starts on a 64-byte
     // chunk, as the scan's flush addresses streams in chunks
