@@ -181,7 +181,9 @@ struct ScanParams {
     int g;                  // group size (prefix of row j = max(j*g, 1))
     int kstride, koff;      // key sampling
     const float *tau;       // per-row threshold, nullptr = keep all
-    uint32_t *out;          // survivors [(row*2+half)*stride + slot]: (float bits, key) pairs
+    uint32_t *out;          // survivors [(row*2+half)*stride + slot]: (float bits, key) pairs,
+                            // or float bits alone when score_only
+    int score_only;         // write scores without keys (the sample pass)
     int cap_half;           // more than this many in a half = overflow
     int stride;             // slots per (row, half): cap_half + 32, a multiple of 8
     int *cnt;               // survivors per (row, half); > cap_half = overflow
@@ -274,6 +276,10 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
     // array, bits 0..12 the LDS byte offset / 8 of its first ring entry.
     unsigned char *sb = (unsigned char *)p.out + ((int64_t)hl * p.G + j0) * 2 * (int64_t)p.stride * 8;
     unsigned char *sbw = sb + (int64_t)(32 * GB * w) * 2 * (int64_t)p.stride * 8;
+    // the same streams with 4-byte entries (score_only)
+    unsigned char *sb4 = (unsigned char *)p.out + ((int64_t)hl * p.G + j0) * 2 * (int64_t)p.stride * 4;
+    unsigned char *sbw4 = sb4 + (int64_t)(32 * GB * w) * 2 * (int64_t)p.stride * 4;
+    const bool score_only = p.score_only != 0;
     uint32_t soff0[GB], cs[GB], fl[GB], pk[GB];
     int vcount[GB];
     float tau[GB];
@@ -418,6 +424,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
     static_assert(NSTREAM <= 1024, "ring entry offsets / 8 fit 13 bits");
     const uint32_t lds_q = 2u * (uint32_t)(l & 3) * RROW;  // ring rows 2q, 2q+1 of a chunk
     unsigned char *sbq = sbw + 16u * (uint32_t)(l & 3);    // entries 2q, 2q+1 of a chunk
+    unsigned char *sbq4 = sbw4 + 8u * (uint32_t)(l & 3);   // the same, 4-byte entries
     auto flush = [&]() {
         bool need[GB];
         uint64_t M[GB];
@@ -450,7 +457,8 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
                 if ((l >> 2) < nf[gb] - r0) {
                     const uint2 *e = (const uint2 *)((unsigned char *)ringS + (((got[gb] & 0x1FFFu) << 3) | lds_q));
                     const uint2 a = e[0], b = e[NSTREAM];
-                    *(uint4 *)(sbq + (got[gb] >> 13) * 64u) = make_uint4(a.x, a.y, b.x, b.y);
+                    if (score_only) *(uint2 *)(sbq4 + (got[gb] >> 13) * 32u) = make_uint2(a.x, b.x);
+                    else *(uint4 *)(sbq + (got[gb] >> 13) * 64u) = make_uint4(a.x, a.y, b.x, b.y);
                 }
             }
         }
@@ -563,7 +571,10 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
     for (int gb = 0; gb < GB; ++gb) {
         const uint2 *rs = ringS + gb * SCAN_THREADS + stream0;
         const uint32_t cnt = cs[gb] / RROW;
-        for (uint32_t e = fl[gb] / RROW; e < cnt; ++e) *(uint2 *)(sb + soff0[gb] + e * 8u) = rs[(e % RING) * NSTREAM];
+        for (uint32_t e = fl[gb] / RROW; e < cnt; ++e) {
+            if (score_only) *(uint32_t *)(sb4 + soff0[gb] / 2u + e * 4u) = rs[(e % RING) * NSTREAM].x;
+            else *(uint2 *)(sb + soff0[gb] + e * 8u) = rs[(e % RING) * NSTREAM];
+        }
         const int64_t j = j0 + 32 * GB * w + 32 * gb + (l & 31);
         if (j < p.G) p.cnt[((int64_t)hl * p.G + j) * 2 + half] = (int)cnt;
     }
@@ -572,7 +583,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
 // -------------------------------------------------------------------- tau
 
 struct TauParams {
-    const uint2 *samp;      // samples: (float bits, key)
+    const uint32_t *samp;   // samples: float bits
     const int *scnt;
     int samp_half, samp_stride;
     float *tau;
@@ -608,14 +619,14 @@ __global__ void __launch_bounds__(SEL_THREADS) k_tau(TauParams p) {
     Selector<4, SEL_LOG2NB> sel{G, hist, vars};
     const int elim = (int)((ns + SEL_THREADS - 1) / SEL_THREADS);
     uint32_t key[TAU_E];
-    const uint2 *b0 = p.samp + (2 * r) * (int64_t)p.samp_stride;
-    const uint2 *b1 = p.samp + (2 * r + 1) * (int64_t)p.samp_stride;
+    const uint32_t *b0 = p.samp + (2 * r) * (int64_t)p.samp_stride;
+    const uint32_t *b1 = p.samp + (2 * r + 1) * (int64_t)p.samp_stride;
     bool has[TAU_E];
 #pragma unroll
     for (int e = 0; e < TAU_E; ++e) {
         const uint32_t gi = e * SEL_THREADS + threadIdx.x;
         has[e] = e < elim && gi < ns;
-        key[e] = has[e] ? (gi < (uint32_t)c0 ? b0[gi].x : b1[gi - c0].x) : 0u;
+        key[e] = has[e] ? (gi < (uint32_t)c0 ? b0[gi] : b1[gi - c0]) : 0u;
     }
 #pragma unroll
     for (int e = 0; e < TAU_E; ++e) key[e] = has[e] ? score_key(__uint_as_float(key[e])) : 0u;
@@ -2775,8 +2786,9 @@ int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio,
     if ((uint64_t)s * (uint64_t)H * (uint64_t)D * (uint64_t)pl.esz * SCAN_KEYS + (uint64_t)D * pl.esz >= (1ull << 32))
         return PIVOT_EUNSUPPORTED;
     const int64_t vmax = (pl.n_max + s - 1) / s;
-    // a multiple of 8: every stream of the sample pass starts on a 64-byte
-    // chunk, as the scan's flush addresses streams in chunks
+    // a multiple of 8: every stream of the sample pass (4-byte scores)
+    // starts on a 32-byte chunk, as the scan's flush addresses streams in
+    // chunks of 8 entries
     pl.samp_half = (int)(((vmax + 1) / 2 + 8 + 7) & ~(int64_t)7);
     pl.n_tiles = (int)((pl.G + SCAN_ROWS - 1) / SCAN_ROWS);
     const size_t rows = (size_t)pl.G;
@@ -2785,7 +2797,7 @@ int make_plan(Plan &pl, int64_t S, int H, int D, int top_k, int g, double ratio,
     pl.b_cnt = align256(rows * 8);
     pl.b_scnt = align256(rows * 8);
     pl.b_surv = align256(rows * 2 * (size_t)(pl.cap_half + 32) * 8);
-    pl.b_samp = pl.n_max > pl.keep_all_n ? align256(rows * 2 * (size_t)(pl.samp_half + 32) * 8) : 0;
+    pl.b_samp = pl.n_max > pl.keep_all_n ? align256(rows * 2 * (size_t)(pl.samp_half + 32) * 4) : 0;
     pl.b_cand = pl.mode == PIVOT_REFINE ? align256(rows * (size_t)K * 4) : 0;
     pl.b_fbl = align256(rows * 4);
     pl.b_big = pl.mode == PIVOT_REUSE ? align256(rows * 4) : 0;
@@ -2966,7 +2978,7 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
         int *cnt = (int *)take(pl.b_cnt);
         int *scnt = (int *)take(pl.b_scnt);
         uint32_t *surv = (uint32_t *)take(pl.b_surv);
-        uint2 *samp = (uint2 *)take(pl.b_samp);
+        uint32_t *samp = (uint32_t *)take(pl.b_samp);
         uint32_t *cand = (uint32_t *)take(pl.b_cand);
         uint32_t *fbl = (uint32_t *)take(pl.b_fbl);
         uint32_t *bigl = (uint32_t *)take(pl.b_big);
@@ -3005,7 +3017,8 @@ int run_prefill(const Plan &pl, const T *q, const T *k, int32_t *out_idx, float 
             ss.kstride = pl.kstride;
             ss.koff = pl.kstride - 1;
             ss.tau = nullptr;
-            ss.out = (uint32_t *)samp;
+            ss.out = samp;
+            ss.score_only = 1;
             ss.cap_half = pl.samp_half;
             ss.stride = pl.samp_half + 32;
             ss.cnt = scnt;
