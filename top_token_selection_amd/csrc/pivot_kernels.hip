@@ -375,9 +375,11 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
     typedef f32x16_t acc_t[GB];
     // fragment of k-step ks: chunk (2 ks + half) ^ (r & SWZ) of tile row r,
     // i.e. LDS address A0 ^ (ks << 5) with A0 that of k-step 0 (the chunk
-    // bits lie below the row's); A0 is renewed opaquely every tile so that
-    // the eight addresses are formed in the loop instead of held in
-    // registers
+    // bits lie below the row's, and the tiles -- the dynamic LDS, which
+    // starts right after the static rings -- are 512-byte aligned); A0 is
+    // renewed opaquely every tile so that the eight addresses are formed in
+    // the loop instead of held in registers
+    static_assert((RING * NSTREAM * 8) % 512 == 0 && TILE % 512 == 0, "key tiles start 512-byte aligned");
     const uint32_t A0 = (uint32_t)(uintptr_t)smem + (uint32_t)((l & 31) * RB) +
                         ((uint32_t)(half ^ ((l & 31) & SWZ)) << 4);
     typedef __attribute__((address_space(3))) const unsigned char *lds_cptr;
@@ -473,13 +475,13 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
     // keep the scores of tile kt that reach the row's threshold; at most 16
     // per stream and tile. Tiles below every row's prefix end skip the causal
     // test. A flush check after every 8 scores of each column block keeps
-    // the ring from filling. Per score: one compare (two on causal tiles),
-    // the count update, the ring slot address from the count (one and-or),
-    // the key index, and one LDS instruction storing score bits and key
-    // index from their own registers; the 16 key indices of the tile are
-    // shared by both column blocks. A slot is written whether kept or not
-    // (row cnt % RING is free: fewer than RING entries wait); only kept ones
-    // are counted.
+    // the ring from filling (at most 7 wait after a flush, 8 more arrive).
+    // Per score: one compare (two on causal tiles), the ring slot address
+    // from the count (one and-or) and the key index; then, with exec set to
+    // the lanes that keep the score (their ballot) and restored at once, one
+    // LDS instruction stores score bits and key index from their own
+    // registers and one add steps the count: no branch, and the other lanes
+    // neither write nor count.
     auto filter = [&](int kt, const acc_t &acc) {
 #pragma unroll
         for (int gb = 0; gb < GB; ++gb)
