@@ -474,8 +474,10 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
 
     // keep the scores of tile kt that reach the row's threshold; at most 16
     // per stream and tile. Tiles below every row's prefix end skip the causal
-    // test. A flush check after every 8 scores of each column block keeps
-    // the ring from filling (at most 7 wait after a flush, 8 more arrive).
+    // test. Flushes keep the ring from filling: at a step's end every stream
+    // with 8 or more waiting sends one chunk, so at most 8 wait when a step
+    // starts; after its first 8 scores (at most 16 waiting) the flush runs
+    // only if some stream has more than 8 waiting, so that its next 8 fit.
     // Per score: one compare (two on causal tiles), the ring slot address
     // from the count (one and-or) and the key index; then, with exec set to
     // the lanes that keep the score (their ballot) and restored at once, one
@@ -518,7 +520,16 @@ __global__ void __launch_bounds__(SCAN_THREADS, (sizeof(T) == 4 && D == 128) ? 2
                             : "memory");
                     }
                 }
-                flush();
+                if (hv == 1) {
+                    flush();
+                } else {
+                    // at most 8 wait at a step's start: the mid-step flush is
+                    // needed only where more than 8 wait now
+                    bool over = false;
+#pragma unroll
+                    for (int gb = 0; gb < GB; ++gb) over = over || (cs[gb] - fl[gb] > (uint32_t)FLUSH * RROW);
+                    if (__builtin_amdgcn_ballot_w64(over) != 0) flush();
+                }
             }
         };
         if ((int64_t)(kt + 1) * SCAN_KEYS <= vfull) run(std::false_type{});
